@@ -1,0 +1,149 @@
+/*
+ * pba.h - C ABI of libpba: pair-biased gated attention and MSA pair-weighted
+ * averaging on AMD Instinct MI355X (gfx950), forward and backward.
+ *
+ * What is computed (citations are to the AlphaFold3 open-source
+ * implementation page, molayo1419.me "Show HN: AlphaFold3 open-source
+ * implementation", mirrored on gittoolsai.com):
+ *
+ *   Attention, per batch row b and head h (section "Model Efficiency": the
+ *   pair bias is projected from the pair representation and added after the
+ *   key-query dot product, and it needs a gradient):
+ *     L[b,h,i,j] = (Q[b,h,i,:] . K[b,h,j,:]) / sqrt(d) + bias[h,i,j]
+ *                  (-inf where key_mask[j] == 0)
+ *     P = softmax_j(L),  A = P V,  out = sigmoid(G) * A   (elementwise gate)
+ *     lse[b,h,i] = log sum_j exp(L[b,h,i,j])              (natural log)
+ *   The backward pass returns dQ, dK, dV, dG and dBias, where dBias is the
+ *   gradient of the scaled QK^T product summed over the batch axis: the
+ *   forward broadcast of the bias over b becomes a reduction (same section).
+ *
+ *   Pair-weighted average, per MSA row s and head h (section "MSA Pair
+ *   Averaging Efficiency": weights from the pair bias alone, no query-key
+ *   term, never materialising the (S, N, N, H, d) intermediate):
+ *     w[h,i,j] = softmax_j(b[h,i,j] + mask),  lse_w[h,i] = log sum_j exp(...)
+ *     out[s,i,h,:] = sigmoid(G[s,i,h,:]) * sum_j w[h,i,j] V[s,j,h,:]
+ *   The backward pass returns dV, dG and db (db is reduced over s).
+ *
+ * Conventions for every entry point:
+ *   - All tensor arguments are DEVICE pointers to contiguous row-major
+ *     buffers owned by the caller, 16-byte aligned.  Outputs must not alias
+ *     inputs.  The library never allocates, frees or synchronises.
+ *   - Element type: PBA_F32 (float) or PBA_BF16 (bfloat16 bit patterns,
+ *     uint16).  Outputs and gradients use the input type; lse, lse_w and all
+ *     workspace partials are float32.
+ *   - key_mask: [N] uint8 device pointer, 0 = masked key, nonzero = keep;
+ *     NULL means every key is kept.  A query with every key masked gets
+ *     out = 0, lse = -inf and zero gradients.
+ *   - d (head width) must be a multiple of 8 in [8, 64]; sizes must be > 0.
+ *   - stream: a hipStream_t (NULL = the default stream).  Work is enqueued
+ *     and the call returns; errors in kernels surface at the caller's next
+ *     synchronisation.
+ *   - Arguments are validated before anything is enqueued; an invalid call
+ *     returns a status code and enqueues nothing.  A failed launch returns
+ *     PBA_ERR_HIP.  No C++ exception crosses this boundary.
+ *   - Results are deterministic: the same inputs give bitwise identical
+ *     outputs (no floating-point atomics; fixed-order reductions).
+ *   - Calls on different streams that share no output buffers and no
+ *     workspace are independent; the library keeps no state.
+ */
+#ifndef PBA_H
+#define PBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { PBA_F32 = 0, PBA_BF16 = 1 } pba_dtype;
+
+typedef enum {
+  PBA_OK = 0,
+  PBA_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  PBA_ERR_SHAPE = 2,       /* a size is <= 0 or too large for 32-bit indexing */
+  PBA_ERR_UNSUPPORTED = 3, /* unsupported dtype or head width d               */
+  PBA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
+  PBA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
+  PBA_ERR_HIP = 6          /* the HIP runtime reported an error at launch     */
+} pba_status;
+
+/* ABI version; bumped on any change of signature or semantics. */
+int pba_abi_version(void);
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pba_status_string(int status);
+
+/*
+ * Forward attention.
+ *   q, k, v, g : [B, H, N, d]   input type
+ *   bias       : [H, N, N]      input type, shared by every b
+ *   key_mask   : [N] uint8 or NULL
+ *   out        : [B, H, N, d]   input type (written)
+ *   lse        : [B, H, N]      float32 (written; needed by pba_backward)
+ */
+int pba_forward(int B, int H, int N, int d, int dtype,
+                const void* q, const void* k, const void* v, const void* g,
+                const void* bias, const uint8_t* key_mask,
+                void* out, float* lse, void* stream);
+
+/* Bytes of device workspace pba_backward needs for these sizes (0 if invalid). */
+size_t pba_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward attention.  Inputs as in pba_forward, plus the forward's out and
+ * lse and the upstream gradient dout [B, H, N, d].  Writes
+ *   dq, dk, dv, dg : [B, H, N, d]  input type
+ *   dbias          : [H, N, N]     input type, = sum over b of dS[b]
+ * workspace: device buffer of at least pba_backward_workspace_bytes(...)
+ * bytes, no initialisation needed; its contents after the call are
+ * unspecified.  The P matrix is recomputed from q, k, bias and lse.
+ */
+int pba_backward(int B, int H, int N, int d, int dtype,
+                 const void* q, const void* k, const void* v, const void* g,
+                 const void* bias, const uint8_t* key_mask,
+                 const void* out, const float* lse, const void* dout,
+                 void* dq, void* dk, void* dv, void* dg, void* dbias,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace pair_weighted_avg needs (0 if invalid). */
+size_t pair_weighted_avg_workspace_bytes(int S, int N, int H, int d, int dtype);
+
+/*
+ * Forward pair-weighted average (no query-key term, no scale).  bf16 only.
+ *   b          : [H, N, N]      input type (pair bias logits)
+ *   key_mask   : [N] uint8 or NULL
+ *   v, g       : [S, N, H, d]   input type (MSA row, token, head, channel)
+ *   out        : [S, N, H, d]   input type (written)
+ *   lse_w      : [H, N]         float32 (written; needed by the backward)
+ * workspace: at least pair_weighted_avg_workspace_bytes(...) bytes; it holds
+ * the [H, N, N] weights between the softmax and the weighted-sum kernels.
+ */
+int pair_weighted_avg(int S, int N, int H, int d, int dtype,
+                      const void* b, const uint8_t* key_mask,
+                      const void* v, const void* g,
+                      void* out, float* lse_w,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace pair_weighted_avg_backward needs (0 if invalid). */
+size_t pair_weighted_avg_backward_workspace_bytes(int S, int N, int H, int d, int dtype);
+
+/*
+ * Backward pair-weighted average (bf16 only).  Inputs as in pair_weighted_avg, plus the
+ * forward's out and lse_w and dout [S, N, H, d].  Writes
+ *   dv, dg : [S, N, H, d]  input type
+ *   db     : [H, N, N]     input type (reduced over the S MSA rows)
+ * workspace as for pba_backward.
+ */
+int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype,
+                               const void* b, const uint8_t* key_mask,
+                               const void* v, const void* g,
+                               const void* out, const float* lse_w, const void* dout,
+                               void* dv, void* dg, void* db,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PBA_H */

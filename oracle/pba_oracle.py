@@ -88,20 +88,23 @@ def _logits(q, k, bias_b, keep, scale):
 
 
 def _check_attention_args(q, k, v, g, bias, key_mask):
-    B, H, N, d = q.shape
-    if k.shape != q.shape:
-        raise ValueError(f"k has shape {k.shape}, expected {q.shape}")
-    # the value/gate width may differ from the query/key width
-    if v.shape[:3] != q.shape[:3] or v.ndim != 4:
-        raise ValueError(f"v has shape {v.shape}, expected {q.shape[:3]} + (dv,)")
-    if g.shape != v.shape:
-        raise ValueError(f"g has shape {g.shape}, expected {v.shape}")
-    if bias.shape not in ((H, N, N), (B, H, N, N)):
-        raise ValueError(f"bias has shape {bias.shape}, expected {(H, N, N)} or {(B, H, N, N)}")
+    """Shapes: q [B,H,Nq,d], k [B,H,Nk,d], v [B,H,Nk,dv], g [B,H,Nq,dv],
+    bias [H,Nq,Nk] or [B,H,Nq,Nk], key_mask [Nk].  Every workload has Nq = Nk
+    and dv = d; the general form lets a test take a subset of query rows."""
+    B, H, Nq, d = q.shape
+    if k.ndim != 4 or k.shape[:2] != (B, H) or k.shape[3] != d:
+        raise ValueError(f"k has shape {k.shape}, expected {(B, H)} + (Nk, {d})")
+    Nk = k.shape[2]
+    if v.ndim != 4 or v.shape[:3] != (B, H, Nk):
+        raise ValueError(f"v has shape {v.shape}, expected {(B, H, Nk)} + (dv,)")
+    if g.shape != (B, H, Nq, v.shape[3]):
+        raise ValueError(f"g has shape {g.shape}, expected {(B, H, Nq, v.shape[3])}")
+    if bias.shape not in ((H, Nq, Nk), (B, H, Nq, Nk)):
+        raise ValueError(f"bias has shape {bias.shape}, expected {(H, Nq, Nk)} or {(B, H, Nq, Nk)}")
     keep = None
     if key_mask is not None:
-        keep = np.asarray(key_mask).reshape(N) != 0
-    return B, H, N, d, keep
+        keep = np.asarray(key_mask).reshape(Nk) != 0
+    return B, H, Nq, d, keep
 
 
 def attention_forward(q, k, v, g, bias, key_mask=None, scale=None, chunk=32):
@@ -112,12 +115,13 @@ def attention_forward(q, k, v, g, bias, key_mask=None, scale=None, chunk=32):
     LSE[b,h,i] = log sum_j exp(logit[b,h,i,j]) (natural log).
 
     q, k: [B, H, N, d]; v, g: [B, H, N, dv] (dv = d in every workload);
-    bias: [H, N, N] shared over B, or [B, H, N, N].
+    bias: [H, N, N] shared over B, or [B, H, N, N].  (Query and key counts
+    may differ; see _check_attention_args.)
     """
     q, k, v, g, bias = (np.asarray(t, dtype=np.float64) for t in (q, k, v, g, bias))
     B, H, N, d, keep = _check_attention_args(q, k, v, g, bias, key_mask)
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
-    O = np.empty(v.shape)
+    O = np.empty(g.shape)
     LSE = np.empty((B, H, N))
     for b0 in range(0, B, chunk):
         b1 = min(B, b0 + chunk)
@@ -176,15 +180,18 @@ def attention_backward(q, k, v, g, bias, key_mask, dout, scale=None, chunk=32):
 
 
 def _check_pwa_args(b, v, g, key_mask):
-    S, N, H, d = v.shape
-    if g.shape != v.shape:
-        raise ValueError(f"g has shape {g.shape}, expected {v.shape}")
-    if b.shape != (H, N, N):
-        raise ValueError(f"b has shape {b.shape}, expected {(H, N, N)}")
+    """Shapes: b [H,Nq,Nk], v [S,Nk,H,d], g [S,Nq,H,d], key_mask [Nk]
+    (Nq = Nk in every workload; a test may take a subset of rows i)."""
+    S, Nk, H, d = v.shape
+    if b.ndim != 3 or b.shape[0] != H or b.shape[2] != Nk:
+        raise ValueError(f"b has shape {b.shape}, expected {(H,)} + (Nq, {Nk})")
+    Nq = b.shape[1]
+    if g.shape != (S, Nq, H, d):
+        raise ValueError(f"g has shape {g.shape}, expected {(S, Nq, H, d)}")
     keep = None
     if key_mask is not None:
-        keep = np.asarray(key_mask).reshape(N) != 0
-    return S, N, H, d, keep
+        keep = np.asarray(key_mask).reshape(Nk) != 0
+    return S, Nk, H, d, keep
 
 
 def _pwa_weights(b, keep):
@@ -198,17 +205,20 @@ def pwa_forward(b, v, g, key_mask=None, chunk=128):
     w[h,i,j] = softmax_j(b[h,i,j] + mask);
     O[s,i,h,:] = sigmoid(G[s,i,h,:]) * sum_j w[h,i,j] V[s,j,h,:].
     b: [H, N, N]; v, g: [S, N, H, d].  Returns (O, lse_w) with lse_w [H, N].
+    (Row and token counts may differ; see _check_pwa_args.)
     """
     b, v, g = (np.asarray(t, dtype=np.float64) for t in (b, v, g))
-    S, N, H, d, keep = _check_pwa_args(b, v, g, key_mask)
+    S, Nk, H, d, keep = _check_pwa_args(b, v, g, key_mask)
+    Nq = b.shape[1]
     w, lse = _pwa_weights(b, keep)
-    O = np.empty((S, N, H, d))
+    O = np.empty(g.shape)
     for s0 in range(0, S, chunk):
         s1 = min(S, s0 + chunk)
+        n = s1 - s0
         for h in range(H):
-            # [N, N] @ [N, (s, c)] per head, with the MSA rows as extra columns
-            vh = np.transpose(v[s0:s1, :, h, :], (1, 0, 2)).reshape(N, -1)
-            Ah = (w[h] @ vh).reshape(N, s1 - s0, d).transpose(1, 0, 2)
+            # [Nq, Nk] @ [Nk, (s, c)] per head, with the MSA rows as extra columns
+            vh = np.transpose(v[s0:s1, :, h, :], (1, 0, 2)).reshape(Nk, n * d)
+            Ah = (w[h] @ vh).reshape(Nq, n, d).transpose(1, 0, 2)
             O[s0:s1, :, h, :] = sigmoid(g[s0:s1, :, h, :]) * Ah
     return O, lse
 
@@ -221,25 +231,27 @@ def pwa_backward(b, v, g, key_mask, dout, chunk=128):
       dV[s,j,h,:] = sum_i w[h,i,j] dA[s,i,h,:]
       dw[h,i,j]   = sum_{s,c} dA[s,i,h,c] V[s,j,h,c]   (broadcast over s -> reduction)
       db = w * (dw - sum_j w * dw)                      (softmax Jacobian)
-    Returns a dict with dv, dg ([S,N,H,d]) and db ([H,N,N]).
+    Returns a dict with dv, dg ([S,N,H,d]) and db ([H,N,N]).  With a subset of
+    rows i, dv holds only those rows' contributions.
     """
     b, v, g, dout = (np.asarray(t, dtype=np.float64) for t in (b, v, g, dout))
-    S, N, H, d, keep = _check_pwa_args(b, v, g, key_mask)
+    S, Nk, H, d, keep = _check_pwa_args(b, v, g, key_mask)
+    Nq = b.shape[1]
     w, _ = _pwa_weights(b, keep)
     dv = np.empty_like(v)
     dg = np.empty_like(g)
-    dw = np.zeros((H, N, N))
+    dw = np.zeros((H, Nq, Nk))
     for s0 in range(0, S, chunk):
         s1 = min(S, s0 + chunk)
         n = s1 - s0
         for h in range(H):
-            vh = np.transpose(v[s0:s1, :, h, :], (1, 0, 2)).reshape(N, n * d)
-            Ah = (w[h] @ vh).reshape(N, n, d).transpose(1, 0, 2)
+            vh = np.transpose(v[s0:s1, :, h, :], (1, 0, 2)).reshape(Nk, n * d)
+            Ah = (w[h] @ vh).reshape(Nq, n, d).transpose(1, 0, 2)
             sh = sigmoid(g[s0:s1, :, h, :])
             dAh = dout[s0:s1, :, h, :] * sh
             dg[s0:s1, :, h, :] = dout[s0:s1, :, h, :] * Ah * sh * (1.0 - sh)
-            dAh_m = np.transpose(dAh, (1, 0, 2)).reshape(N, n * d)
-            dv[s0:s1, :, h, :] = (w[h].T @ dAh_m).reshape(N, n, d).transpose(1, 0, 2)
+            dAh_m = np.transpose(dAh, (1, 0, 2)).reshape(Nq, n * d)
+            dv[s0:s1, :, h, :] = (w[h].T @ dAh_m).reshape(Nk, n, d).transpose(1, 0, 2)
             dw[h] += dAh_m @ vh.T
     db = w * (dw - np.sum(w * dw, axis=-1, keepdims=True))
     return {"dv": dv, "dg": dg, "db": db}

@@ -1,0 +1,178 @@
+// pba_api.hip - the C ABI declared in include/pba.h: argument validation,
+// workspace sizing and dispatch to the gfx950 kernels.  Every check runs on
+// the host before anything is enqueued; nothing here allocates, frees,
+// synchronises or prints.
+#include <math.h>
+
+#include "pba.h"
+#include "pba_kernels.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr long long kMaxElems = (1LL << 31) - 1;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_dims(long long a, long long b, long long c, int d, int dtype, bool bf16_only) {
+  if (dtype != PBA_F32 && dtype != PBA_BF16) return PBA_ERR_UNSUPPORTED;
+  if (bf16_only && dtype != PBA_BF16) return PBA_ERR_UNSUPPORTED;
+  if (a <= 0 || b <= 0 || c <= 0 || d <= 0) return PBA_ERR_SHAPE;
+  if (d % 8 != 0 || d > 64) return PBA_ERR_UNSUPPORTED;
+  if (a * b * c * d > kMaxElems) return PBA_ERR_SHAPE;
+  return PBA_OK;
+}
+
+// attention sizes: tensors [B,H,N,d], bias [H,N,N]
+int check_attn_sizes(int B, int H, int N, int d, int dtype) {
+  int st = check_dims(B, H, N, d, dtype, false);
+  if (st != PBA_OK) return st;
+  if ((long long)H * N * N > kMaxElems) return PBA_ERR_SHAPE;
+  if ((long long)B * H * ((N + 63) / 64) > 0x7FFFFFFFLL) return PBA_ERR_SHAPE;
+  return PBA_OK;
+}
+
+int check_pwa_sizes(int S, int N, int H, int d, int dtype) {
+  int st = check_dims(S, N, H, d, dtype, true);
+  if (st != PBA_OK) return st;
+  if ((long long)H * N * N > kMaxElems) return PBA_ERR_SHAPE;
+  return PBA_OK;
+}
+
+int all_nonnull(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (p == nullptr) return PBA_ERR_NULL;
+  return PBA_OK;
+}
+int all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned16(p)) return PBA_ERR_ALIGN;
+  return PBA_OK;
+}
+
+float attn_scale(int d) { return 1.0f / sqrtf((float)d); }
+
+}  // namespace
+
+extern "C" {
+
+int pba_abi_version(void) { return kAbiVersion; }
+
+const char* pba_status_string(int status) {
+  switch (status) {
+    case PBA_OK: return "PBA_OK";
+    case PBA_ERR_NULL: return "PBA_ERR_NULL: a required pointer is NULL";
+    case PBA_ERR_SHAPE: return "PBA_ERR_SHAPE: a size is <= 0 or too large";
+    case PBA_ERR_UNSUPPORTED: return "PBA_ERR_UNSUPPORTED: unsupported dtype or head width";
+    case PBA_ERR_ALIGN: return "PBA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case PBA_ERR_WORKSPACE: return "PBA_ERR_WORKSPACE: workspace missing or too small";
+    case PBA_ERR_HIP: return "PBA_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown pba status";
+  }
+}
+
+int pba_forward(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                const void* g, const void* bias, const uint8_t* key_mask, void* out, float* lse,
+                void* stream) {
+  int st = check_attn_sizes(B, H, N, d, dtype);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({q, k, v, g, bias, out, lse})) != PBA_OK) return st;
+  if ((st = all_aligned16({q, k, v, g, bias, out})) != PBA_OK) return st;
+  if (!aligned4(lse)) return PBA_ERR_ALIGN;
+  pba::FwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.bias = bias; a.mask = key_mask;
+  a.out = out; a.lse = lse;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.scale = attn_scale(d);
+  const hipError_t e = pba::launch_attn_fwd(a, dtype == PBA_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+size_t pba_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  if (check_attn_sizes(B, H, N, d, dtype) != PBA_OK) return 0;
+  return pba::plan_attn_bwd(B, H, N, d, dtype == PBA_BF16).total;
+}
+
+int pba_backward(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                 const void* g, const void* bias, const uint8_t* key_mask, const void* out,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dg, void* dbias,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_attn_sizes(B, H, N, d, dtype);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({q, k, v, g, bias, out, lse, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
+  if ((st = all_aligned16({q, k, v, g, bias, out, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
+  if (!aligned4(lse)) return PBA_ERR_ALIGN;
+  const bool bf16 = dtype == PBA_BF16;
+  const pba::BwdPlan pl = pba::plan_attn_bwd(B, H, N, d, bf16);
+  if (workspace == nullptr || workspace_bytes < pl.total) return PBA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PBA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  pba::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.g = g; a.bias = bias; a.mask = key_mask;
+  a.out = out; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbias = dbias;
+  a.da = ws + pl.off_da;
+  a.drow = reinterpret_cast<float*>(ws + pl.off_drow);
+  a.partial = reinterpret_cast<float*>(ws + pl.off_partial);
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.scale = attn_scale(d);
+  a.P = pl.P; a.C = pl.C; a.slab = pl.slab;
+  const hipError_t e = pba::launch_attn_bwd(a, bf16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+size_t pair_weighted_avg_workspace_bytes(int S, int N, int H, int d, int dtype) {
+  if (check_pwa_sizes(S, N, H, d, dtype) != PBA_OK) return 0;
+  return ((size_t)H * N * N * 2 + 255) & ~size_t(255);
+}
+
+int pair_weighted_avg(int S, int N, int H, int d, int dtype, const void* b, const uint8_t* key_mask,
+                      const void* v, const void* g, void* out, float* lse_w, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_pwa_sizes(S, N, H, d, dtype);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({b, v, g, out, lse_w})) != PBA_OK) return st;
+  if ((st = all_aligned16({b, v, g, out})) != PBA_OK) return st;
+  if (!aligned4(lse_w)) return PBA_ERR_ALIGN;
+  if (workspace == nullptr || workspace_bytes < pair_weighted_avg_workspace_bytes(S, N, H, d, dtype))
+    return PBA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PBA_ERR_ALIGN;
+  pba::PwaArgs a{};
+  a.b = b; a.mask = key_mask; a.v = v; a.g = g;
+  a.o = out; a.lse_w = lse_w; a.w = workspace;
+  a.S = S; a.N = N; a.H = H; a.d = d; a.P = 1;
+  const hipError_t e = pba::launch_pwa_fwd(a, true, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+size_t pair_weighted_avg_backward_workspace_bytes(int S, int N, int H, int d, int dtype) {
+  if (check_pwa_sizes(S, N, H, d, dtype) != PBA_OK) return 0;
+  return pba::plan_pwa_bwd(S, N, H, d, true).total;
+}
+
+int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype, const void* b,
+                               const uint8_t* key_mask, const void* v, const void* g, const void* out,
+                               const float* lse_w, const void* dout, void* dv, void* dg, void* db,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_pwa_sizes(S, N, H, d, dtype);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({b, v, g, out, lse_w, dout, dv, dg, db})) != PBA_OK) return st;
+  if ((st = all_aligned16({b, v, g, out, dout, dv, dg, db})) != PBA_OK) return st;
+  if (!aligned4(lse_w)) return PBA_ERR_ALIGN;
+  const pba::PwaPlan pl = pba::plan_pwa_bwd(S, N, H, d, true);
+  if (workspace == nullptr || workspace_bytes < pl.total) return PBA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PBA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  pba::PwaArgs a{};
+  a.b = b; a.mask = key_mask; a.v = v; a.g = g; a.out = out; a.lse_w_in = lse_w; a.dout = dout;
+  a.dv = dv; a.dg = dg; a.db = db;
+  a.w = ws + pl.off_w;
+  a.da = ws + pl.off_da;
+  a.partial = reinterpret_cast<float*>(ws + pl.off_partial);
+  a.S = S; a.N = N; a.H = H; a.d = d; a.P = pl.P;
+  const hipError_t e = pba::launch_pwa_bwd(a, true, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// pba_kernels.h - argument blocks and launchers of the gfx950 kernels
+// (host-visible; included by the C-ABI translation unit).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pba {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* bias;
+  const uint8_t* mask;
+  void* out;
+  float* lse;
+  int B, H, N, d;
+  float scale;
+  int nqb;  // query blocks per (b, h), set by the launcher
+};
+
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* bias;
+  const uint8_t* mask;
+  const void* out;
+  const float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dg;
+  void* dbias;
+  // workspace views
+  void* da;         // dA = dout * sigmoid(G), [B,H,N,d] (bf16 for bf16 inputs, fp32 otherwise)
+  float* drow;      // D = rowsum(dout * out), [B,H,N]
+  float* partial;   // dBias partial sums, [P,H,N,N]
+  int B, H, N, d;
+  float scale;
+  int P;            // number of batch chunks (partials)
+  int C;            // batch rows per chunk
+  int slab;         // 1: accumulate dS over the chunk in LDS; 0: one partial per row
+};
+
+struct PwaArgs {
+  const void* b;
+  const uint8_t* mask;
+  const void* v;
+  const void* g;
+  const void* out;
+  const float* lse_w_in;
+  const void* dout;
+  void* o;          // forward output
+  float* lse_w;     // forward lse (written)
+  void* dv;
+  void* dg;
+  void* db;
+  void* w;          // workspace: softmax weights, [H,N,N] bf16 or fp32
+  void* da;         // workspace: dA [S,N,H,d]
+  float* partial;   // workspace: dw partial sums [P,H,N,N]
+  int S, N, H, d;
+  int P;            // S chunks of the dw reduction
+};
+
+// Workspace plan of the attention backward (byte offsets into one buffer).
+struct BwdPlan {
+  size_t off_da, off_drow, off_partial, total;
+  int P, C, slab;
+};
+BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16);
+
+struct PwaPlan {
+  size_t off_w, off_da, off_partial, total;
+  int P;
+};
+PwaPlan plan_pwa_bwd(int S, int N, int H, int d, bool bf16);
+
+hipError_t launch_attn_fwd(const FwdArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_pwa_fwd(const PwaArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_pwa_bwd(const PwaArgs& a, bool bf16, hipStream_t stream);
+
+}  // namespace pba

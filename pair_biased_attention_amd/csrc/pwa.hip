@@ -1,0 +1,466 @@
+// pwa.hip - MSA pair-weighted averaging (forward and backward) for gfx950.
+//
+// The "MSA Pair Averaging Efficiency" section of the AlphaFold3 open-source
+// implementation page (molayo1419.me) describes the operation: a weighted
+// average over tokens j whose weights come from the pair bias alone,
+// w[h,i,j] = softmax_j(b[h,i,j]), replacing MSA row attention; the naive
+// form allocates a (*, N_seq, N_res, N_res, heads, c_hidden) intermediate.
+// Here nothing of that size exists: per head the average is the GEMM
+//   A_h[i, (s,c)] = sum_j w[h,i,j] V[s,j,h,c]     (M = N, K = N, cols = S*d)
+// evaluated as O^T = V^T w^T so each lane ends with 4 consecutive channels of
+// one (s, i) row for the sigmoid-gate epilogue.
+//
+// Kernels (all on the caller's stream):
+//   pwa_softmax   w and w^T (bf16 workspace) and lse_w
+//   pwa_gemm<FWD> out = sigmoid(G) * (w V)   or  dV = w^T dA   (same kernel)
+//   pwa_bwd_pre   dA = dO*sigmoid(G), dG = dO*O*(1-sigmoid(G))
+//   pwa_dw        split-K GEMM dw_p[h,i,j] = sum_{s in chunk p, c} dA[s,i,h,c] V[s,j,h,c]
+//   pwa_db        dw = sum_p dw_p (index order), db = w*(dw - sum_j w*dw)
+#include "pba_device.h"
+#include "pba_kernels.h"
+
+namespace pba {
+
+namespace {
+__device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u16 lo16(uint32_t w) { return (u16)(w & 0xFFFFu); }
+__device__ __forceinline__ u16 hi16(uint32_t w) { return (u16)(w >> 16); }
+__device__ __forceinline__ float sigmoid_precise(float x) { return 1.0f / (1.0f + expf(-x)); }
+}  // namespace
+
+// ------------------------------------------------------------------ softmax
+// One wave per (h, i) row.
+__global__ void __launch_bounds__(256) pwa_softmax_kernel(PwaArgs a, u16* wt) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int N = a.N;
+  if (row >= (long long)a.H * N) return;
+  const int h = (int)(row / N), i = (int)(row % N);
+  const u16* brow = static_cast<const u16*>(a.b) + row * N;
+  float mx = kNegInf;
+  for (int j = lane; j < N; j += 64) {
+    const bool keep = a.mask == nullptr || a.mask[j] != 0;
+    if (keep) mx = fmaxf(mx, bf2f(brow[j]));
+  }
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float msafe = (mx == kNegInf) ? 0.f : mx;
+  float l = 0.f;
+  for (int j = lane; j < N; j += 64) {
+    const bool keep = a.mask == nullptr || a.mask[j] != 0;
+    if (keep) l += expf(bf2f(brow[j]) - msafe);
+  }
+  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  u16* wrow = static_cast<u16*>(a.w) + row * N;
+  u16* wcol = wt + (size_t)h * N * N + i;
+  for (int j = lane; j < N; j += 64) {
+    const bool keep = a.mask == nullptr || a.mask[j] != 0;
+    const float w = keep ? expf(bf2f(brow[j]) - msafe) * inv : 0.f;
+    const u16 wb = f2bf(w);
+    wrow[j] = wb;
+    if (wt) wcol[(size_t)j * N] = wb;
+  }
+  if (lane == 0 && a.lse_w) a.lse_w[row] = l > 0.f ? msafe + logf(l) : kNegInf;
+}
+
+// ------------------------------------------------------------------ GEMM with transposed X
+// out^T[(s,c)][n] = sum_k X[s,k,h,c] * W[h,n,k]
+//   forward:  X = V,  W = w   (n = i, k = j), epilogue * sigmoid(G)
+//   dV:       X = dA, W = w^T (n = j, k = i), no epilogue
+// Workgroup tile: 256 columns (s, c) x 256 rows n, K in chunks of 64; eight
+// waves, each 64 columns x 128 rows (4 x 8 accumulator tiles).
+template <int DP>
+struct PwaGemmSmem {
+  u32x4 xt[2][16 * 2 * 64];   // X^T fragments [ct][kh][lane]
+  u32x4 w[2][16 * 2 * 64];    // W fragments   [nt][kh][lane]
+};
+
+template <int DP, bool FWD>
+__global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X, const u16* __restrict__ W,
+                                                       const u16* __restrict__ G, u16* __restrict__ out,
+                                                       int S, int N, int H, int d, int ncolt, int nnt) {
+  constexpr int SPT = 256 / DP;  // MSA rows per column tile
+  __shared__ PwaGemmSmem<DP> sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, ln = lane & 15;
+  const int wc = wave & 3, wn = wave >> 2;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int nt_blk = L % nnt;
+  const int rest = L / nnt;
+  const int colt = rest % ncolt, h = rest / ncolt;
+  const int s0 = colt * SPT, n0 = nt_blk * 256;
+  const u16* Wh = W + (size_t)h * N * N;
+  const size_t srow = (size_t)N * H * d;   // stride of s in [S,N,H,d]
+  const size_t krow = (size_t)H * d;       // stride of the token index
+
+  // staging assignment
+  //   X: thread -> (s_local, k quad u, c8); 4 rows k = 4u..4u+3
+  //   W: 4 chunks per thread -> (n_local, k8)
+  constexpr int C8 = DP / 8;
+  u32x4 rx[4];
+  u32x4 rw[4];
+  auto fetch = [&](int k0) {
+    {
+      const int c8 = tid % C8;
+      const int u = (tid / C8) % 16;
+      const int sl = tid / (C8 * 16);
+      const int s = s0 + sl;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int k = k0 + 4 * u + q;
+        rx[q] = (s < S && k < N && 8 * c8 < d) ? ld16(X + s * srow + (size_t)k * krow + (size_t)h * d + 8 * c8)
+                                               : u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int c = tid + 512 * it;
+      const int nl = c >> 3, k8 = c & 7;
+      const int n = n0 + nl, k = k0 + 8 * k8;
+      if (n < N && k + 8 <= N && (N & 7) == 0) {
+        rw[it] = ld16(Wh + (size_t)n * N + k);
+      } else {
+        uint32_t w4[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int kk = k + 2 * e;
+          const uint32_t lo = (n < N && kk < N) ? Wh[(size_t)n * N + kk] : 0u;
+          const uint32_t hi = (n < N && kk + 1 < N) ? Wh[(size_t)n * N + kk + 1] : 0u;
+          w4[e] = lo | (hi << 16);
+        }
+        rw[it] = u32x4{w4[0], w4[1], w4[2], w4[3]};
+      }
+    }
+  };
+  auto commit = [&](int buf) {
+    {
+      const int c8 = tid % C8;
+      const int u = (tid / C8) % 16;
+      const int sl = tid / (C8 * 16);
+      const int kl0 = 4 * u;
+      const int kh = kl0 >> 5, ga = (kl0 & 31) >> 3, v0 = kl0 & 7;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int col = sl * DP + 8 * c8 + e;
+        const int ct = col >> 4, ii = col & 15;
+        uint32_t x[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[q] = (e & 1) ? hi16(rx[q][e >> 1]) : lo16(rx[q][e >> 1]);
+        u32x2 pk = u32x2{x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
+        char* base = reinterpret_cast<char*>(&sm.xt[buf][0]);
+        *reinterpret_cast<u32x2*>(base + ((size_t)((ct * 2 + kh) * 64 + ga * 16 + ii)) * 16 + v0 * 2) = pk;
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int c = tid + 512 * it;
+      const int nl = c >> 3, k8 = c & 7;
+      const int nt = nl >> 4, nn = nl & 15, kh = k8 >> 2, gg = k8 & 3;
+      sm.w[buf][(nt * 2 + kh) * 64 + gg * 16 + nn] = rw[it];
+    }
+  };
+
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[ct][nt] = zero4;
+
+  const int nkc = (N + 63) / 64;
+  fetch(0);
+  commit(0);
+  __syncthreads();
+  for (int kcix = 0; kcix < nkc; ++kcix) {
+    const int buf = kcix & 1;
+    if (kcix + 1 < nkc) fetch(64 * (kcix + 1));
+#pragma unroll
+    for (int kh = 0; kh < 2; ++kh) {
+      bf16x8 af[4], bfr[8];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) af[ct] = as_bf8(sm.xt[buf][((4 * wc + ct) * 2 + kh) * 64 + lane]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) bfr[nt] = as_bf8(sm.w[buf][((8 * wn + nt) * 2 + kh) * 64 + lane]);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) acc[ct][nt] = mfma32(af[ct], bfr[nt], acc[ct][nt]);
+    }
+    if (kcix + 1 < nkc) commit(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane (g, n) of tile (ct, nt) holds columns 4g..4g+3 of row n
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct) {
+    const int col = 64 * wc + 16 * ct + 4 * g;
+    const int sl = col / DP, c = col % DP;
+    const int s = s0 + sl;
+    if (s >= S || c >= d) continue;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) {
+      const int nrow = n0 + 128 * wn + 16 * nt + ln;
+      if (nrow >= N) continue;
+      const size_t off = s * srow + (size_t)nrow * krow + (size_t)h * d + c;
+      f32x4 o = acc[ct][nt];
+      if constexpr (FWD) {
+        const u32x2 gr = *reinterpret_cast<const u32x2*>(G + off);
+        o[0] *= sigmoidf_fast(bf2f(lo16(gr[0])));
+        o[1] *= sigmoidf_fast(bf2f(hi16(gr[0])));
+        o[2] *= sigmoidf_fast(bf2f(lo16(gr[1])));
+        o[3] *= sigmoidf_fast(bf2f(hi16(gr[1])));
+      }
+      *reinterpret_cast<u32x2*>(out + off) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+    }
+  }
+}
+
+// ------------------------------------------------------------------ backward elementwise
+__global__ void __launch_bounds__(256) pwa_bwd_pre_kernel(PwaArgs a) {
+  const size_t n8 = (size_t)a.S * a.N * a.H * a.d / 8;
+  const size_t i8 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i8 >= n8) return;
+  const u16* dO = static_cast<const u16*>(a.dout);
+  const u16* O = static_cast<const u16*>(a.out);
+  const u16* G = static_cast<const u16*>(a.g);
+  const u32x4 xo = ld16(dO + 8 * i8), xv = ld16(O + 8 * i8), xg = ld16(G + 8 * i8);
+  u32x4 ra, rg;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float f0 = bf2f(lo16(xo[e])), f1 = bf2f(hi16(xo[e]));
+    const float o0 = bf2f(lo16(xv[e])), o1 = bf2f(hi16(xv[e]));
+    const float s0 = sigmoid_precise(bf2f(lo16(xg[e]))), s1 = sigmoid_precise(bf2f(hi16(xg[e])));
+    ra[e] = pack2(f0 * s0, f1 * s1);
+    rg[e] = pack2(f0 * o0 * (1.f - s0), f1 * o1 * (1.f - s1));
+  }
+  *reinterpret_cast<u32x4*>(static_cast<u16*>(a.da) + 8 * i8) = ra;
+  *reinterpret_cast<u32x4*>(static_cast<u16*>(a.dg) + 8 * i8) = rg;
+}
+
+// ------------------------------------------------------------------ dw split-K GEMM
+// dw_p[h][i][j] = sum_{s in chunk p} sum_c dA[s,i,h,c] V[s,j,h,c].  Both operands
+// keep their natural layout (channels contiguous = the MFMA k axis).
+// Workgroup tile 256 i x 256 j, eight waves of 64 i x 128 j; 64 k values
+// (64/DP MSA rows) staged per iteration.
+template <int DP>
+struct PwaDwSmem {
+  static constexpr int SPS = 64 / DP;        // MSA rows per stage (64 k values)
+  static constexpr int KS = 2;               // k steps of 32 per stage
+  u32x4 a[2][16 * KS * 64];  // dA fragments [it][ks][lane]
+  u32x4 b[2][16 * KS * 64];  // V  fragments [jt][ks][lane]
+};
+
+template <int DP>
+__global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA, const u16* __restrict__ V,
+                                                     float* __restrict__ partial, int S, int N, int H, int d,
+                                                     int P, int spc, int nt1) {
+  using Sm = PwaDwSmem<DP>;
+  constexpr int KS = Sm::KS, SPS = Sm::SPS;
+  constexpr int C8 = DP / 8;
+  __shared__ Sm sm;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, ln = lane & 15;
+  const int wi = wave & 3, wj = wave >> 2;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  // logical order: (h, p) outer, the nt1 x nt1 tiles inner
+  const int tile = L % (nt1 * nt1);
+  const int hp = L / (nt1 * nt1);
+  const int p = hp % P, h = hp / P;
+  const int it0 = (tile / nt1) * 256, jt0 = (tile % nt1) * 256;
+  const int sb = p * spc, se = min(S, sb + spc);
+  const size_t srow = (size_t)N * H * d;
+  const size_t krow = (size_t)H * d;
+
+  // per stage: SPS MSA rows x 256 tokens x C8 chunks, for each operand
+  constexpr int NCHUNK = SPS * 256 * C8;    // chunks of 16 B per operand
+  constexpr int PER = NCHUNK / 512;         // per thread
+  u32x4 ra[PER], rb[PER];
+  auto fetch = [&](int s_begin) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = tid + 512 * it;
+      const int c8 = c % C8, tok = (c / C8) % 256, sl = c / (C8 * 256);
+      const int s = s_begin + sl;
+      const int ia = it0 + tok, jb = jt0 + tok;
+      const bool cok = s < se && 8 * c8 < d;
+      ra[it] = (cok && ia < N) ? ld16(dA + s * srow + (size_t)ia * krow + (size_t)h * d + 8 * c8) : u32x4{0, 0, 0, 0};
+      rb[it] = (cok && jb < N) ? ld16(V + s * srow + (size_t)jb * krow + (size_t)h * d + 8 * c8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto commit = [&](int buf) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int c = tid + 512 * it;
+      const int c8 = c % C8, tok = (c / C8) % 256, sl = c / (C8 * 256);
+      const int ks = sl * (DP / 32) + (c8 >> 2), ga = c8 & 3;
+      const int t = tok >> 4, r = tok & 15;
+      sm.a[buf][(t * KS + ks) * 64 + ga * 16 + r] = ra[it];
+      sm.b[buf][(t * KS + ks) * 64 + ga * 16 + r] = rb[it];
+    }
+  };
+
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+    for (int b8 = 0; b8 < 8; ++b8) acc[a4][b8] = zero4;
+
+  const int nst = se > sb ? (se - sb + SPS - 1) / SPS : 0;
+  if (nst > 0) {
+    fetch(sb);
+    commit(0);
+  }
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nst) fetch(sb + SPS * (st + 1));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 af[4], bfr[8];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) af[a4] = as_bf8(sm.a[buf][((4 * wi + a4) * KS + ks) * 64 + lane]);
+#pragma unroll
+      for (int b8 = 0; b8 < 8; ++b8) bfr[b8] = as_bf8(sm.b[buf][((8 * wj + b8) * KS + ks) * 64 + lane]);
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int b8 = 0; b8 < 8; ++b8) acc[a4][b8] = mfma32(af[a4], bfr[b8], acc[a4][b8]);
+    }
+    if (st + 1 < nst) commit(buf ^ 1);
+    __syncthreads();
+  }
+
+  // lane (g, n) of tile (a4, b8) holds rows i = 4g..4g+3 of column j = n
+  float* part = partial + ((size_t)p * H + h) * N * N;
+#pragma unroll
+  for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+    for (int b8 = 0; b8 < 8; ++b8) {
+      const int j = jt0 + 128 * wj + 16 * b8 + ln;
+      if (j >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = it0 + 64 * wi + 16 * a4 + 4 * g + r;
+        if (i < N) part[(size_t)i * N + j] = acc[a4][b8][r];
+      }
+    }
+}
+
+// ------------------------------------------------------------------ db
+// One wave per (h, i) row: dw = sum_p partial (index order); w recomputed in
+// fp32 from b and lse_w; db = w * (dw - sum_j w dw).
+__global__ void __launch_bounds__(256) pwa_db_kernel(PwaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int N = a.N;
+  if (row >= (long long)a.H * N) return;
+  const u16* brow = static_cast<const u16*>(a.b) + row * N;
+  const float lse = a.lse_w_in[row];
+  const size_t plane = (size_t)a.H * N * N;
+  float t = 0.f;
+  for (int j = lane; j < N; j += 64) {
+    const bool keep = (a.mask == nullptr || a.mask[j] != 0) && lse != kNegInf;
+    const float w = keep ? expf(bf2f(brow[j]) - lse) : 0.f;
+    float dw = 0.f;
+    for (int p = 0; p < a.P; ++p) dw += a.partial[p * plane + row * N + j];
+    t = fmaf(w, dw, t);
+  }
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+  u16* db = static_cast<u16*>(a.db) + row * N;
+  for (int j = lane; j < N; j += 64) {
+    const bool keep = (a.mask == nullptr || a.mask[j] != 0) && lse != kNegInf;
+    const float w = keep ? expf(bf2f(brow[j]) - lse) : 0.f;
+    float dw = 0.f;
+    for (int p = 0; p < a.P; ++p) dw += a.partial[p * plane + row * N + j];
+    db[j] = f2bf(w * (dw - t));
+  }
+}
+
+// ------------------------------------------------------------------ plan + launch
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+PwaPlan plan_pwa_bwd(int S, int N, int H, int d, bool /*bf16*/) {
+  PwaPlan pl{};
+  const int nt1 = (N + 255) / 256;
+  const long long tiles = (long long)nt1 * nt1 * H;
+  int P = (int)std::max<long long>(1, std::min<long long>(S / 2 > 0 ? S / 2 : 1, (256 + tiles - 1) / tiles));
+  pl.P = P;
+  size_t off = 0;
+  pl.off_w = off;                                         // w and w^T
+  off = align256(off + 2 * (size_t)H * N * N * 2);
+  pl.off_da = off;
+  off = align256(off + (size_t)S * N * H * d * 2);
+  pl.off_partial = off;
+  off = align256(off + (size_t)P * H * N * N * 4);
+  pl.total = off;
+  return pl;
+}
+
+static hipError_t launch_softmax(const PwaArgs& a, u16* wt, hipStream_t stream) {
+  const long long rows = (long long)a.H * a.N;
+  hipLaunchKernelGGL(pwa_softmax_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a, wt);
+  return hipGetLastError();
+}
+
+template <bool FWD>
+static hipError_t launch_gemm(const u16* X, const u16* W, const u16* G, u16* out, const PwaArgs& a,
+                              hipStream_t stream) {
+  const int dp = a.d <= 32 ? 32 : 64;
+  const int spt = 256 / dp;
+  const int ncolt = (a.S + spt - 1) / spt;
+  const int nnt = (a.N + 255) / 256;
+  const dim3 grid((unsigned)((long long)ncolt * nnt * a.H));
+  if (dp == 32)
+    hipLaunchKernelGGL((pwa_gemm_kernel<32, FWD>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, a.H, a.d, ncolt, nnt);
+  else
+    hipLaunchKernelGGL((pwa_gemm_kernel<64, FWD>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, a.H, a.d, ncolt, nnt);
+  return hipGetLastError();
+}
+
+hipError_t launch_pwa_fwd(const PwaArgs& a, bool /*bf16*/, hipStream_t stream) {
+  hipError_t e = launch_softmax(a, nullptr, stream);
+  if (e != hipSuccess) return e;
+  return launch_gemm<true>(static_cast<const u16*>(a.v), static_cast<const u16*>(a.w), static_cast<const u16*>(a.g),
+                           static_cast<u16*>(a.o), a, stream);
+}
+
+hipError_t launch_pwa_bwd(const PwaArgs& args, bool /*bf16*/, hipStream_t stream) {
+  PwaArgs a = args;
+  const size_t plane = (size_t)a.H * a.N * a.N;
+  u16* w = static_cast<u16*>(a.w);
+  u16* wt = w + plane;
+  PwaArgs sa = a;
+  sa.lse_w = nullptr;  // the backward reuses the caller's lse_w; only w, w^T are rebuilt
+  hipError_t e = launch_softmax(sa, wt, stream);
+  if (e != hipSuccess) return e;
+  {
+    const size_t n8 = (size_t)a.S * a.N * a.H * a.d / 8;
+    hipLaunchKernelGGL(pwa_bwd_pre_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  e = launch_gemm<false>(static_cast<const u16*>(a.da), wt, nullptr, static_cast<u16*>(a.dv), a, stream);
+  if (e != hipSuccess) return e;
+  {
+    const int dp = a.d <= 32 ? 32 : 64;
+    const int nt1 = (a.N + 255) / 256;
+    const int spc = ((a.S + a.P - 1) / a.P + 1) & ~1;  // even number of MSA rows per chunk
+    // chunks past the end write zero partials, so every one of the P slots is defined
+    const dim3 grid((unsigned)((long long)nt1 * nt1 * a.H * a.P));
+    if (dp == 32)
+      hipLaunchKernelGGL(pwa_dw_kernel<32>, grid, dim3(512), 0, stream, static_cast<const u16*>(a.da),
+                         static_cast<const u16*>(a.v), a.partial, a.S, a.N, a.H, a.d, a.P, spc, nt1);
+    else
+      hipLaunchKernelGGL(pwa_dw_kernel<64>, grid, dim3(512), 0, stream, static_cast<const u16*>(a.da),
+                         static_cast<const u16*>(a.v), a.partial, a.S, a.N, a.H, a.d, a.P, spc, nt1);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  {
+    const long long rows = (long long)a.H * a.N;
+    hipLaunchKernelGGL(pwa_db_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+}  // namespace pba

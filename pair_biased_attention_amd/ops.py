@@ -1,0 +1,127 @@
+"""PyTorch-facing wrappers with the names of the C ABI.
+
+PyTorch supplies device memory and the current HIP stream; every step of the
+computation runs in libpba's kernels.  Layouts (contiguous, row-major):
+  attention  q, k, v, g, out, dout, dq, dk, dv, dg: [B, H, N, d]; bias, dbias: [H, N, N]
+  pair-weighted average  v, g, out, dout, dv, dg: [S, N, H, d]; b, db: [H, N, N]
+  key_mask: [N] uint8 (0 = masked) or None.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_DT = {torch.float32: _lib.PBA_F32, torch.bfloat16: _lib.PBA_BF16}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev):
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check_tensors(ref: torch.Tensor, named: dict, shapes: dict):
+    if ref.dtype not in _DT:
+        raise TypeError(f"unsupported dtype {ref.dtype}")
+    if ref.device.type != "cuda":
+        raise ValueError("pba kernels run on the GPU; got a tensor on " + str(ref.device))
+    for name, t in named.items():
+        if t is None:
+            continue
+        want_dtype = torch.uint8 if name == "key_mask" else (torch.float32 if name.startswith("lse") else ref.dtype)
+        if t.dtype != want_dtype:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {want_dtype}")
+        if t.device != ref.device:
+            raise ValueError(f"{name} is on {t.device}, expected {ref.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        if name in shapes and tuple(t.shape) != tuple(shapes[name]):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shapes[name])}")
+
+
+def pba_forward(q, k, v, g, bias, key_mask=None):
+    """Pair-biased gated attention forward; returns (out, lse)."""
+    lib = _lib.load()
+    B, H, N, d = q.shape
+    shp = {"q": (B, H, N, d), "k": (B, H, N, d), "v": (B, H, N, d), "g": (B, H, N, d),
+           "bias": (H, N, N), "key_mask": (N,)}
+    _check_tensors(q, dict(q=q, k=k, v=v, g=g, bias=bias, key_mask=key_mask), shp)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = lib.pba_forward(B, H, N, d, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bias),
+                         _ptr(key_mask), _ptr(out), _ptr(lse), _stream(q.device))
+    _lib.check("pba_forward", st)
+    return out, lse
+
+
+def pba_backward_workspace_bytes(B, H, N, d, dtype) -> int:
+    return int(_lib.load().pba_backward_workspace_bytes(B, H, N, d, _DT[dtype]))
+
+
+def pba_backward(q, k, v, g, bias, key_mask, out, lse, dout, workspace=None):
+    """Backward; returns dict(dq, dk, dv, dg, dbias).  dbias is summed over B."""
+    lib = _lib.load()
+    B, H, N, d = q.shape
+    shp = {n: (B, H, N, d) for n in ("q", "k", "v", "g", "out", "dout")}
+    shp.update(bias=(H, N, N), key_mask=(N,), lse=(B, H, N))
+    _check_tensors(q, dict(q=q, k=k, v=v, g=g, bias=bias, key_mask=key_mask, out=out, lse=lse,
+                           dout=dout), shp)
+    nbytes = lib.pba_backward_workspace_bytes(B, H, N, d, _DT[q.dtype])
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq, dk, dv, dg = (torch.empty_like(q) for _ in range(4))
+    dbias = torch.empty_like(bias)
+    st = lib.pba_backward(B, H, N, d, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bias),
+                          _ptr(key_mask), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                          _ptr(dv), _ptr(dg), _ptr(dbias), _ptr(workspace), workspace.numel(),
+                          _stream(q.device))
+    _lib.check("pba_backward", st)
+    return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dbias": dbias}
+
+
+def pair_weighted_avg_workspace_bytes(S, N, H, d, dtype) -> int:
+    return int(_lib.load().pair_weighted_avg_workspace_bytes(S, N, H, d, _DT[dtype]))
+
+
+def pair_weighted_avg(b, v, g, key_mask=None, workspace=None):
+    """MSA pair-weighted average forward; returns (out, lse_w)."""
+    lib = _lib.load()
+    S, N, H, d = v.shape
+    _check_tensors(v, dict(b=b, v=v, g=g, key_mask=key_mask),
+                   {"b": (H, N, N), "v": (S, N, H, d), "g": (S, N, H, d), "key_mask": (N,)})
+    nbytes = lib.pair_weighted_avg_workspace_bytes(S, N, H, d, _DT[v.dtype])
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=v.device)
+    out = torch.empty_like(v)
+    lse_w = torch.empty((H, N), dtype=torch.float32, device=v.device)
+    st = lib.pair_weighted_avg(S, N, H, d, _DT[v.dtype], _ptr(b), _ptr(key_mask), _ptr(v), _ptr(g),
+                               _ptr(out), _ptr(lse_w), _ptr(workspace), workspace.numel(),
+                               _stream(v.device))
+    _lib.check("pair_weighted_avg", st)
+    return out, lse_w
+
+
+def pair_weighted_avg_backward_workspace_bytes(S, N, H, d, dtype) -> int:
+    return int(_lib.load().pair_weighted_avg_backward_workspace_bytes(S, N, H, d, _DT[dtype]))
+
+
+def pair_weighted_avg_backward(b, v, g, key_mask, out, lse_w, dout, workspace=None):
+    """Backward of the pair-weighted average; returns dict(dv, dg, db)."""
+    lib = _lib.load()
+    S, N, H, d = v.shape
+    shp = {n: (S, N, H, d) for n in ("v", "g", "out", "dout")}
+    shp.update(b=(H, N, N), key_mask=(N,), lse_w=(H, N))
+    _check_tensors(v, dict(b=b, v=v, g=g, key_mask=key_mask, out=out, lse_w=lse_w, dout=dout), shp)
+    nbytes = lib.pair_weighted_avg_backward_workspace_bytes(S, N, H, d, _DT[v.dtype])
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=v.device)
+    dv, dg = torch.empty_like(v), torch.empty_like(g)
+    db = torch.empty_like(b)
+    st = lib.pair_weighted_avg_backward(S, N, H, d, _DT[v.dtype], _ptr(b), _ptr(key_mask), _ptr(v),
+                                        _ptr(g), _ptr(out), _ptr(lse_w), _ptr(dout), _ptr(dv), _ptr(dg),
+                                        _ptr(db), _ptr(workspace), workspace.numel(), _stream(v.device))
+    _lib.check("pair_weighted_avg_backward", st)
+    return {"dv": dv, "dg": dg, "db": db}

@@ -1,0 +1,138 @@
+"""The C-ABI library without a GPU: it loads, exports every symbol that
+include/pba.h declares, sizes workspaces, and rejects invalid calls with the
+documented status codes before touching the HIP runtime."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from pair_biased_attention_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pba.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS = 0, 1, 2, 3, 4, 5
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", src, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail(f"libpba.so is not built ({_lib.LIB_PATH}); run __graft_entry__.build()")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for fn in ("pba_forward", "pba_backward", "pba_backward_workspace_bytes", "pair_weighted_avg",
+               "pair_weighted_avg_backward", "pair_weighted_avg_workspace_bytes",
+               "pair_weighted_avg_backward_workspace_bytes", "pba_status_string", "pba_abi_version"):
+        assert fn in names, fn
+    assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
+
+
+def test_every_declared_symbol_is_exported(lib):
+    raw = ctypes.CDLL(_lib.LIB_PATH)
+    for name in _declared():
+        assert hasattr(raw, name), name
+
+
+def test_version_and_status_strings(lib):
+    assert lib.pba_abi_version() == 1
+    for code in range(7):
+        assert lib.pba_status_string(code)
+    assert b"unknown" in lib.pba_status_string(99)
+
+
+def test_workspace_sizes(lib):
+    # attention: dA (input dtype) + D (fp32) + partials (fp32 [P,H,N,N]); >= the dA part
+    for (B, H, N, d, dt) in [(384, 4, 384, 32, 1), (1, 16, 768, 24, 1), (48, 16, 384, 48, 1), (32, 4, 32, 32, 0)]:
+        ws = lib.pba_backward_workspace_bytes(B, H, N, d, dt)
+        assert ws >= B * H * N * d * (2 if dt else 4) + B * H * N * 4 + H * N * N * 4
+        assert ws % 256 == 0
+    # B = 1: a single partial, equal to dS
+    assert lib.pba_backward_workspace_bytes(1, 16, 768, 24, 1) < 1 * 16 * 768 * 24 * 2 + 16 * 768 * 4 + 2 * 16 * 768 * 768 * 4
+    assert lib.pair_weighted_avg_workspace_bytes(1024, 768, 8, 32, 1) >= 8 * 768 * 768 * 2
+    assert lib.pair_weighted_avg_backward_workspace_bytes(1024, 768, 8, 32, 1) >= 1024 * 768 * 8 * 32 * 2
+    # invalid sizes give 0
+    assert lib.pba_backward_workspace_bytes(0, 4, 384, 32, 1) == 0
+    assert lib.pba_backward_workspace_bytes(1, 4, 384, 30, 1) == 0
+    assert lib.pair_weighted_avg_workspace_bytes(4, 16, 2, 32, 0) == 0  # fp32 not offered for PWA
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: validation fails before use
+
+
+def _fwd(lib, B=2, H=2, N=64, d=32, dt=1, ptrs=None, mask=None):
+    p = [FAKE] * 8 if ptrs is None else ptrs
+    return lib.pba_forward(B, H, N, d, dt, p[0], p[1], p[2], p[3], p[4], mask, p[5], p[6], None)
+
+
+def test_forward_validation(lib):
+    assert _fwd(lib, B=0) == ERR_SHAPE
+    assert _fwd(lib, N=-3) == ERR_SHAPE
+    assert _fwd(lib, d=12) == ERR_UNSUP
+    assert _fwd(lib, d=72) == ERR_UNSUP
+    assert _fwd(lib, dt=7) == ERR_UNSUP
+    for i in range(7):
+        ptrs = [FAKE] * 8
+        ptrs[i] = None
+        assert _fwd(lib, ptrs=ptrs) == ERR_NULL, i
+    for i in range(6):
+        ptrs = [FAKE] * 8
+        ptrs[i] = FAKE + 8
+        assert _fwd(lib, ptrs=ptrs) == ERR_ALIGN, i
+    assert _fwd(lib, B=1 << 20, H=64, N=4096, d=64) == ERR_SHAPE
+
+
+def test_backward_validation(lib):
+    B, H, N, d = 2, 2, 64, 32
+    need = lib.pba_backward_workspace_bytes(B, H, N, d, 1)
+
+    def call(ws=FAKE, wsb=None, null_at=None, misalign_at=None, d_=d):
+        p = [FAKE] * 13
+        if null_at is not None:
+            p[null_at] = None
+        if misalign_at is not None:
+            p[misalign_at] = FAKE + 4
+        return lib.pba_backward(B, H, N, d_, 1, p[0], p[1], p[2], p[3], p[4], None, p[5], p[6], p[7],
+                                p[8], p[9], p[10], p[11], p[12], ws, need if wsb is None else wsb, None)
+
+    assert call(d_=20) == ERR_UNSUP
+    for i in range(13):
+        assert call(null_at=i) == ERR_NULL, i
+    assert call(misalign_at=0) == ERR_ALIGN
+    assert call(ws=None) == ERR_WS
+    assert call(wsb=need - 1) == ERR_WS
+    assert call(ws=FAKE + 8) == ERR_ALIGN
+
+
+def test_pwa_validation(lib):
+    S, N, H, d = 4, 64, 2, 32
+    need = lib.pair_weighted_avg_workspace_bytes(S, N, H, d, 1)
+    f = lambda dt=1, ws=FAKE, wsb=need, p4=FAKE: lib.pair_weighted_avg(
+        S, N, H, d, dt, FAKE, None, FAKE, FAKE, p4, FAKE, ws, wsb, None)
+    assert f(dt=0) == ERR_UNSUP
+    assert f(p4=None) == ERR_NULL
+    assert f(ws=None) == ERR_WS
+    assert f(wsb=need - 2) == ERR_WS
+    needb = lib.pair_weighted_avg_backward_workspace_bytes(S, N, H, d, 1)
+    g = lambda ws=FAKE, wsb=needb, db=FAKE: lib.pair_weighted_avg_backward(
+        S, N, H, d, 1, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, db, ws, wsb, None)
+    assert g(db=None) == ERR_NULL
+    assert g(db=FAKE + 2) == ERR_ALIGN
+    assert g(wsb=needb - 1) == ERR_WS
+
+
+def test_binding_rejects_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    import pair_biased_attention_amd as pba
+    x = torch.zeros(1, 1, 8, 8, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pba.pba_forward(x, x, x, x, torch.zeros(1, 8, 8, dtype=torch.bfloat16))

@@ -405,3 +405,30 @@ def test_workload_recipe_matches_fixture():
     inp = workloads.attention_inputs(tri)
     assert np.all(inp["key_mask"][:365] == 1) and np.all(inp["key_mask"][365:] == 0)
     assert inp["q"].dtype == np.uint16
+
+
+# ------------------------------------------------------- query-row subsets
+
+def test_query_row_subset_matches_full():
+    """The general (Nq != Nk) form on a subset of query rows gives those rows
+    of the full result; the dBias rows still sum over every batch row."""
+    q, k, v, g, bias, keep, dout = _tiny(B=3, H=2, N=7, d=4, masked=(2,))
+    rows = np.array([0, 5, 6])
+    O, L = oracle.attention_forward(q, k, v, g, bias, keep)
+    gr = oracle.attention_backward(q, k, v, g, bias, keep, dout)
+    Os, Ls = oracle.attention_forward(q[:, :, rows], k, v, g[:, :, rows], bias[:, rows], keep)
+    grs = oracle.attention_backward(q[:, :, rows], k, v, g[:, :, rows], bias[:, rows], keep,
+                                    dout[:, :, rows])
+    np.testing.assert_allclose(Os, O[:, :, rows], atol=1e-15)
+    np.testing.assert_allclose(Ls, L[:, :, rows], atol=1e-15)
+    np.testing.assert_allclose(grs["dq"], gr["dq"][:, :, rows], atol=1e-15)
+    np.testing.assert_allclose(grs["dbias"], gr["dbias"][:, rows], atol=1e-14)
+    b, v2, g2, keep2, dout2 = _tiny_pwa(S=3, N=8, H=2, d=3, masked=(4,))
+    Op, lp = oracle.pwa_forward(b, v2, g2, keep2)
+    gp = oracle.pwa_backward(b, v2, g2, keep2, dout2)
+    Ops, lps = oracle.pwa_forward(b[:, rows], v2, g2[:, rows], keep2)
+    gps = oracle.pwa_backward(b[:, rows], v2, g2[:, rows], keep2, dout2[:, rows])
+    np.testing.assert_allclose(Ops, Op[:, rows], atol=1e-15)
+    np.testing.assert_allclose(lps, lp[:, rows], atol=1e-15)
+    np.testing.assert_allclose(gps["db"], gp["db"][:, rows], atol=1e-14)
+    np.testing.assert_allclose(gps["dg"], gp["dg"][:, rows], atol=1e-15)

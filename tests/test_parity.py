@@ -1,0 +1,312 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Bar: per output tensor, max |gpu - oracle| <= tol * max |oracle| with
+tol = 1e-4 for fp32 inputs and 2e-2 for bf16 inputs (fp32 accumulation);
+masked positions and fully-masked rows bit-exact.  Small cases compare every
+element; the full-size workloads compare sampled batch rows exactly (each
+batch row is independent) and sampled bias-gradient rows, which the oracle
+sums over every batch row.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL, assert_close, bits_to_f64, check_all, log, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import pair_biased_attention_amd._lib as L
+    L.load()  # fails loudly if the library is missing
+
+
+import pair_biased_attention_amd as pba  # noqa: E402
+
+
+# ----------------------------------------------------------------- helpers
+
+def _attn_case(B, H, N, d, dtype, mask, seed):
+    cfg = workloads.AttnConfig("case", B=B, H=H, N=N, d=d, dtype=dtype, mask=mask, seed=seed)
+    return workloads.attention_inputs(cfg)
+
+
+def _run_attn(inp, dtype):
+    dev = {n: to_dev(inp[n], dtype) for n in ("q", "k", "v", "g", "bias", "dout")}
+    km = None if inp["key_mask"] is None else to_dev(inp["key_mask"], dtype)
+    out, lse = pba.pba_forward(dev["q"], dev["k"], dev["v"], dev["g"], dev["bias"], km)
+    grads = pba.pba_backward(dev["q"], dev["k"], dev["v"], dev["g"], dev["bias"], km, out, lse, dev["dout"])
+    torch.cuda.synchronize()
+    res = {"out": to_f64(out), "lse": lse.cpu().numpy().astype(np.float64)}
+    res.update({k: to_f64(v) for k, v in grads.items()})
+    return res
+
+
+def _check_attn_full(inp, res, dtype, tag):
+    tol = TOL[dtype]
+    O, L = oracle.attention_forward(inp["q64"], inp["k64"], inp["v64"], inp["g64"], inp["bias64"], inp["key_mask"])
+    gr = oracle.attention_backward(inp["q64"], inp["k64"], inp["v64"], inp["g64"], inp["bias64"],
+                                   inp["key_mask"], inp["dout64"])
+    # D = rowsum(dO * O) is formed from O in the storage dtype, so dS carries an
+    # absolute error of order eps * |dO| |O| even where the exact dS is 0
+    # (a single kept key); the bar for dq, dk, dbias is then taken relative to
+    # the magnitude of dV, the gradient that does not vanish.
+    floor = float(np.max(np.abs(gr["dv"])))
+    pairs = {"out": (res["out"], O), "lse": (res["lse"], L)}
+    pairs.update({n: (res[n], gr[n]) for n in ("dq", "dk", "dv", "dg", "dbias")})
+    check_all(tag, pairs, tol, {n: floor for n in ("dq", "dk", "dbias")})
+    return gr
+
+
+# ----------------------------------------------------------------- attention, small
+
+SMALL_ATTN = [
+    # B, H, N, d, dtype, mask
+    (3, 2, 200, 32, "bf16", "tail:7"),       # ragged N, tail mask, several key blocks
+    (2, 3, 130, 24, "bf16", "random:10"),    # d padded 24 -> 32
+    (2, 2, 96, 48, "bf16", "none"),          # d = 48 (three 16-wide column tiles)
+    (2, 2, 77, 64, "bf16", "random:5"),
+    (2, 2, 70, 8, "bf16", "none"),
+    (1, 2, 150, 16, "bf16", "random:4"),     # B = 1: the bias gradient is dS itself
+    (40, 1, 64, 32, "bf16", "tail:3"),       # several batch chunks and partials
+    (4, 2, 100, 32, "f32", "random:9"),
+    (2, 2, 65, 48, "f32", "none"),
+    (3, 1, 33, 64, "f32", "random:2"),
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,dtype,mask", SMALL_ATTN)
+def test_attention_small(B, H, N, d, dtype, mask):
+    log(f"attention small B={B} H={H} N={N} d={d} {dtype} mask={mask}")
+    inp = _attn_case(B, H, N, d, dtype, mask, seed=100 + N + d)
+    res = _run_attn(inp, dtype)
+    gr = _check_attn_full(inp, res, dtype, f"small[{B},{H},{N},{d},{dtype}]")
+    if inp["key_mask"] is not None:
+        dead = inp["key_mask"] == 0
+        assert np.all(res["dk"][:, :, dead] == 0) and np.all(res["dv"][:, :, dead] == 0)
+        assert np.all(res["dbias"][:, :, dead] == 0)
+        assert np.all(gr["dk"][:, :, dead] == 0)
+
+
+# ----------------------------------------------------------------- attention, full workloads
+
+def _sample_rows(N):
+    return np.array(sorted({0, 1, N // 3, N // 2 + 1, N - 20 if N > 20 else 0, N - 1}))
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "tri_attn_n384", "pairformer_apb", "dit_apb_x48"])
+def test_attention_workload(name):
+    cfg = workloads.CONFIGS[name]
+    dtype = cfg.dtype
+    tol = TOL[dtype]
+    log(f"attention workload {name}: B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} {dtype} mask={cfg.mask}")
+    inp = workloads.attention_inputs(cfg)
+    res = _run_attn(inp, dtype)
+    if cfg.B * cfg.H * cfg.N * cfg.N <= 4_000_000:
+        _check_attn_full(inp, res, dtype, name)
+        return
+    # every batch row is independent: compare a sample of rows completely
+    bs = np.array(sorted({b for b in (0, 1, cfg.B // 2, cfg.B - 1) if b < cfg.B}))
+    sub = {n: inp[n + "64"][bs] for n in ("q", "k", "v", "g", "dout")}
+    O, L = oracle.attention_forward(sub["q"], sub["k"], sub["v"], sub["g"], inp["bias64"], inp["key_mask"])
+    gr = oracle.attention_backward(sub["q"], sub["k"], sub["v"], sub["g"], inp["bias64"], inp["key_mask"], sub["dout"])
+    # bias gradient: sampled query rows, summed by the oracle over every batch row
+    rows = _sample_rows(cfg.N)
+    grr = oracle.attention_backward(inp["q64"][:, :, rows], inp["k64"], inp["v64"], inp["g64"][:, :, rows],
+                                    inp["bias64"][:, rows], inp["key_mask"], inp["dout64"][:, :, rows])
+    pairs = {"out": (res["out"][bs], O), "lse": (res["lse"][bs], L)}
+    pairs.update({n: (res[n][bs], gr[n]) for n in ("dq", "dk", "dv", "dg")})
+    pairs["dbias_rows"] = (res["dbias"][:, rows], grr["dbias"])
+    check_all(name, pairs, tol)
+    if inp["key_mask"] is not None:
+        dead = inp["key_mask"] == 0
+        assert np.all(res["dk"][:, :, dead] == 0) and np.all(res["dv"][:, :, dead] == 0)
+        assert np.all(res["dbias"][:, :, dead] == 0)
+
+
+# ----------------------------------------------------------------- edge cases
+
+def test_fully_masked_keys_and_single_key():
+    log("edge: fully masked and single kept key")
+    for dtype in ("bf16", "f32"):
+        inp = _attn_case(2, 2, 40, 32, dtype, "none", seed=5)
+        inp["key_mask"] = np.zeros(40, np.uint8)
+        res = _run_attn(inp, dtype)
+        assert np.all(res["out"] == 0) and np.all(np.isneginf(res["lse"]))
+        for n in ("dq", "dk", "dv", "dg", "dbias"):
+            assert np.all(res[n] == 0), (dtype, n)
+        km = np.zeros(40, np.uint8)
+        km[17] = 1
+        inp["key_mask"] = km
+        res = _run_attn(inp, dtype)
+        _check_attn_full(inp, res, dtype, f"single-key {dtype}")
+
+
+def test_tiny_sizes():
+    for (B, H, N, d) in [(1, 1, 1, 8), (1, 1, 2, 8), (2, 1, 3, 16), (1, 3, 17, 64)]:
+        for dtype in ("bf16", "f32"):
+            log(f"edge: tiny B={B} H={H} N={N} d={d} {dtype}")
+            inp = _attn_case(B, H, N, d, dtype, "none", seed=9)
+            res = _run_attn(inp, dtype)
+            _check_attn_full(inp, res, dtype, f"tiny[{B},{H},{N},{d},{dtype}]")
+
+
+def test_reduction_to_plain_attention_on_gpu():
+    """bias = 0, G = 40 turns the kernel into plain attention; compare with a
+    float32 CPU attention computed by PyTorch's own routine."""
+    log("special: bias 0, gate 40 vs torch scaled_dot_product_attention (fp32, CPU)")
+    inp = _attn_case(3, 2, 150, 32, "bf16", "random:6", seed=21)
+    inp["g"] = workloads.bf16_round_bits(np.full(inp["q"].shape, 40.0, np.float32))
+    inp["bias"] = workloads.bf16_round_bits(np.zeros(inp["bias"].shape, np.float32))
+    res = _run_attn(inp, "bf16")
+    q, k, v = (torch.from_numpy(bits_to_f64(inp[n], "bf16")).float() for n in ("q", "k", "v"))
+    mask = torch.from_numpy(inp["key_mask"] != 0).view(1, 1, 1, -1).expand(3, 2, 150, 150)
+    ref = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=mask).double().numpy()
+    assert_close("plain attention", res["out"], ref, TOL["bf16"])
+
+
+def test_zero_query_key_attention_equals_pwa_on_gpu():
+    """Q = K = 0: the attention kernels and the pair-weighted-average kernels
+    compute the same function (on transposed layouts)."""
+    log("special: attention with Q=K=0 vs pair-weighted average")
+    S, N, H, d = 4, 130, 2, 32
+    pin = workloads.pwa_inputs(workloads.PwaConfig("eq", S=S, N=N, H=H, d=d, dtype="bf16", mask="none", seed=33))
+    t = lambda x: np.ascontiguousarray(np.transpose(x, (0, 2, 1, 3)))
+    z = np.zeros((S, H, N, d), np.uint16)
+    ainp = {"q": z, "k": z, "v": t(pin["v"]), "g": t(pin["g"]), "bias": pin["b"], "dout": t(pin["dout"]),
+            "key_mask": None}
+    ares = _run_attn(ainp, "bf16")
+    pres = _run_pwa(pin)
+    tol = TOL["bf16"]
+    assert_close("Q=K=0 out", t(pres["out"]), ares["out"], tol)
+    assert_close("Q=K=0 dv", t(pres["dv"]), ares["dv"], tol)
+    assert_close("Q=K=0 dg", t(pres["dg"]), ares["dg"], tol)
+    assert_close("Q=K=0 db", pres["db"], ares["dbias"], tol)
+
+
+# ----------------------------------------------------------------- determinism and guard bands
+
+def test_backward_is_bitwise_deterministic():
+    log("determinism: two identical attention backward and PWA backward calls")
+    inp = _attn_case(64, 4, 384, 32, "bf16", "tail:19", seed=77)
+    r1 = _run_attn(inp, "bf16")
+    r2 = _run_attn(inp, "bf16")
+    diff = [n for n in r1 if not np.array_equal(r1[n], r2[n], equal_nan=True)]
+    assert not diff, f"attention outputs differ between identical calls: {diff}"
+    pin = workloads.pwa_inputs(workloads.PwaConfig("det", S=16, N=256, H=2, d=32, dtype="bf16", mask="none", seed=3))
+    p1, p2 = _run_pwa(pin), _run_pwa(pin)
+    diff = [n for n in p1 if not np.array_equal(p1[n], p2[n])]
+    assert not diff, f"pwa outputs differ between identical calls: {diff}"
+
+
+def test_outputs_stay_inside_their_buffers():
+    """Raw C-ABI call with every output placed inside a larger canary-filled buffer."""
+    log("guard bands: raw pba_forward / pba_backward")
+    import pair_biased_attention_amd._lib as L
+    lib = L.load()
+    B, H, N, d = 3, 2, 100, 24
+    inp = _attn_case(B, H, N, d, "bf16", "random:5", seed=8)
+    dev = {n: to_dev(inp[n], "bf16") for n in ("q", "k", "v", "g", "bias", "dout")}
+    km = to_dev(inp["key_mask"], "bf16")
+    G = 4096  # guard elements on each side (16-byte aligned offsets)
+    canary = -12352.0  # exactly representable in bf16 and fp32
+
+    def guarded(n_elem, dtype):
+        buf = torch.full((n_elem + 2 * G,), canary, dtype=dtype, device="cuda")
+        return buf, buf[G:G + n_elem]
+
+    nt = B * H * N * d
+    bufs = {n: guarded(nt, torch.bfloat16) for n in ("out", "dq", "dk", "dv", "dg")}
+    bufs["dbias"] = guarded(H * N * N, torch.bfloat16)
+    bufs["lse"] = guarded(B * H * N, torch.float32)
+    wsb = lib.pba_backward_workspace_bytes(B, H, N, d, 1)
+    p = lambda t: t.data_ptr()
+    st = lib.pba_forward(B, H, N, d, 1, p(dev["q"]), p(dev["k"]), p(dev["v"]), p(dev["g"]), p(dev["bias"]),
+                         p(km), p(bufs["out"][1]), p(bufs["lse"][1]), None)
+    assert st == 0
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    st = lib.pba_backward(B, H, N, d, 1, p(dev["q"]), p(dev["k"]), p(dev["v"]), p(dev["g"]), p(dev["bias"]),
+                          p(km), p(bufs["out"][1]), p(bufs["lse"][1]), p(dev["dout"]), p(bufs["dq"][1]),
+                          p(bufs["dk"][1]), p(bufs["dv"][1]), p(bufs["dg"][1]), p(bufs["dbias"][1]),
+                          p(ws), wsb, None)
+    assert st == 0
+    torch.cuda.synchronize()
+    for n, (buf, _) in bufs.items():
+        head, tail = buf[:G].float().cpu(), buf[-G:].float().cpu()
+        assert torch.all(head == canary) and torch.all(tail == canary), n
+    O, _ = oracle.attention_forward(inp["q64"], inp["k64"], inp["v64"], inp["g64"], inp["bias64"], inp["key_mask"])
+    assert_close("guarded out", to_f64(bufs["out"][1]).reshape(O.shape), O, TOL["bf16"])
+
+
+# ----------------------------------------------------------------- pair-weighted average
+
+def _run_pwa(inp):
+    dev = {n: to_dev(inp[n], "bf16") for n in ("b", "v", "g", "dout")}
+    km = None if inp["key_mask"] is None else to_dev(inp["key_mask"], "bf16")
+    out, lse = pba.pair_weighted_avg(dev["b"], dev["v"], dev["g"], km)
+    grads = pba.pair_weighted_avg_backward(dev["b"], dev["v"], dev["g"], km, out, lse, dev["dout"])
+    torch.cuda.synchronize()
+    res = {"out": to_f64(out), "lse": lse.cpu().numpy().astype(np.float64)}
+    res.update({k: to_f64(v) for k, v in grads.items()})
+    return res
+
+
+SMALL_PWA = [
+    # S, N, H, d, mask
+    (6, 200, 2, 32, "none"),
+    (5, 90, 3, 64, "random:7"),
+    (9, 300, 2, 24, "tail:11"),
+    (3, 257, 1, 48, "none"),
+    (1, 64, 2, 8, "none"),
+]
+
+
+@pytest.mark.parametrize("S,N,H,d,mask", SMALL_PWA)
+def test_pwa_small(S, N, H, d, mask):
+    log(f"pwa small S={S} N={N} H={H} d={d} mask={mask}")
+    inp = workloads.pwa_inputs(workloads.PwaConfig("case", S=S, N=N, H=H, d=d, dtype="bf16", mask=mask,
+                                                   seed=200 + N))
+    res = _run_pwa(inp)
+    tol = TOL["bf16"]
+    O, L = oracle.pwa_forward(inp["b64"], inp["v64"], inp["g64"], inp["key_mask"])
+    gr = oracle.pwa_backward(inp["b64"], inp["v64"], inp["g64"], inp["key_mask"], inp["dout64"])
+    pairs = {"out": (res["out"], O), "lse": (res["lse"], L)}
+    pairs.update({n: (res[n], gr[n]) for n in ("dv", "dg", "db")})
+    check_all(f"pwa[{S},{N},{H},{d}]", pairs, tol)
+    if inp["key_mask"] is not None:
+        dead = inp["key_mask"] == 0
+        assert np.all(res["dv"][:, dead] == 0) and np.all(res["db"][:, :, dead] == 0)
+
+
+def test_pwa_workload():
+    cfg = workloads.CONFIGS["msa_pwa"]
+    log(f"pwa workload: S={cfg.S} N={cfg.N} H={cfg.H} d={cfg.d}")
+    inp = workloads.pwa_inputs(cfg, with_f64=False)
+    res = _run_pwa(inp)
+    tol = TOL["bf16"]
+    f64 = lambda x: bits_to_f64(x, "bf16")
+    b64 = f64(inp["b"])
+    ss = np.array([0, 1, 517, cfg.S - 1])
+    v_s, g_s, do_s = f64(inp["v"][ss]), f64(inp["g"][ss]), f64(inp["dout"][ss])
+    O, L = oracle.pwa_forward(b64, v_s, g_s, None)
+    gr = oracle.pwa_backward(b64, v_s, g_s, None, do_s)
+    pairs = {"out": (res["out"][ss], O), "lse": (res["lse"], L), "dv": (res["dv"][ss], gr["dv"]),
+             "dg": (res["dg"][ss], gr["dg"])}
+    del v_s, g_s, do_s
+    # db rows reduce over all 1024 MSA rows
+    rows = np.array([0, 5, 400, cfg.N - 1])
+    v_all = f64(inp["v"])
+    grr = oracle.pwa_backward(b64[:, rows], v_all, f64(inp["g"][:, rows]), None, f64(inp["dout"][:, rows]))
+    pairs["db_rows"] = (res["db"][:, rows], grr["db"])
+    check_all("msa_pwa", pairs, tol)
