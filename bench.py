@@ -1,0 +1,225 @@
+#!/usr/bin/env python3
+"""Throughput of the pair-biased attention hot path on one MI355X.
+
+A step is one forward + backward pass of pair-biased gated attention over one
+batch of the triangle-attention workload (B=384 rows, N=384 tokens, H=4
+heads, d=32, bf16 in / fp32 accumulate, last 19 keys masked): pba_forward then
+pba_backward, i.e. every kernel of the attention path.  The pair-weighted
+average (S=1024 MSA rows, N=768, H=8, d=32) is timed in its own loop and
+reported in the same JSON line under "pair_avg".
+
+Prints one JSON line (see the design doc for the definitions of every figure).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import workloads  # noqa: E402
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def attn_flops(B, H, N, d):
+    """Algorithmic flops of forward + backward: 4 + 10 = 14 * B*H*N^2*d."""
+    return 14.0 * B * H * N * N * d
+
+
+def attn_fwd_flops(B, H, N, d):
+    return 4.0 * B * H * N * N * d
+
+
+def pwa_bytes(S, N, H, d, elt=2):
+    """Algorithmic HBM bytes of PWA forward + backward.
+
+    forward reads V, G, b and writes O (3T + b); backward reads dO, O, G, V and
+    b and writes dV, dG and db (6T + 2b).  T = S*N*H*d elements.
+    """
+    T = S * N * H * d * elt
+    b = H * N * N * elt
+    return 9 * T + 3 * b
+
+
+def pwa_fwd_bytes(S, N, H, d, elt=2):
+    T = S * N * H * d * elt
+    return 3 * T + H * N * N * elt
+
+
+def pwa_flops(S, N, H, d):
+    return 6.0 * S * H * N * N * d
+
+
+def to_dev(arr, torch):
+    if arr.dtype == np.uint8:
+        return torch.from_numpy(arr).cuda()
+    return torch.from_numpy(arr.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def time_loop(fn, steps, warmup, torch):
+    """Warm up, then time `steps` calls with HIP events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(steps):
+        fn()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    return t0.elapsed_time(t1) / steps, wall
+
+
+def cpu_baseline(cfg, target_s=15.0):
+    """The fp64 oracle on a bounded sample of the same workload (rows of B)."""
+    import oracle  # test infrastructure: used only for this baseline leg
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=None)
+    except Exception:
+        pass
+    cores = len(os.sched_getaffinity(0))
+    B = 4
+    while True:
+        sub = workloads.scaled_attention_config(cfg, B=B)
+        inp = workloads.attention_inputs(sub)
+        t = time.perf_counter()
+        oracle.attention_forward(inp["q64"], inp["k64"], inp["v64"], inp["g64"], inp["bias64"], inp["key_mask"])
+        oracle.attention_backward(inp["q64"], inp["k64"], inp["v64"], inp["g64"], inp["bias64"],
+                                  inp["key_mask"], inp["dout64"])
+        dt = time.perf_counter() - t
+        if dt * 2 > target_s or B >= cfg.B:
+            break
+        B = min(cfg.B, max(B * 2, int(B * target_s / max(dt, 1e-3) * 0.9)))
+    flops = attn_flops(B, cfg.H, cfg.N, cfg.d)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads or cores, "kind": "oracle",
+            "sample": f"{B} of {cfg.B} rows (B), fwd+bwd, fp64 NumPy, {dt:.2f} s; host {platform.processor() or platform.machine()}, "
+                      f"{cores} cores visible, BLAS threads {threads}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--pwa-steps", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-pwa", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (no sharding, no collectives); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import pair_biased_attention_amd as pba
+    from pair_biased_attention_amd import _lib
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    _lib.load()  # fails loudly without the HIP library
+
+    cfg = workloads.CONFIGS["tri_attn_n384"]
+    B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
+    inp = workloads.attention_inputs(cfg, with_f64=False)
+    t = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "g", "bias", "dout")}
+    km = to_dev(inp["key_mask"], torch)
+    ws = torch.empty(pba.pba_backward_workspace_bytes(B, H, N, d, torch.bfloat16), dtype=torch.uint8, device="cuda")
+    state = {}
+
+    def fwd():
+        state["out"], state["lse"] = pba.pba_forward(t["q"], t["k"], t["v"], t["g"], t["bias"], km)
+
+    def step():
+        fwd()
+        pba.pba_backward(t["q"], t["k"], t["v"], t["g"], t["bias"], km, state["out"], state["lse"], t["dout"],
+                         workspace=ws)
+
+    ms_step, wall = time_loop(step, args.steps, args.warmup, torch)
+    ms_fwd, _ = time_loop(fwd, args.steps, 2, torch)
+    flops = attn_flops(B, H, N, d)
+    value = flops / (ms_step * 1e-3) / 1e12
+    fwd_tflops = attn_fwd_flops(B, H, N, d) / (ms_fwd * 1e-3) / 1e12
+
+    result = {
+        "metric": "fwd+bwd TFLOP/s & %MFMA peak (N=384 tri-attn); GB/s & %HBM (pair-avg)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "tri_attn_n384: triangle attention fwd+bwd, B=384 rows, N=384, H=4, d=32, "
+                               "bf16 in / fp32 accumulate, last 19 keys masked, bias [4,384,384] broadcast over rows",
+                   "B": B, "H": H, "N": N, "d": d, "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
+        "mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
+        "wall_s_timed": round(wall, 3),
+        # the forward kernel is the one launch pba_forward makes, so HIP events
+        # around the call time that kernel alone
+        "roofline": {"kernel": "attn_fwd_bf16_kernel<32,2>", "bound": "mfma", "achieved": round(fwd_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "ms_per_launch": round(ms_fwd, 4), "traffic": None},
+    }
+
+    if not args.no_pwa:
+        del t, state, ws
+        torch.cuda.empty_cache()
+        pc = workloads.CONFIGS["msa_pwa"]
+        pin = workloads.pwa_inputs(pc, with_f64=False)
+        pt = {n: to_dev(pin[n], torch) for n in ("b", "v", "g", "dout")}
+        del pin
+        pws_f = torch.empty(pba.pair_weighted_avg_workspace_bytes(pc.S, pc.N, pc.H, pc.d, torch.bfloat16),
+                            dtype=torch.uint8, device="cuda")
+        pws_b = torch.empty(pba.pair_weighted_avg_backward_workspace_bytes(pc.S, pc.N, pc.H, pc.d, torch.bfloat16),
+                            dtype=torch.uint8, device="cuda")
+        pst = {}
+
+        def pfwd():
+            pst["out"], pst["lse"] = pba.pair_weighted_avg(pt["b"], pt["v"], pt["g"], None, workspace=pws_f)
+
+        def pstep():
+            pfwd()
+            pba.pair_weighted_avg_backward(pt["b"], pt["v"], pt["g"], None, pst["out"], pst["lse"], pt["dout"],
+                                           workspace=pws_b)
+
+        ms_p, _ = time_loop(pstep, args.pwa_steps, 2, torch)
+        ms_pf, _ = time_loop(pfwd, args.pwa_steps, 2, torch)
+        gbs = pwa_bytes(pc.S, pc.N, pc.H, pc.d) / (ms_p * 1e-3) / 1e9
+        gbs_f = pwa_fwd_bytes(pc.S, pc.N, pc.H, pc.d) / (ms_pf * 1e-3) / 1e9
+        result["pair_avg"] = {
+            "workload": "msa_pwa: S=1024 MSA rows, N=768, H=8, d=32, bf16, fwd+bwd",
+            "value": round(gbs, 1), "unit": "GB/s", "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "ms_per_step": round(ms_p, 4),
+            "tflops": round(pwa_flops(pc.S, pc.N, pc.H, pc.d) / (ms_p * 1e-3) / 1e12, 2),
+            "fwd": {"ms": round(ms_pf, 4), "value": round(gbs_f, 1), "unit": "GB/s",
+                    "hbm_frac": round(gbs_f / PEAK_HBM_GBS, 4)},
+        }
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg)
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

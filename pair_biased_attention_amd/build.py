@@ -14,9 +14,14 @@ LIB = os.path.join(LIBDIR, "libpba.so")
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU
 # instructions; plain fp32 VALU code is generated instead.
+# -amdgpu-mfma-vgpr-form: matrix-core results stay in ordinary VGPRs, so the
+# softmax arithmetic on them needs no accumulator-register copies.
+# -fno-honor-nans: no NaN canonicalisation around every max (the kernels
+# never produce NaN from finite inputs).
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form", "-fno-honor-nans",
     "-Wno-unused-result",
 ]
 

@@ -29,46 +29,39 @@ __device__ __forceinline__ void kperm_slot(int kappa, int& t, int& i) {
   i = ((kappa >> 4) << 2) | (kappa & 3);
 }
 
-template <int DP>
-struct FwdSmemBf16 {
-  static constexpr int KC = DP / 32;   // 32-wide k chunks of the QK^T product
-  static constexpr int CT = DP / 16;   // 16-wide output column tiles
-  u32x4 k[2][4 * KC * 64];             // K fragments  [t][kc][lane]
-  u32x4 v[2][CT * 2 * 64];             // V^T fragments [ct][m][lane]
-  uint32_t keep[2][16];                // 64 keep bytes per block
-  int any_masked[2];
-};
-
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
-// 16 contiguous bf16 bias values row[k0 .. k0+15], zero past N.
-__device__ __forceinline__ void load_bias16(const u16* row, int k0, int N, bool vec_ok, u32x4& lo, u32x4& hi) {
-  if (vec_ok && k0 + 16 <= N) {
-    lo = ld16(row + k0);
-    hi = ld16(row + k0 + 8);
-  } else {
-    uint32_t w[8];
+// 16 bias values plane[q][k0 .. k0+15] with element-wise guards (any N);
+// entries outside the [N, N] plane read as zero.
+__device__ __forceinline__ void bias_row16(const u16* plane, int q, int k0, int N, u32x4& lo, u32x4& hi) {
+  uint32_t w[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int k = k0 + 2 * e;
-      const uint32_t a = (k < N) ? row[k] : 0u;
-      const uint32_t b = (k + 1 < N) ? row[k + 1] : 0u;
-      w[e] = a | (b << 16);
-    }
-    lo = u32x4{w[0], w[1], w[2], w[3]};
-    hi = u32x4{w[4], w[5], w[6], w[7]};
+  for (int e = 0; e < 8; ++e) {
+    const int k = k0 + 2 * e;
+    const uint32_t x = (q < N && k < N) ? plane[(size_t)q * N + k] : 0u;
+    const uint32_t y = (q < N && k + 1 < N) ? plane[(size_t)q * N + k + 1] : 0u;
+    w[e] = x | (y << 16);
   }
+  lo = u32x4{w[0], w[1], w[2], w[3]};
+  hi = u32x4{w[4], w[5], w[6], w[7]};
 }
 
 }  // namespace
 
-template <int DP, int QT>
+// One workgroup = 4 waves = 64*QT queries of one (b, h).  LDS holds the
+// current and the next 64-key block of K and V in plain row-major form (row
+// stride DP+8 elements); the K operand of S^T = K Q^T is read row-wise and the
+// V^T operand of O^T = V^T P^T with the transpose read, so staging is two
+// 16-byte copies per thread and no transposition happens in the copy.
+template <int DP, int QT, bool ALIGNED>
 __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
-  using Sm = FwdSmemBf16<DP>;
-  constexpr int KC = Sm::KC, CT = Sm::CT;
+  constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
   constexpr int QW = 16 * QT, QBLK = 4 * QW;
-  constexpr int NCH = DP / 32;  // 16-byte staging chunks per thread per tensor
-  __shared__ Sm sm;
+  constexpr int NCH = DP / 32;  // 16-byte chunks per thread per tensor per block
+  __shared__ __attribute__((aligned(16))) u16 sK[2][64 * RS];
+  __shared__ __attribute__((aligned(16))) u16 sV[2][64 * RS];
+  __shared__ uint32_t sKeep[2][16];
+  __shared__ int sAny[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, ln = lane & 15;
@@ -82,11 +75,12 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
   const u16* K = static_cast<const u16*>(a.k) + bh * N * d;
   const u16* V = static_cast<const u16*>(a.v) + bh * N * d;
   const u16* G = static_cast<const u16*>(a.g) + bh * N * d;
-  const u16* Bias = static_cast<const u16*>(a.bias) + (size_t)h * N * N;
   u16* O = static_cast<u16*>(a.out) + bh * N * d;
   float* LSE = a.lse + bh * N;
   const int q0 = qb * QBLK + wave * QW;
-  const bool bias_vec = (N % 8) == 0;
+  // the head's bias plane; reads past its end return zero
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(static_cast<const u16*>(a.bias) + (size_t)h * N * N,
+                                               (uint32_t)((size_t)N * N * 2));
 
   // ---- staging of one 64-key block: global -> registers -> LDS
   u32x4 rk[NCH], rv[NCH];
@@ -115,25 +109,13 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
     for (int it = 0; it < NCH; ++it) {
       const int c = tid + 256 * it;
       const int kappa = c / (DP / 8), c8 = c % (DP / 8);
-      int t, i;
-      kperm_slot(kappa, t, i);
-      const int kc = c8 >> 2, ga = c8 & 3;
-      sm.k[buf][(t * KC + kc) * 64 + ga * 16 + i] = rk[it];
-      // V^T fragment: lane (gA, i=c%16) of tile (ct, m) holds keys 16gA+8m+v
-      u16* v16 = reinterpret_cast<u16*>(&sm.v[buf][0]);
-      const int gv = kappa >> 4, m = (kappa >> 3) & 1, vv = kappa & 7;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int cc = 8 * c8 + e;
-        const int ct = cc >> 4, ii = cc & 15;
-        const uint32_t word = rv[it][e >> 1];
-        v16[((ct * 2 + m) * 64 + gv * 16 + ii) * 8 + vv] = (u16)((e & 1) ? (word >> 16) : (word & 0xFFFFu));
-      }
+      *reinterpret_cast<u32x4*>(&sK[buf][kappa * RS + 8 * c8]) = rk[it];
+      *reinterpret_cast<u32x4*>(&sV[buf][kappa * RS + 8 * c8]) = rv[it];
     }
     if (tid < 64) {
-      reinterpret_cast<uint8_t*>(&sm.keep[buf][0])[tid] = rkeep ? 1 : 0;
+      reinterpret_cast<uint8_t*>(&sKeep[buf][0])[tid] = rkeep ? 1 : 0;
       const unsigned long long bal = __ballot(!rkeep);
-      if (tid == 0) sm.any_masked[buf] = bal != 0ull;
+      if (tid == 0) sAny[buf] = bal != 0ull;
     }
   };
 
@@ -149,11 +131,8 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
       if (qrow < N && c0 < d) raw = ld16(Q + (size_t)qrow * d + c0);
       u32x4 sc;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float lo = bf2f((u16)(raw[e] & 0xFFFFu)) * a.scale;
-        const float hi = bf2f((u16)(raw[e] >> 16)) * a.scale;
-        sc[e] = pack2(lo, hi);
-      }
+      for (int e = 0; e < 4; ++e)
+        sc[e] = pack2(bf2f((u16)(raw[e] & 0xFFFFu)) * a.scale, bf2f((u16)(raw[e] >> 16)) * a.scale);
       qf[s][kc] = as_bf8(sc);
     }
   }
@@ -171,6 +150,9 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) oacc[s][ct] = zero4;
   }
+  // key row of A-operand row i in score tile t: 16*(i/4) + 4t + (i%4), so the
+  // 16 keys of lane group g are 16g..16g+15 (one 32-byte bias read per lane)
+  const int krow = 16 * (ln >> 2) + (ln & 3);
 
   const int nkb = (N + 63) / 64;
   fetch(0);
@@ -182,42 +164,63 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
     const int kb = blk * 64;
     if (blk + 1 < nkb) fetch(kb + 64);
 
-    const bool masked_blk = sm.any_masked[buf] != 0;
-    uint32_t keepw[4] = {0x01010101u, 0x01010101u, 0x01010101u, 0x01010101u};
+    // key-block operands shared by the wave's query sub-tiles
+    bf16x8 kf[4][KC], vt[CT][2];
+    const u16* tK = sK[buf];
+    const u16* tV = sV[buf];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kf[t][kc] = as_bf8(*reinterpret_cast<const u32x4*>(tK + (krow + 4 * t) * RS + 32 * kc + 8 * g));
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) vt[ct][m] = tr_frag<RS>(tV, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
+
+    // masked keys (and keys past N) get the most negative bias
+    const bool masked_blk = sAny[buf] != 0;
+    u32x4 mlo = u32x4{0, 0, 0, 0}, mhi = u32x4{0, 0, 0, 0};
     if (masked_blk) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) keepw[e] = sm.keep[buf][4 * g + e];
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kw = sKeep[buf][4 * g + e];  // keep bytes of keys 16g+4e .. +3
+        const uint32_t m01 = ((kw & 0xFFu) ? 0u : 0xFFFFu) | ((kw & 0xFF00u) ? 0u : 0xFFFF0000u);
+        const uint32_t m23 = ((kw & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw & 0xFF000000u) ? 0u : 0xFFFF0000u);
+        if (e < 2) { mlo[2 * e] = m01; mlo[2 * e + 1] = m23; }
+        else { mhi[2 * (e - 2)] = m01; mhi[2 * (e - 2) + 1] = m23; }
+      }
     }
 
 #pragma unroll
     for (int s = 0; s < QT; ++s) {
       const int qrow = q0 + 16 * s + ln;
-      u32x4 blo = u32x4{0, 0, 0, 0}, bhi = u32x4{0, 0, 0, 0};
-      if (qrow < N) load_bias16(Bias + (size_t)qrow * N, kb + 16 * g, N, bias_vec, blo, bhi);
-
-      // scores S^T (rows: keys, columns: this wave's queries), bias entered by
-      // the identity product so that no VALU conversion is spent on it
+      u32x4 blo, bhi;
+      if constexpr (ALIGNED) {  // N % 8 == 0: 16-byte aligned rows
+        const uint32_t boff = (uint32_t)(((size_t)qrow * N + kb + 16 * g) * 2);
+        blo = buf_load16(brs, boff);
+        bhi = buf_load16(brs, boff + 16);
+      } else {
+        bias_row16(static_cast<const u16*>(a.bias) + (size_t)h * N * N, qrow, kb + 16 * g, N, blo, bhi);
+      }
+      if (masked_blk) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          blo[e] = (blo[e] & ~mlo[e]) | (kMaskedBias2 & mlo[e]);
+          bhi[e] = (bhi[e] & ~mhi[e]) | (kMaskedBias2 & mhi[e]);
+        }
+      }
+      // scores S^T (rows: keys, columns: this wave's queries); the bias enters
+      // through the identity product so no VALU work converts it
       f32x4 acc[4];
       acc[0] = mfma32(id_lo, as_bf8(blo), zero4);  // keys 16g + 0..3
       acc[1] = mfma32(id_hi, as_bf8(blo), zero4);  // keys 16g + 4..7
       acc[2] = mfma32(id_lo, as_bf8(bhi), zero4);  // keys 16g + 8..11
       acc[3] = mfma32(id_hi, as_bf8(bhi), zero4);  // keys 16g + 12..15
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) acc[t] = mfma32(as_bf8(sm.k[buf][(t * KC + kc) * 64 + lane]), qf[s][kc], acc[t]);
-      }
-
-      if (masked_blk) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int byte = 4 * t + r;  // key 16g + 4t + r
-            if (((keepw[byte >> 2] >> (8 * (byte & 3))) & 0xFFu) == 0u) acc[t][r] = kNegInf;
-          }
-        }
-      }
+        for (int kc = 0; kc < KC; ++kc) acc[t] = mfma32(kf[t][kc], qf[s][kc], acc[t]);
 
       float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
                        fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
@@ -226,25 +229,27 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
       mx = max_over_groups(mx);
       const float mnew = fmaxf(mrun[s], mx);
       if (__any(mnew > mrun[s])) {
-        const float alpha = (mnew == kNegInf) ? 1.f : exp2_fast((mrun[s] - mnew) * kLog2e);
+        const float alpha = exp2_fast((mrun[s] - mnew) * kLog2e);  // 0 when mrun is -inf or masked
+        if (mnew > mrun[s]) {
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) oacc[s][ct] *= alpha;
-        lacc[s] *= alpha;
-        mrun[s] = mnew;
+          for (int ct = 0; ct < CT; ++ct) oacc[s][ct] *= alpha;
+          lacc[s] *= alpha;
+          mrun[s] = mnew;
+        }
       }
-      const float msc = (mrun[s] == kNegInf) ? 0.f : mrun[s] * kLog2e;
+      // a row whose keys so far are all masked keeps P = 0
+      const float msc = (mrun[s] < kMaskedThreshold) ? kPosInf : mrun[s] * kLog2e;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
         for (int r = 0; r < 4; ++r) acc[t][r] = exp2_fast(fmaf(acc[t][r], kLog2e, -msc));
-      }
       // P^T as the B operand: k slot (g, v) <-> key 16g + 8m + v
       const bf16x8 p0 = pack8(acc[0], acc[1]);
       const bf16x8 p1 = pack8(acc[2], acc[3]);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
-        oacc[s][ct] = mfma32(as_bf8(sm.v[buf][(ct * 2 + 0) * 64 + lane]), p0, oacc[s][ct]);
-        oacc[s][ct] = mfma32(as_bf8(sm.v[buf][(ct * 2 + 1) * 64 + lane]), p1, oacc[s][ct]);
+        oacc[s][ct] = mfma32(vt[ct][0], p0, oacc[s][ct]);
+        oacc[s][ct] = mfma32(vt[ct][1], p1, oacc[s][ct]);
       }
       // row sums of the same rounded P, on the matrix core
       lacc[s] = mfma32(ones, p0, lacc[s]);
@@ -470,16 +475,20 @@ hipError_t launch_attn_fwd(const FwdArgs& args, bool bf16, hipStream_t stream) {
     return hipGetLastError();
   }
   // two query sub-tiles per wave when that still leaves enough workgroups
-  const bool qt2 = bhs * ((a.N + 127) / 128) >= 1024;
+  const bool qt2 = dp == 32 && bhs * ((a.N + 127) / 128) >= 1024;
+  const bool al = (a.N % 8) == 0;
   a.nqb = qt2 ? (a.N + 127) / 128 : (a.N + 63) / 64;
   const dim3 grid((unsigned)(bhs * a.nqb));
+#define PBA_FWD_LAUNCH(DPV, QTV, ALV) \
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<DPV, QTV, ALV>), grid, dim3(256), 0, stream, a)
   if (dp == 32) {
-    if (qt2) hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, 2>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<32, 1>), grid, dim3(256), 0, stream, a);
+    if (qt2) { if (al) PBA_FWD_LAUNCH(32, 2, true); else PBA_FWD_LAUNCH(32, 2, false); }
+    else { if (al) PBA_FWD_LAUNCH(32, 1, true); else PBA_FWD_LAUNCH(32, 1, false); }
   } else {
-    if (qt2) hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 2>), grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((attn_fwd_bf16_kernel<64, 1>), grid, dim3(256), 0, stream, a);
+    if (qt2) { if (al) PBA_FWD_LAUNCH(64, 2, true); else PBA_FWD_LAUNCH(64, 2, false); }
+    else { if (al) PBA_FWD_LAUNCH(64, 1, true); else PBA_FWD_LAUNCH(64, 1, false); }
   }
+#undef PBA_FWD_LAUNCH
   return hipGetLastError();
 }
 

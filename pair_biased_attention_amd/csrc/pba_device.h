@@ -39,8 +39,12 @@ __device__ __forceinline__ f32x4 mfma4f(float a, float b, f32x4 c) {
 
 __device__ __forceinline__ float bf2f(u16 x) { return __uint_as_float(uint32_t(x) << 16); }
 __device__ __forceinline__ u16 f2bf(float x) { return __builtin_bit_cast(u16, (__bf16)x); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+// Two floats -> two bf16 (RNE) in one dword; a single v_cvt_pk_bf16_f32.
 __device__ __forceinline__ uint32_t pack2(float lo, float hi) {
-  return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float sigmoidf_fast(float x) {
@@ -95,17 +99,64 @@ __device__ __forceinline__ bf16x8 ident_cols_frag(int lane) {
   }
   return as_bf8(r);
 }
+// ---- LDS transpose reads (gfx950 ds_read_b64_tr_b16)
+// Within each 16-lane group, lane 4e+a supplies the address of 4 consecutive
+// bf16 values of some row R(e) starting at column c+4a; lane j = 4a+v then
+// receives the column c+j of the four rows R(0..3).  Two such reads build one
+// 16x16x32 operand whose k axis runs down the rows of a row-major tile.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+__device__ __forceinline__ u32x2 lds_tr16(const u16* p) {
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (lds_s16x4*)((__attribute__((address_space(3))) char*)(p)));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Operand whose lane (g, j) holds X[rb0 + e][c0 + j] in element e and
+// X[rb1 + e][c0 + j] in element 4 + e (e = 0..3), for a row-major LDS tile X
+// with row stride RS elements; rb0/rb1 are this lane group's row bases.
+template <int RS>
+__device__ __forceinline__ bf16x8 tr_frag(const u16* tile, int rb0, int rb1, int c0, int lane) {
+  const int j = lane & 15;
+  const int e = j >> 2, a = j & 3;
+  const u32x2 lo = lds_tr16(tile + (rb0 + e) * RS + c0 + 4 * a);
+  const u32x2 hi = lds_tr16(tile + (rb1 + e) * RS + c0 + 4 * a);
+  return as_bf8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
+// ---- bounds-checked global loads through a buffer resource: any byte past
+// num_bytes reads as zero, so ragged tiles need no per-element guards.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Most negative finite bf16 (-3.39e38), packed twice: the bias value given to
+// masked keys so their scores stay finite through the identity product
+// (0 * -inf would be NaN) and their probabilities underflow to exactly 0.
+constexpr uint32_t kMaskedBias2 = 0xFF7FFF7Fu;
+constexpr float kMaskedThreshold = -1.0e38f;
+
 __device__ __forceinline__ bf16x8 ones_frag() {
   u32x4 r;
   r[0] = r[1] = r[2] = r[3] = 0x3F803F80u;
   return as_bf8(r);
 }
 
-// Reduction over the four lanes that share a lane column (l, l^16, l^32, l^48).
+// Reduction over the four lanes that share a lane column (l, l^16, l^32, l^48),
+// with the gfx950 row-swap permutes (VALU, no LDS round trip): swapping the
+// two 32-lane halves (then the odd/even 16-lane rows) between two copies of x
+// leaves each lane with its partner's value in one of the two results.
 __device__ __forceinline__ float max_over_groups(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  x = fmaxf(x, __shfl_xor(x, 32));
-  return x;
+  const uint32_t u = __float_as_uint(x);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = fmaxf(__uint_as_float(s32[0]), __uint_as_float(s32[1]));
+  const uint32_t w = __float_as_uint(x);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+  return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
 }
 
 // Workgroup index remap so that consecutive logical tiles run on the same

@@ -45,7 +45,7 @@ struct BwdArgs {
   float scale;
   int P;            // number of batch chunks (partials)
   int C;            // batch rows per chunk
-  int slab;         // 1: accumulate dS over the chunk in LDS; 0: one partial per row
+  int slab;         // 2: dS sums over the chunk in registers; 1: in an LDS slab; 0: one partial per row
 };
 
 struct PwaArgs {
