@@ -8,7 +8,8 @@
 //
 // Four launches on the caller's stream, no host synchronisation:
 //   1. attn_bwd_pre      dA = dO*sigmoid(G), dG = dO*O*(1-sigmoid(G)),
-//                        D = rowsum(dO*O)  (= rowsum(P*dP), so dS = P*(dP-D))
+//                        D = rowsum(dO*O)  (= rowsum(P*dP), so dS = P*(dP-D)),
+//                        and (bf16) Q * log2(e) / sqrt(d) for the dK/dV kernel
 //   2. attn_bwd_dkdv     key-stationary: each workgroup owns 32 keys of one
 //                        head for a chunk of C batch rows; per row it walks all
 //                        queries, accumulates dK, dV in registers, and adds dS
@@ -17,16 +18,21 @@
 //   3. attn_bwd_dq       query-stationary: recomputes P and dP per key block
 //                        and accumulates dQ = dS K in registers.
 //   4. bias_grad_reduce  dBias = sum of the P partials in index order.
-// No floating-point atomics reach global memory; the only LDS atomics add into
-// slab cells owned by a single wave, in program order, so results are bitwise
-// repeatable (the deterministic-reduction principle the Design-CP page states
+// No floating-point atomics anywhere; every slab cell is owned by a single
+// wave and updated in program order, so results are bitwise repeatable (the deterministic-reduction principle the Design-CP page states
 // for atomic float reductions).
+#include <algorithm>
+#include <type_traits>
+
 #include "pba_device.h"
 #include "pba_kernels.h"
 
 namespace pba {
 
 namespace {
+
+// fp32 dK/dV kernel: LDS slab row stride (floats) for 32 keys, padded
+constexpr int kSlabStride = 36;
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void kperm_slot(int kappa, int& t, int& i) {
@@ -69,52 +75,71 @@ __device__ __forceinline__ u32x4 load_bias8(const u16* row, int k0, int N, bool 
 }  // namespace
 
 // ------------------------------------------------------------------ 1. pre
-template <bool BF16>
-__global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
+// bf16: one lane per 16-byte chunk of a row (L = d/8 lanes per row, 256/L
+// rows per workgroup), so every load and store is a coalesced 16-byte access;
+// D is summed over a row's lanes through LDS in a fixed order.
+__global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int rows_per_wg) {
+  __shared__ float sPart[256];
+  const int tid = threadIdx.x;
+  const int L = a.d / 8;
+  const long long rows = (long long)a.B * a.H * a.N;
+  const long long row0 = (long long)blockIdx.x * rows_per_wg;
+  const int r = tid / L, c = tid % L;
+  const long long row = row0 + r;
+  const float qscale = a.scale * kLog2e;
+  float D = 0.f;
+  if (r < rows_per_wg && row < rows) {
+    const size_t off = (size_t)row * a.d + 8 * c;
+    const u32x4 xo = ld16(static_cast<const u16*>(a.dout) + off);
+    const u32x4 xv = ld16(static_cast<const u16*>(a.out) + off);
+    const u32x4 xg = ld16(static_cast<const u16*>(a.g) + off);
+    const u32x4 xq = ld16(static_cast<const u16*>(a.q) + off);
+    u32x4 ra, rg, rq;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float f[2], s[2], o[2], ga[2], gg[2];
+      f[0] = bf2f(lo16(xo[e])); f[1] = bf2f(hi16(xo[e]));
+      o[0] = bf2f(lo16(xv[e])); o[1] = bf2f(hi16(xv[e]));
+      s[0] = sigmoid_precise(bf2f(lo16(xg[e]))); s[1] = sigmoid_precise(bf2f(hi16(xg[e])));
+#pragma unroll
+      for (int z = 0; z < 2; ++z) {
+        ga[z] = f[z] * s[z];
+        gg[z] = f[z] * o[z] * (1.f - s[z]);
+        D = fmaf(f[z], o[z], D);
+      }
+      ra[e] = pack2(ga[0], ga[1]);
+      rg[e] = pack2(gg[0], gg[1]);
+      rq[e] = pack2(bf2f(lo16(xq[e])) * qscale, bf2f(hi16(xq[e])) * qscale);
+    }
+    *reinterpret_cast<u32x4*>(static_cast<u16*>(a.da) + off) = ra;
+    *reinterpret_cast<u32x4*>(static_cast<u16*>(a.dg) + off) = rg;
+    *reinterpret_cast<u32x4*>(static_cast<u16*>(a.qs) + off) = rq;
+  }
+  sPart[tid] = D;
+  __syncthreads();
+  if (tid < rows_per_wg && row0 + tid < rows) {
+    float s = 0.f;
+    for (int j = 0; j < L; ++j) s += sPart[tid * L + j];
+    a.drow[row0 + tid] = s;
+  }
+}
+
+__global__ void __launch_bounds__(256) attn_bwd_pre_f32_kernel(BwdArgs a) {
   const long long rows = (long long)a.B * a.H * a.N;
   const long long row = (long long)blockIdx.x * 256 + threadIdx.x;
   if (row >= rows) return;
   const int d = a.d;
   float D = 0.f;
-  if constexpr (BF16) {
-    const u16* dO = static_cast<const u16*>(a.dout) + row * d;
-    const u16* O = static_cast<const u16*>(a.out) + row * d;
-    const u16* G = static_cast<const u16*>(a.g) + row * d;
-    u16* dA = static_cast<u16*>(a.da) + row * d;
-    u16* dG = static_cast<u16*>(a.dg) + row * d;
-    for (int c = 0; c < d; c += 8) {
-      const u32x4 xo = ld16(dO + c), xv = ld16(O + c), xg = ld16(G + c);
-      u32x4 ra, rg;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float f[2], s[2], o[2], ga[2], gg[2];
-        f[0] = bf2f(lo16(xo[e])); f[1] = bf2f(hi16(xo[e]));
-        o[0] = bf2f(lo16(xv[e])); o[1] = bf2f(hi16(xv[e]));
-        s[0] = sigmoid_precise(bf2f(lo16(xg[e]))); s[1] = sigmoid_precise(bf2f(hi16(xg[e])));
-#pragma unroll
-        for (int z = 0; z < 2; ++z) {
-          ga[z] = f[z] * s[z];
-          gg[z] = f[z] * o[z] * (1.f - s[z]);
-          D = fmaf(f[z], o[z], D);
-        }
-        ra[e] = pack2(ga[0], ga[1]);
-        rg[e] = pack2(gg[0], gg[1]);
-      }
-      *reinterpret_cast<u32x4*>(dA + c) = ra;
-      *reinterpret_cast<u32x4*>(dG + c) = rg;
-    }
-  } else {
-    const float* dO = static_cast<const float*>(a.dout) + row * d;
-    const float* O = static_cast<const float*>(a.out) + row * d;
-    const float* G = static_cast<const float*>(a.g) + row * d;
-    float* dA = static_cast<float*>(a.da) + row * d;
-    float* dG = static_cast<float*>(a.dg) + row * d;
-    for (int c = 0; c < d; ++c) {
-      const float f = dO[c], o = O[c], s = sigmoid_precise(G[c]);
-      dA[c] = f * s;
-      dG[c] = f * o * (1.f - s);
-      D = fmaf(f, o, D);
-    }
+  const float* dO = static_cast<const float*>(a.dout) + row * d;
+  const float* O = static_cast<const float*>(a.out) + row * d;
+  const float* G = static_cast<const float*>(a.g) + row * d;
+  float* dA = static_cast<float*>(a.da) + row * d;
+  float* dG = static_cast<float*>(a.dg) + row * d;
+  for (int c = 0; c < d; ++c) {
+    const float f = dO[c], o = O[c], s = sigmoid_precise(G[c]);
+    dA[c] = f * s;
+    dG[c] = f * o * (1.f - s);
+    D = fmaf(f, o, D);
   }
   a.drow[row] = D;
 }
@@ -122,34 +147,42 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_kernel(BwdArgs a) {
 // ------------------------------------------------------------------ 2. dK, dV, dBias (bf16)
 // One workgroup = 4 waves = 32 keys of one head, for a chunk of C batch rows.
 // Wave (kt, qh) owns keys kb+16kt..+15 and query half qh of every 64-query
-// block.  Per (row b, query block) the workgroup stages Q (scaled by
-// 1/sqrt(d), exactly as the forward rounds it) and dA in row-major LDS tiles;
-//   S  = Q K^T   and dP = dA V^T   read them row-wise (A operands),
-//   dK^T = Q^T dS and dV^T = dA^T P read them through the transpose read.
-// The next iteration's tiles, bias fragments and K/V rows are prefetched
-// into registers while the current one is computed.  dS is added into an LDS
-// slab [Npad x 32] (row stride 36 floats) that sums over the chunk; each slab
-// cell belongs to one lane of one wave, so plain read-add-write is race free
-// and ordered.  (This is the path for N > 768; shorter rows keep the sums in
-// registers, see attn_bwd_dkdv_rs_kernel.)
-constexpr int kSlabStride = 36;
-
+// block.  Iteration `it` covers (row b, query block); its Q tile (pre-scaled
+// by log2(e)/sqrt(d) in the preprocess step), dA tile, -log2(e)*LSE and -D
+// rows sit in one of two LDS buffers, and the loads of iteration it+2 are in
+// flight in registers while iteration it computes, so one barrier per
+// iteration suffices and HBM latency is hidden behind two iterations.
+//   S' = log2(e) * (Q K^T / sqrt(d) + bias) - log2(e) * LSE: the bias enters
+//        through two identity products (log2(e) split into bf16 hi + lo) and
+//        -log2(e) * LSE as the accumulator's initial value, so P = exp2(S').
+//   dP - D = dA V^T accumulated onto -D;  dS = P * (dP - D).
+//   dV^T += dA^T P and dK^T += Q^T dS read the staged tiles through the
+//   transpose read; dK is rescaled by ln 2 / 1 at the end (Q carried log2(e)).
+// dBias: with `slab`, each wave adds dS of every row of the chunk into an LDS
+// slab kept in accumulator layout (16 bytes per lane per tile, so no bank
+// conflicts), through an identity product that reads the slab tile as its
+// accumulator: no VALU, no atomics, one owner per cell, fixed order.  The
+// chunk's sums are stored once as this workgroup's slice of partial p.
+// Without `slab` (one row per chunk) dS goes straight to partial b.
 template <int DP>
+struct DkdvStage {
+  u32x4 q[DP / 32], da[DP / 32];  // Q and dA chunks of the staged tile
+  u32x4 k[DP / 32], v[DP / 32];   // this lane's K and V row of the tile's batch row
+  u32x4 bias[2];                  // bias fragments of the wave's two query tiles
+  float l, dd;                    // LSE and D of query (tid mod 64) of the block
+};
+
+template <int DP, bool ALIGNED>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
   constexpr int NCH = DP / 32;
-  // staging tiles; at batch-row boundaries the same space holds the
-  // (key tile, dK|dV, ct, lane) partials of the odd query half
-  constexpr int kStageBytes = 2 * 64 * RS * 2;
-  constexpr int kCombBytes = 2 * 2 * CT * 64 * 16;
-  static_assert(kCombBytes <= kStageBytes, "combine area must fit in the staging tiles");
-  __shared__ __attribute__((aligned(16))) u16 sQA[2 * 64 * RS];  // [Q tile | dA tile]
-  __shared__ __attribute__((aligned(16))) float sL[64];          // log2(e) * LSE (+inf: no keys)
-  __shared__ __attribute__((aligned(16))) float sD[64];          // D = rowsum(dO * O)
-  extern __shared__ float slab[];                               // [Npad][kSlabStride] when a.slab
-  u16* const sQ = sQA;
-  u16* const sA = sQA + 64 * RS;
-  f32x4* const comb = reinterpret_cast<f32x4*>(sQA);
+  constexpr int kTile = 64 * RS;
+  constexpr int kCombF4 = 2 * 2 * CT * 64;
+  static_assert(kCombF4 * 16 <= 2 * kTile * 2, "combine area must fit in one staging buffer");
+  __shared__ __attribute__((aligned(16))) u16 sQA[2][2 * kTile];  // [buffer][Q tile | dA tile]
+  __shared__ __attribute__((aligned(16))) float sLD[2][2][64];    // [buffer][-log2(e) LSE | -D]
+  extern __shared__ f32x4 slab_lds[];
+  f32x4* const slab = slab_lds;  // [nqb][4 query tiles][2 key tiles][64 lanes] when a.slab
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -167,169 +200,198 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int T = (b1 - b0) * nqb;              // iterations (row, query block)
   const u16* BiasH = static_cast<const u16*>(a.bias) + (size_t)h * N * N;
   const __amdgpu_buffer_rsrc_t brs = make_rsrc(BiasH, (uint32_t)((size_t)N * N * 2));
-  const bool bias_vec = (N % 8) == 0;
+  const size_t plane = (size_t)N * d;
+  const uint32_t plane_bytes = (uint32_t)(plane * 2);
 
   const bool keep_lane = key < N && (a.mask == nullptr || a.mask[key] != 0);
   const bool wave_masked = __any(!keep_lane);
 
   if (a.slab) {
-    for (int idx = tid; idx < nqb * 64 * kSlabStride; idx += 256) slab[idx] = 0.f;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int idx = tid; idx < nqb * 8 * 64; idx += 256) slab[idx] = z;
   }
 
-  // ---- prefetch state (registers)
-  u32x4 rq[NCH], ra[NCH];
-  float rl = kPosInf, rd = 0.f;
-  u32x4 rb[2];                    // bias fragments of the wave's two query tiles
-  u32x4 rkn[KC], rvn[KC];         // K, V rows of the next batch row
-  auto fetch = [&](int it) {      // global -> registers for iteration it
-    const int b = b0 + it / nqb, qbase = (it % nqb) * 64;
-    const size_t bh = (size_t)b * H + h;
+  // Every load below goes through a buffer resource that spans one (b, h)
+  // plane (the whole offset in the per-lane register, which the range check
+  // covers), so rows past N read as zeros and no load sits under a branch:
+  // the compiler can then wait for exactly the stage it needs.  Columns
+  // d..DP-1 of a staged Q/dA chunk hold the next row's leading values; they
+  // only ever meet the zeroed K/V columns or land in dK/dV columns that are
+  // not stored.
+  uint32_t chunk_off[NCH];  // byte offset of this thread's chunks in a query block
+  int kap[NCH], col[NCH];
+#pragma unroll
+  for (int c8i = 0; c8i < NCH; ++c8i) {
+    const int c = tid + 256 * c8i;
+    kap[c8i] = c / (DP / 8);
+    col[c8i] = 8 * (c % (DP / 8));
+    chunk_off[c8i] = (uint32_t)((kap[c8i] * d + col[c8i]) * 2);
+  }
+  // this lane's bias rows: queries 16(2qh+j)+n of the block, keys k0..k0+7
+  // (lanes g and g+2 fetch the same values; the identity keeps groups 0-1)
+  const int k0 = kb + 16 * kt + 8 * (g & 1);
+  uint32_t bias_off[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) bias_off[j] = (uint32_t)(((16 * (2 * qh + j) + n) * N + k0) * 2);
+  bool colok[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) colok[kc] = 32 * kc + 8 * g < d;
+
+  DkdvStage<DP> R[2];
+  auto fetch = [&](DkdvStage<DP>& st, int b, int qblk) {
+    const bool ok = b < b1;  // past the chunk: empty resources, zeros
+    const size_t bh = (size_t)(ok ? b : b0) * H + h;
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const u16*>(a.qs) + bh * plane, ok ? plane_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const u16*>(a.da) + bh * plane, ok ? plane_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const u16*>(a.k) + bh * plane, ok ? plane_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const u16*>(a.v) + bh * plane, ok ? plane_bytes : 0u);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + bh * N, ok ? (uint32_t)N * 4u : 0u);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.drow + bh * N, ok ? (uint32_t)N * 4u : 0u);
+    const uint32_t qoff = (uint32_t)(qblk * 64 * d * 2);
 #pragma unroll
     for (int c8i = 0; c8i < NCH; ++c8i) {
-      const int c = tid + 256 * c8i;
-      const int kappa = c / (DP / 8), c8 = c % (DP / 8);
-      const int q = qbase + kappa;
-      if (q < N && 8 * c8 < d) {
-        rq[c8i] = ld16(static_cast<const u16*>(a.q) + (bh * N + q) * d + 8 * c8);
-        ra[c8i] = ld16(static_cast<const u16*>(a.da) + (bh * N + q) * d + 8 * c8);
-      } else {
-        rq[c8i] = u32x4{0, 0, 0, 0};
-        ra[c8i] = u32x4{0, 0, 0, 0};
-      }
+      st.q[c8i] = buf_load16(rq, chunk_off[c8i] + qoff);
+      st.da[c8i] = buf_load16(ra, chunk_off[c8i] + qoff);
     }
-    if (tid < 64) {
-      const int q = qbase + tid;
-      rl = kPosInf;
-      rd = 0.f;
-      if (q < N) {
-        const float l = a.lse[bh * N + q];
-        rl = (l == kNegInf) ? kPosInf : l * kLog2e;
-        rd = a.drow[bh * N + q];
-      }
-    }
-    // lanes g and g+2 both fetch row qa's keys kb+16kt+8(g&1)..+7; the
-    // identity B operand keeps lane groups 0-1
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int qa = qbase + 16 * (2 * qh + j) + n;
-      const int k0 = kb + 16 * kt + 8 * (g & 1);
-      if (bias_vec) {
-        rb[j] = buf_load16(brs, (uint32_t)(((size_t)qa * N + k0) * 2));
-      } else {
-        rb[j] = (qa < N) ? load_bias8(BiasH + (size_t)qa * N, k0, N, false) : u32x4{0, 0, 0, 0};
-      }
-    }
-  };
-  auto fetch_kv = [&](int b) {
-    const size_t bh = (size_t)b * H + h;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      const int c0 = 32 * kc + 8 * g;
-      rkn[kc] = u32x4{0, 0, 0, 0};
-      rvn[kc] = u32x4{0, 0, 0, 0};
-      if (key < N && c0 < d) {
-        rkn[kc] = ld16(static_cast<const u16*>(a.k) + (bh * N + key) * d + c0);
-        rvn[kc] = ld16(static_cast<const u16*>(a.v) + (bh * N + key) * d + c0);
+      const uint32_t off = (uint32_t)((key * d + 32 * kc + 8 * g) * 2);
+      st.k[kc] = buf_load16(rk, off);
+      st.v[kc] = buf_load16(rv, off);
+    }
+    st.l = buf_load_f32(rl, (uint32_t)((qblk * 64 + lane) * 4));
+    st.dd = buf_load_f32(rd, (uint32_t)((qblk * 64 + lane) * 4));
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (ALIGNED) {
+        st.bias[j] = buf_load16(brs, bias_off[j] + (uint32_t)(qblk * 64 * N * 2));
+      } else {
+        const int qa = qblk * 64 + 16 * (2 * qh + j) + n;
+        st.bias[j] = (qa < N) ? load_bias8(BiasH + (size_t)qa * N, k0, N, false) : u32x4{0, 0, 0, 0};
       }
     }
   };
-  auto commit = [&]() {
+  auto commit = [&](const DkdvStage<DP>& st, int buf, int qblk) {
+    u16* tQ = sQA[buf];
 #pragma unroll
     for (int c8i = 0; c8i < NCH; ++c8i) {
-      const int c = tid + 256 * c8i;
-      const int kappa = c / (DP / 8), c8 = c % (DP / 8);
-      u32x4 qs;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qs[e] = pack2(bf2f(lo16(rq[c8i][e])) * a.scale, bf2f(hi16(rq[c8i][e])) * a.scale);
-      *reinterpret_cast<u32x4*>(&sQ[kappa * RS + 8 * c8]) = qs;
-      *reinterpret_cast<u32x4*>(&sA[kappa * RS + 8 * c8]) = ra[c8i];
+      *reinterpret_cast<u32x4*>(&tQ[kap[c8i] * RS + col[c8i]]) = st.q[c8i];
+      *reinterpret_cast<u32x4*>(&tQ[kTile + kap[c8i] * RS + col[c8i]]) = st.da[c8i];
     }
     if (tid < 64) {
-      sL[tid] = rl;
-      sD[tid] = rd;
+      // queries past N and rows without keys (LSE = -inf) get P = exp2(-inf) = 0
+      const bool live = qblk * 64 + tid < N && st.l != kNegInf;
+      sLD[buf][0][tid] = live ? -st.l * kLog2e : kNegInf;
+      sLD[buf][1][tid] = -st.dd;
     }
   };
 
-  const bf16x8 ident = ident_cols_frag(lane);
+  const bf16x8 id_l2hi = ident_cols_frag(lane, kLog2eHiBf16);
+  const bf16x8 id_l2lo = ident_cols_frag(lane, kLog2eLoBf16);
+  const bf16x8 id_lo = ident_rows_frag(lane, 0), id_hi = ident_rows_frag(lane, 1);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero_u4 = {0u, 0u, 0u, 0u};
   bf16x8 kf[KC], vf[KC];
   f32x4 dk[CT], dv[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
-
-  if (T > 0) {
-    fetch(0);
-    fetch_kv(b0);
-    commit();
+  u32x4 bcur[2];
+  auto take_kv = [&](const DkdvStage<DP>& st) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      kf[kc] = as_bf8(rkn[kc]);
-      vf[kc] = as_bf8(rvn[kc]);
+      kf[kc] = as_bf8(colok[kc] ? st.k[kc] : zero_u4);
+      vf[kc] = as_bf8(colok[kc] ? st.v[kc] : zero_u4);
     }
+  };
+
+  // positions: (cb, cq) of the current iteration, (fb, fq) of the next fetch
+  int cb = b0, cq = 0, fb = b0, fq = 0;
+  auto advance = [&](int& b, int& q) {
+    if (++q == nqb) {
+      q = 0;
+      ++b;
+    }
+  };
+  if (T > 0) {
+    fetch(R[0], fb, fq);
+    advance(fb, fq);
+    fetch(R[1], fb, fq);
+    advance(fb, fq);
+    commit(R[0], 0, 0);
+    bcur[0] = R[0].bias[0];
+    bcur[1] = R[0].bias[1];
+    take_kv(R[0]);
   }
   __syncthreads();
 
-  for (int it = 0; it < T; ++it) {
-    const int b = b0 + it / nqb;
-    const int qblk = it % nqb, qbase = qblk * 64;
+  auto step = [&](auto S_c) {
+    constexpr int S = decltype(S_c)::value;  // == it & 1: LDS buffer and register set of this iteration
+    const int b = cb, qblk = cq;
     const bool last_q = qblk == nqb - 1;
-    const u32x4 bcur0 = rb[0], bcur1 = rb[1];
-    if (it + 1 < T) {
-      fetch(it + 1);
-      if (last_q) fetch_kv(b + 1);
-    }
+    fetch(R[S], fb, fq);  // iteration it+2
+    advance(fb, fq);
 
-    // ---- two 16-query tiles per wave: S, P, dP, dS
+    const u16* tQ = sQA[S];
+    const u16* tA = tQ + kTile;
+    // ---- two 16-query tiles per wave: P, dS
     f32x4 pj[2], dsj[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int qtile = 2 * qh + j;
-      f32x4 s = mfma32(as_bf8(j == 0 ? bcur0 : bcur1), ident, zero4);
-      f32x4 dp = zero4;
+      const f32x4 nl4 = *reinterpret_cast<const f32x4*>(&sLD[S][0][16 * qtile + 4 * g]);
+      f32x4 dp = *reinterpret_cast<const f32x4*>(&sLD[S][1][16 * qtile + 4 * g]);
+      f32x4 s = mfma32(as_bf8(bcur[j]), id_l2hi, nl4);
+      s = mfma32(as_bf8(bcur[j]), id_l2lo, s);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        s = mfma32(as_bf8(*reinterpret_cast<const u32x4*>(&sQ[(16 * qtile + n) * RS + 32 * kc + 8 * g])), kf[kc], s);
-        dp = mfma32(as_bf8(*reinterpret_cast<const u32x4*>(&sA[(16 * qtile + n) * RS + 32 * kc + 8 * g])), vf[kc], dp);
+        s = mfma32(as_bf8(*reinterpret_cast<const u32x4*>(&tQ[(16 * qtile + n) * RS + 32 * kc + 8 * g])), kf[kc], s);
+        dp = mfma32(as_bf8(*reinterpret_cast<const u32x4*>(&tA[(16 * qtile + n) * RS + 32 * kc + 8 * g])), vf[kc], dp);
       }
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[16 * qtile + 4 * g]);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[16 * qtile + 4 * g]);
-      f32x4 pp, ds;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float pr = exp2_fast(fmaf(s[r], kLog2e, -l4[r]));
+        float pr = exp2_fast(s[r]);
         if (wave_masked && !keep_lane) pr = 0.f;
-        pp[r] = pr;
-        ds[r] = pr * (dp[r] - d4[r]);
+        pj[j][r] = pr;
+        dsj[j][r] = pr * dp[r];
       }
-      pj[j] = pp;
-      dsj[j] = ds;
-      if (a.slab) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) slab[(qbase + 16 * qtile + 4 * g + r) * kSlabStride + 16 * kt + n] += ds[r];
-      } else {
+      if (!a.slab) {
         float* part = a.partial + ((size_t)b * H + h) * N * N;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int q = qbase + 16 * qtile + 4 * g + r;
-          if (q < N && key < N) part[(size_t)q * N + key] = ds[r];
+          const int q = qblk * 64 + 16 * qtile + 4 * g + r;
+          if (q < N && key < N) part[(size_t)q * N + key] = dsj[j][r];
         }
       }
     }
-    // ---- dV^T += dA^T P, dK^T += Q^T dS over this wave's 32 queries; the k
-    // slot (g, v) is query row 32qh + 16(v/4) + 4g + v%4 on both sides
+    // P and dS as 16x16x32 operands: k slot (g, v) is query row
+    // 32qh + 16(v/4) + 4g + v%4 of the block
     const bf16x8 pb = pack8(pj[0], pj[1]);
     const bf16x8 dsb = pack8(dsj[0], dsj[1]);
+    if (a.slab) {
+      // slab tiles (qblk, 2qh+j, kt) += dS rows of query tile 2qh+j
+      f32x4* st = slab + ((qblk * 4 + 2 * qh) * 2 + kt) * 64 + lane;
+      st[0] = mfma32(id_lo, dsb, st[0]);
+      st[128] = mfma32(id_hi, dsb, st[128]);
+    }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
       const int r0 = 32 * qh + 4 * g;
-      dv[ct] = mfma32(tr_frag<RS>(sA, r0, r0 + 16, 16 * ct, lane), pb, dv[ct]);
-      dk[ct] = mfma32(tr_frag<RS>(sQ, r0, r0 + 16, 16 * ct, lane), dsb, dk[ct]);
+      dv[ct] = mfma32(tr_frag<RS>(tA, r0, r0 + 16, 16 * ct, lane), pb, dv[ct]);
+      dk[ct] = mfma32(tr_frag<RS>(tQ, r0, r0 + 16, 16 * ct, lane), dsb, dk[ct]);
     }
-    __syncthreads();  // every wave is done with this iteration's tiles
+    // ---- stage iteration it+1 into the other buffer (its loads were issued
+    // one iteration ago)
+    advance(cb, cq);
+    commit(R[S ^ 1], S ^ 1, cq);
+    bcur[0] = R[S ^ 1].bias[0];
+    bcur[1] = R[S ^ 1].bias[1];
+    if (last_q) take_kv(R[S ^ 1]);  // iteration it+1 starts the next row
+    __syncthreads();
 
     if (last_q) {
-      // ---- combine the two query halves and store dK, dV of row b
+      // ---- combine the two query halves and store dK, dV of row b; the
+      // buffer this iteration read is free until the next iteration commits
+      f32x4* comb = reinterpret_cast<f32x4*>(sQA[S]);
       if (qh == 1) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -340,14 +402,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
       __syncthreads();
       if (qh == 0 && key < N) {
         const size_t bh = (size_t)b * H + h;
-        u16* dK = static_cast<u16*>(a.dk) + bh * N * d;
-        u16* dV = static_cast<u16*>(a.dv) + bh * N * d;
+        u16* dK = static_cast<u16*>(a.dk) + bh * plane;
+        u16* dV = static_cast<u16*>(a.dv) + bh * plane;
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
           const int c = 16 * ct + 4 * g;
           if (c >= d) continue;
-          // Q was staged pre-scaled, so dK needs no further scale
-          const f32x4 sk = dk[ct] + comb[((kt * 2 + 0) * CT + ct) * 64 + lane];
+          // the staged Q carried log2(e) / sqrt(d); dK needs 1 / sqrt(d)
+          const f32x4 sk = (dk[ct] + comb[((kt * 2 + 0) * CT + ct) * 64 + lane]) * kLn2;
           const f32x4 sv = dv[ct] + comb[((kt * 2 + 1) * CT + ct) * 64 + lane];
           *reinterpret_cast<u32x2*>(dK + (size_t)key * d + c) = u32x2{pack2(sk[0], sk[1]), pack2(sk[2], sk[3])};
           *reinterpret_cast<u32x2*>(dV + (size_t)key * d + c) = u32x2{pack2(sv[0], sv[1]), pack2(sv[2], sv[3])};
@@ -355,264 +417,27 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        kf[kc] = as_bf8(rkn[kc]);
-        vf[kc] = as_bf8(rvn[kc]);
-      }
-      __syncthreads();  // the combine area is the staging space
+      __syncthreads();  // the combine area is the next commit's buffer
     }
-    if (it + 1 < T) {
-      commit();
-      __syncthreads();
-    }
+  };
+  for (int it = 0; it < T; it += 2) {
+    step(std::integral_constant<int, 0>{});
+    if (it + 1 < T) step(std::integral_constant<int, 1>{});
   }
 
-  if (a.slab) {
-    __syncthreads();
+  if (a.slab && key < N) {
+    // this chunk's dBias sums -> partial p (lane (g, n) of a tile holds rows 4g..4g+3)
     float* part = a.partial + ((size_t)p * H + h) * N * N;
-    for (int idx = tid; idx < N * 32; idx += 256) {
-      const int q = idx >> 5, col = idx & 31;
-      if (kb + col < N) part[(size_t)q * N + kb + col] = slab[q * kSlabStride + col];
-    }
-  }
-}
-
-// Register-slab variant for N <= 768 (ceil(N/64) <= NQB_T): the query-block
-// loop is unrolled, so each wave keeps the dBias sums of its 16 keys x (its
-// half of every query block) in accumulator registers; dS of every batch row
-// is added there with an identity product (no VALU, no LDS).  The sums of the
-// chunk are stored once, as this workgroup's slice of partial p.
-template <int DP, int NQB_T>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_rs_kernel(BwdArgs a) {
-  constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
-  constexpr int NCH = DP / 32;
-  constexpr int kStageBytes = 2 * 64 * RS * 2;
-  constexpr int kCombBytes = 2 * 2 * CT * 64 * 16;
-  static_assert(kCombBytes <= kStageBytes, "combine area must fit in the staging tiles");
-  __shared__ __attribute__((aligned(16))) u16 sQA[2 * 64 * RS];  // [Q tile | dA tile]
-  __shared__ __attribute__((aligned(16))) float sL[64];
-  __shared__ __attribute__((aligned(16))) float sD[64];
-  u16* const sQ = sQA;
-  u16* const sA = sQA + 64 * RS;
-  f32x4* const comb = reinterpret_cast<f32x4*>(sQA);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int g = lane >> 4, n = lane & 15;
-  const int kt = wave & 1, qh = wave >> 1;
-  const int N = a.N, d = a.d, H = a.H;
-  const int nkb = (N + 31) / 32;
-  const int nqb = (N + 63) / 64;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  const int kblk = L % nkb;
-  const int hp = L / nkb;
-  const int p = hp % a.P, h = hp / a.P;
-  const int kb = kblk * 32;
-  const int key = kb + 16 * kt + n;
-  const int b0 = p * a.C, b1 = min(a.B, b0 + a.C);
-  const u16* BiasH = static_cast<const u16*>(a.bias) + (size_t)h * N * N;
-  const __amdgpu_buffer_rsrc_t brs = make_rsrc(BiasH, (uint32_t)((size_t)N * N * 2));
-  const bool bias_vec = (N % 8) == 0;
-  const bool keep_lane = key < N && (a.mask == nullptr || a.mask[key] != 0);
-  const bool wave_masked = __any(!keep_lane);
-
-  u32x4 rq[NCH], ra[NCH];
-  float rl = kPosInf, rd = 0.f;
-  u32x4 rb[2];
-  u32x4 rkn[KC], rvn[KC];
-  auto fetch = [&](int b, int qbase) {
-    const size_t bh = (size_t)b * H + h;
+    for (int qblk = 0; qblk < nqb; ++qblk)
 #pragma unroll
-    for (int c8i = 0; c8i < NCH; ++c8i) {
-      const int c = tid + 256 * c8i;
-      const int kappa = c / (DP / 8), c8 = c % (DP / 8);
-      const int q = qbase + kappa;
-      if (q < N && 8 * c8 < d) {
-        rq[c8i] = ld16(static_cast<const u16*>(a.q) + (bh * N + q) * d + 8 * c8);
-        ra[c8i] = ld16(static_cast<const u16*>(a.da) + (bh * N + q) * d + 8 * c8);
-      } else {
-        rq[c8i] = u32x4{0, 0, 0, 0};
-        ra[c8i] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < 64) {
-      const int q = qbase + tid;
-      rl = kPosInf;
-      rd = 0.f;
-      if (q < N) {
-        const float l = a.lse[bh * N + q];
-        rl = (l == kNegInf) ? kPosInf : l * kLog2e;
-        rd = a.drow[bh * N + q];
-      }
-    }
+      for (int j = 0; j < 2; ++j) {
+        const f32x4 v = slab[((qblk * 4 + 2 * qh + j) * 2 + kt) * 64 + lane];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int qa = qbase + 16 * (2 * qh + j) + n;
-      const int k0 = kb + 16 * kt + 8 * (g & 1);
-      if (bias_vec) rb[j] = buf_load16(brs, (uint32_t)(((size_t)qa * N + k0) * 2));
-      else rb[j] = (qa < N) ? load_bias8(BiasH + (size_t)qa * N, k0, N, false) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto fetch_kv = [&](int b) {
-    const size_t bh = (size_t)b * H + h;
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int c0 = 32 * kc + 8 * g;
-      rkn[kc] = u32x4{0, 0, 0, 0};
-      rvn[kc] = u32x4{0, 0, 0, 0};
-      if (key < N && c0 < d) {
-        rkn[kc] = ld16(static_cast<const u16*>(a.k) + (bh * N + key) * d + c0);
-        rvn[kc] = ld16(static_cast<const u16*>(a.v) + (bh * N + key) * d + c0);
-      }
-    }
-  };
-  auto commit = [&]() {
-#pragma unroll
-    for (int c8i = 0; c8i < NCH; ++c8i) {
-      const int c = tid + 256 * c8i;
-      const int kappa = c / (DP / 8), c8 = c % (DP / 8);
-      u32x4 qs;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        qs[e] = pack2(bf2f(lo16(rq[c8i][e])) * a.scale, bf2f(hi16(rq[c8i][e])) * a.scale);
-      *reinterpret_cast<u32x4*>(&sQ[kappa * RS + 8 * c8]) = qs;
-      *reinterpret_cast<u32x4*>(&sA[kappa * RS + 8 * c8]) = ra[c8i];
-    }
-    if (tid < 64) {
-      sL[tid] = rl;
-      sD[tid] = rd;
-    }
-  };
-
-  const bf16x8 ident = ident_cols_frag(lane);
-  const bf16x8 id_lo = ident_rows_frag(lane, 0), id_hi = ident_rows_frag(lane, 1);
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  bf16x8 kf[KC], vf[KC];
-  f32x4 dk[CT], dv[CT];
-  f32x4 sacc[NQB_T][2];
-#pragma unroll
-  for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
-#pragma unroll
-  for (int qb = 0; qb < NQB_T; ++qb) sacc[qb][0] = sacc[qb][1] = zero4;
-
-  if (b0 < b1) {
-    fetch(b0, 0);
-    fetch_kv(b0);
-    commit();
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      kf[kc] = as_bf8(rkn[kc]);
-      vf[kc] = as_bf8(rvn[kc]);
-    }
-  }
-  __syncthreads();
-
-  for (int b = b0; b < b1; ++b) {
-#pragma unroll
-    for (int qblk = 0; qblk < NQB_T; ++qblk) {
-      if (qblk < nqb) {
-        const int qbase = qblk * 64;
-        const bool last_q = qblk == nqb - 1;
-        const bool has_next = !(last_q && b + 1 >= b1);
-        const u32x4 bcur0 = rb[0], bcur1 = rb[1];
-        if (has_next) {
-          if (last_q) {
-            fetch(b + 1, 0);
-            fetch_kv(b + 1);
-          } else {
-            fetch(b, qbase + 64);
-          }
-        }
-
-        f32x4 pj[2], dsj[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int qtile = 2 * qh + j;
-          f32x4 s = mfma32(as_bf8(j == 0 ? bcur0 : bcur1), ident, zero4);
-          f32x4 dp = zero4;
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            s = mfma32(as_bf8(*reinterpret_cast<const u32x4*>(&sQ[(16 * qtile + n) * RS + 32 * kc + 8 * g])), kf[kc], s);
-            dp = mfma32(as_bf8(*reinterpret_cast<const u32x4*>(&sA[(16 * qtile + n) * RS + 32 * kc + 8 * g])), vf[kc], dp);
-          }
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sL[16 * qtile + 4 * g]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sD[16 * qtile + 4 * g]);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float pr = exp2_fast(fmaf(s[r], kLog2e, -l4[r]));
-            if (wave_masked && !keep_lane) pr = 0.f;
-            pj[j][r] = pr;
-            dsj[j][r] = pr * (dp[r] - d4[r]);
-          }
-        }
-        const bf16x8 pb = pack8(pj[0], pj[1]);
-        const bf16x8 dsb = pack8(dsj[0], dsj[1]);
-        // dBias sums: rows of query tile 2qh+j, the same rounded dS as dK uses
-        sacc[qblk][0] = mfma32(id_lo, dsb, sacc[qblk][0]);
-        sacc[qblk][1] = mfma32(id_hi, dsb, sacc[qblk][1]);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          const int r0 = 32 * qh + 4 * g;
-          dv[ct] = mfma32(tr_frag<RS>(sA, r0, r0 + 16, 16 * ct, lane), pb, dv[ct]);
-          dk[ct] = mfma32(tr_frag<RS>(sQ, r0, r0 + 16, 16 * ct, lane), dsb, dk[ct]);
-        }
-        __syncthreads();
-
-        if (last_q) {
-          if (qh == 1) {
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-              comb[((kt * 2 + 0) * CT + ct) * 64 + lane] = dk[ct];
-              comb[((kt * 2 + 1) * CT + ct) * 64 + lane] = dv[ct];
-            }
-          }
-          __syncthreads();
-          if (qh == 0 && key < N) {
-            const size_t bh = (size_t)b * H + h;
-            u16* dK = static_cast<u16*>(a.dk) + bh * N * d;
-            u16* dV = static_cast<u16*>(a.dv) + bh * N * d;
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-              const int c = 16 * ct + 4 * g;
-              if (c >= d) continue;
-              const f32x4 sk = dk[ct] + comb[((kt * 2 + 0) * CT + ct) * 64 + lane];
-              const f32x4 sv = dv[ct] + comb[((kt * 2 + 1) * CT + ct) * 64 + lane];
-              *reinterpret_cast<u32x2*>(dK + (size_t)key * d + c) = u32x2{pack2(sk[0], sk[1]), pack2(sk[2], sk[3])};
-              *reinterpret_cast<u32x2*>(dV + (size_t)key * d + c) = u32x2{pack2(sv[0], sv[1]), pack2(sv[2], sv[3])};
-            }
-          }
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
-#pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            kf[kc] = as_bf8(rkn[kc]);
-            vf[kc] = as_bf8(rvn[kc]);
-          }
-          __syncthreads();
-        }
-        if (has_next) {
-          commit();
-          __syncthreads();
+        for (int r = 0; r < 4; ++r) {
+          const int q = qblk * 64 + 16 * (2 * qh + j) + 4 * g + r;
+          if (q < N) part[(size_t)q * N + key] = v[r];
         }
       }
-    }
-  }
-
-  // this chunk's dBias sums -> partial p
-  if (key < N) {
-    float* part = a.partial + ((size_t)p * H + h) * N * N;
-#pragma unroll
-    for (int qblk = 0; qblk < NQB_T; ++qblk) {
-      if (qblk < nqb) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int q = qblk * 64 + 16 * (2 * qh + j) + 4 * g + r;
-            if (q < N) part[(size_t)q * N + key] = sacc[qblk][j][r];
-          }
-      }
-    }
   }
 }
 
@@ -834,7 +659,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_f32_kernel(BwdArgs a) {
   __shared__ float sda[64 * RS];   // dA rows
   __shared__ float slse2[64], sdd[64];
   __shared__ f32x4 comb[2 * 2 * CT * 64];
-  extern __shared__ float slab[];
+  extern __shared__ f32x4 slab_lds[];
+  float* const slab = reinterpret_cast<float*>(slab_lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -1095,25 +921,51 @@ __global__ void __launch_bounds__(256) bias_grad_reduce_kernel(const float* part
 // ------------------------------------------------------------------ plan + launch
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-static int slab_bytes(int N) { return ((N + 63) / 64) * 64 * kSlabStride * 4; }
+// dynamic LDS of the dK/dV kernels' dBias slab (32 keys x all queries, fp32)
+static size_t slab_bytes(int N, bool bf16) {
+  const size_t nqb = (size_t)(N + 63) / 64;
+  return bf16 ? nqb * 8 * 64 * 16 : nqb * 64 * kSlabStride * 4;
+}
+constexpr size_t kMaxSlabBytes = 112 * 1024;
 
-// Batch rows per chunk so that the dK/dV launch has about 1024 workgroups.
-static void pick_chunks(int B, long long per_chunk, int& P, int& C) {
-  P = (int)std::min<long long>(B, std::max<long long>(1, (1024 + per_chunk - 1) / per_chunk));
-  C = (B + P - 1) / P;
-  P = (B + C - 1) / C;
+// Resident dK/dV workgroups per CU (160 KiB of LDS; at most 3 by registers).
+static int dkdv_wgs_per_cu(int N, int d, bool bf16, bool slab) {
+  const size_t dp = d <= 32 ? 32 : 64;
+  size_t lds = bf16 ? 2 * 2 * 64 * (dp + 8) * 2 + 1024 : 2 * 64 * (dp + 1) * 4 + 512 + 2 * 2 * (dp / 16) * 64 * 16;
+  if (slab) lds += slab_bytes(N, bf16);
+  return (int)std::max<size_t>(1, std::min<size_t>(3, 160 * 1024 / lds));
+}
+
+// Batch rows per chunk.  Cost model in microseconds: the dK/dV launch runs in
+// rounds of (256 CUs x resident workgroups); each round lasts C rows x nqb
+// query blocks at ~0.4 us per block, and each chunk adds one fp32 [H,N,N]
+// partial that is written and read back once at ~4 TB/s.
+static void pick_chunks(int B, int H, int N, int wpc, int& P, int& C) {
+  const long long per_chunk = (long long)H * ((N + 31) / 32);
+  const long long slots = 256LL * wpc;
+  const double nqb = (N + 63) / 64;
+  const double plane_us = 2.0 * H * (double)N * N * 4 / 4.0e6;
+  double best = 1e300;
+  P = B;
+  C = 1;
+  for (int c = B; c >= 1; --c) {
+    const int p = (B + c - 1) / c;
+    const long long rounds = (per_chunk * p + slots - 1) / slots;
+    const double cost = rounds * c * nqb * 0.4 + p * plane_us;
+    if (cost < best) {
+      best = cost;
+      P = p;
+      C = c;
+    }
+  }
 }
 
 BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16) {
   BwdPlan pl{};
   const size_t rows = (size_t)B * H * N;
-  const long long per_chunk = (long long)H * ((N + 31) / 32);
-  if (bf16 && N <= 768) {
-    pl.slab = 2;  // dBias sums in registers
-    pick_chunks(B, per_chunk, pl.P, pl.C);
-  } else if (B > 1 && slab_bytes(N) <= 112 * 1024) {
+  if (B > 1 && slab_bytes(N, bf16) <= kMaxSlabBytes) {
     pl.slab = 1;  // dBias sums in an LDS slab
-    pick_chunks(B, per_chunk, pl.P, pl.C);
+    pick_chunks(B, H, N, dkdv_wgs_per_cu(N, d, bf16, true), pl.P, pl.C);
   } else {
     pl.slab = 0;  // one partial per batch row
     pl.C = 1;
@@ -1122,6 +974,8 @@ BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16) {
   size_t off = 0;
   pl.off_da = off;
   off = align256(off + rows * d * (bf16 ? 2 : 4));
+  pl.off_qs = off;
+  if (bf16) off = align256(off + rows * d * 2);
   pl.off_drow = off;
   off = align256(off + rows * 4);
   pl.off_partial = off;
@@ -1139,49 +993,38 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream) {
 
   // 1. preprocess
   {
-    const dim3 grid((unsigned)((rows + 255) / 256));
-    if (bf16) hipLaunchKernelGGL(attn_bwd_pre_kernel<true>, grid, dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL(attn_bwd_pre_kernel<false>, grid, dim3(256), 0, stream, a);
+    if (bf16) {
+      const int rpw = 256 / (a.d / 8);
+      const dim3 grid((unsigned)((rows + rpw - 1) / rpw));
+      hipLaunchKernelGGL(attn_bwd_pre_bf16_kernel, grid, dim3(256), 0, stream, a, rpw);
+    } else {
+      const dim3 grid((unsigned)((rows + 255) / 256));
+      hipLaunchKernelGGL(attn_bwd_pre_f32_kernel, grid, dim3(256), 0, stream, a);
+    }
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // 2. dK, dV, dBias partials
   {
     const int nkb = (a.N + 31) / 32;
     const dim3 grid((unsigned)((long long)a.H * a.P * nkb));
-    if (a.slab == 2) {
-      const int nqb = (a.N + 63) / 64;
-      const int nt = nqb <= 4 ? 4 : nqb <= 6 ? 6 : nqb <= 8 ? 8 : 12;
-#define PBA_RS_LAUNCH(DPV, NQV) \
-  hipLaunchKernelGGL((attn_bwd_dkdv_rs_kernel<DPV, NQV>), grid, dim3(256), 0, stream, a)
-      if (dp == 32) {
-        if (nt == 4) PBA_RS_LAUNCH(32, 4); else if (nt == 6) PBA_RS_LAUNCH(32, 6);
-        else if (nt == 8) PBA_RS_LAUNCH(32, 8); else PBA_RS_LAUNCH(32, 12);
-      } else {
-        if (nt == 4) PBA_RS_LAUNCH(64, 4); else if (nt == 6) PBA_RS_LAUNCH(64, 6);
-        else if (nt == 8) PBA_RS_LAUNCH(64, 8); else PBA_RS_LAUNCH(64, 12);
-      }
-#undef PBA_RS_LAUNCH
+    const size_t shmem = a.slab ? slab_bytes(a.N, bf16) : 0;
+    const bool al = (a.N % 8) == 0;
+    const void* fn;
+    if (bf16) {
+      if (dp == 32) fn = al ? reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<32, true>)
+                            : reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<32, false>);
+      else fn = al ? reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<64, true>)
+                   : reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<64, false>);
     } else {
-      const size_t shmem = a.slab ? (size_t)slab_bytes(a.N) : 0;
-      if (shmem > 64 * 1024) {
-        // the slab can exceed the default 64 KiB dynamic LDS limit
-        const void* fns[4] = {reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<32>),
-                              reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<64>),
-                              reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<32>),
-                              reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<64>)};
-        for (const void* f : fns) {
-          if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem)) != hipSuccess)
-            return e;
-        }
-      }
-      if (bf16) {
-        if (dp == 32) hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<32>, grid, dim3(256), shmem, stream, a);
-        else hipLaunchKernelGGL(attn_bwd_dkdv_bf16_kernel<64>, grid, dim3(256), shmem, stream, a);
-      } else {
-        if (dp == 32) hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<32>, grid, dim3(256), shmem, stream, a);
-        else hipLaunchKernelGGL(attn_bwd_dkdv_f32_kernel<64>, grid, dim3(256), shmem, stream, a);
-      }
+      fn = dp == 32 ? reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<32>)
+                    : reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<64>);
     }
+    // the slab can exceed the default 64 KiB dynamic LDS limit
+    if (shmem > 64 * 1024 &&
+        (e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem)) != hipSuccess)
+      return e;
+    void* kargs[] = {&a};
+    if ((e = hipLaunchKernel(fn, grid, dim3(256), kargs, shmem, stream)) != hipSuccess) return e;
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   // 3. dQ

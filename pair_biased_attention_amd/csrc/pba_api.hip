@@ -113,6 +113,7 @@ int pba_backward(int B, int H, int N, int d, int dtype, const void* q, const voi
   a.out = out; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbias = dbias;
   a.da = ws + pl.off_da;
+  a.qs = bf16 ? ws + pl.off_qs : nullptr;
   a.drow = reinterpret_cast<float*>(ws + pl.off_drow);
   a.partial = reinterpret_cast<float*>(ws + pl.off_partial);
   a.B = B; a.H = H; a.N = N; a.d = d;

@@ -29,6 +29,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kPosInf = __builtin_huge_valf();
+// log2(e) as a sum of two bf16 values, hi = 1.4453125 and lo = -0.00262451171875;
+// hi + lo differs from log2(e) by 4.9e-6 relative.
+constexpr uint32_t kLog2eHiBf16 = 0x3FB9u;
+constexpr uint32_t kLog2eLoBf16 = 0xBB2Cu;
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -75,9 +79,11 @@ __device__ __forceinline__ bf16x8 pack8(f32x4 a, f32x4 b) {
 // With B = 8 contiguous bf16 values per lane (lane (g, n) holds row n's
 // entries 8 apart per lane group), D[i][n] = B(lane (i/4, n))[4*half + i%4]:
 // half 0 picks elements 0..3, half 1 elements 4..7 of each lane's B operand.
-__device__ __forceinline__ bf16x8 ident_rows_frag(int lane, int half) {
+// `one` is the bf16 bit pattern placed on the diagonal (1.0 by default; a
+// split constant such as log2(e) = hi + lo scales the moved tile exactly
+// enough with two products).
+__device__ __forceinline__ bf16x8 ident_rows_frag(int lane, int half, uint32_t one = 0x3F80u) {
   const int g = lane >> 4, i = lane & 15;
-  const uint32_t one = 0x3F80u;
   u32x4 r = {0u, 0u, 0u, 0u};
   if (g == (i >> 2)) {
     const int v = 4 * half + (i & 3);  // element index 0..7
@@ -89,9 +95,8 @@ __device__ __forceinline__ bf16x8 ident_rows_frag(int lane, int half) {
 // A lane (g, i) holding row i's entries 8g..8g+7 (lanes g >= 2 may hold any
 // finite values), D[i][n] = A[i][n]: the transpose of the A tile lands in the
 // result layout.
-__device__ __forceinline__ bf16x8 ident_cols_frag(int lane) {
+__device__ __forceinline__ bf16x8 ident_cols_frag(int lane, uint32_t one = 0x3F80u) {
   const int g = lane >> 4, n = lane & 15;
-  const uint32_t one = 0x3F80u;
   u32x4 r = {0u, 0u, 0u, 0u};
   if (g < 2 && (n >> 3) == g) {
     const int v = n & 7;
@@ -130,8 +135,13 @@ __device__ __forceinline__ bf16x8 tr_frag(const u16* tile, int rb0, int rb1, int
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes, 0x00020000);
 }
+// The whole offset goes in the per-lane operand: that is the part the range
+// check sees.
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
 
 // Most negative finite bf16 (-3.39e38), packed twice: the bias value given to

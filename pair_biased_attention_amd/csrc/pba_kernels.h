@@ -39,13 +39,14 @@ struct BwdArgs {
   void* dbias;
   // workspace views
   void* da;         // dA = dout * sigmoid(G), [B,H,N,d] (bf16 for bf16 inputs, fp32 otherwise)
+  void* qs;         // Q / sqrt(d) rounded to bf16, [B,H,N,d] (bf16 inputs only)
   float* drow;      // D = rowsum(dout * out), [B,H,N]
   float* partial;   // dBias partial sums, [P,H,N,N]
   int B, H, N, d;
   float scale;
   int P;            // number of batch chunks (partials)
   int C;            // batch rows per chunk
-  int slab;         // 2: dS sums over the chunk in registers; 1: in an LDS slab; 0: one partial per row
+  int slab;         // 1: dS sums over the chunk in an LDS slab; 0: one partial per batch row
 };
 
 struct PwaArgs {
@@ -70,7 +71,7 @@ struct PwaArgs {
 
 // Workspace plan of the attention backward (byte offsets into one buffer).
 struct BwdPlan {
-  size_t off_da, off_drow, off_partial, total;
+  size_t off_da, off_qs, off_drow, off_partial, total;
   int P, C, slab;
 };
 BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16);
