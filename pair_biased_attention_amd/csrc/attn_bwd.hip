@@ -172,7 +172,7 @@ struct DkdvStage {
   float l, dd;                    // LSE and D of query (tid mod 64) of the block
 };
 
-template <int DP, bool ALIGNED>
+template <int DP, bool ALIGNED, bool SLAB>
 __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
   constexpr int NCH = DP / 32;
@@ -182,9 +182,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 sQA[2][2 * kTile];  // [buffer][Q tile | dA tile]
   __shared__ __attribute__((aligned(16))) float sLD[2][2][64];    // [buffer][-log2(e) LSE | -D]
   extern __shared__ f32x4 slab_lds[];
-  f32x4* const slab = slab_lds;  // [nqb][4 query tiles][2 key tiles][64 lanes] when a.slab
+  f32x4* const slab = slab_lds;  // [nqb][4 query tiles][2 key tiles][64 lanes] when SLAB
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, n = lane & 15;
   const int kt = wave & 1, qh = wave >> 1;
   const int N = a.N, d = a.d, H = a.H;
@@ -206,7 +206,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   const bool keep_lane = key < N && (a.mask == nullptr || a.mask[key] != 0);
   const bool wave_masked = __any(!keep_lane);
 
-  if (a.slab) {
+  if constexpr (SLAB) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     for (int idx = tid; idx < nqb * 8 * 64; idx += 256) slab[idx] = z;
   }
@@ -238,15 +238,44 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   for (int kc = 0; kc < KC; ++kc) colok[kc] = 32 * kc + 8 * g < d;
 
   DkdvStage<DP> R[2];
-  auto fetch = [&](DkdvStage<DP>& st, int b, int qblk) {
-    const bool ok = b < b1;  // past the chunk: empty resources, zeros
-    const size_t bh = (size_t)(ok ? b : b0) * H + h;
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(static_cast<const u16*>(a.qs) + bh * plane, ok ? plane_bytes : 0u);
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(static_cast<const u16*>(a.da) + bh * plane, ok ? plane_bytes : 0u);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(static_cast<const u16*>(a.k) + bh * plane, ok ? plane_bytes : 0u);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(static_cast<const u16*>(a.v) + bh * plane, ok ? plane_bytes : 0u);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(a.lse + bh * N, ok ? (uint32_t)N * 4u : 0u);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(a.drow + bh * N, ok ? (uint32_t)N * 4u : 0u);
+  // Buffer resources of the next fetch's (b, h) plane, rebuilt only when that
+  // row changes.  Past the chunk they are empty (zeros, no traffic); the LSE
+  // and D rows are fetched by wave 0 only, K and V rows only for the first
+  // query block of a row: the other waves and steps issue the same loads
+  // against empty resources.
+  const size_t row_step = (size_t)H * plane;
+  const u16* fK = static_cast<const u16*>(a.k) + ((size_t)b0 * H + h) * plane;
+  const u16* fV = static_cast<const u16*>(a.v) + ((size_t)b0 * H + h) * plane;
+  const u16* fQs = static_cast<const u16*>(a.qs) + ((size_t)b0 * H + h) * plane;
+  const u16* fdA = static_cast<const u16*>(a.da) + ((size_t)b0 * H + h) * plane;
+  const float* fL = a.lse + ((size_t)b0 * H + h) * N;
+  const float* fD = a.drow + ((size_t)b0 * H + h) * N;
+  uint32_t rec_plane = plane_bytes, rec_row = wave == 0 ? (uint32_t)N * 4u : 0u;
+  auto next_row = [&]() {
+    fQs += row_step;
+    fdA += row_step;
+    fK += row_step;
+    fV += row_step;
+    fL += (size_t)H * N;
+    fD += (size_t)H * N;
+  };
+  int fb = b0, fq = 0;
+  auto advance_fetch = [&]() {
+    if (++fq == nqb) {
+      fq = 0;
+      ++fb;
+      next_row();
+      if (fb >= b1) rec_plane = rec_row = 0u;
+    }
+  };
+  auto fetch = [&](DkdvStage<DP>& st, int qblk) {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(fQs, rec_plane);
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(fdA, rec_plane);
+    const uint32_t rec_kv = qblk == 0 ? rec_plane : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(fK, rec_kv);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(fV, rec_kv);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(fL, rec_row);
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(fD, rec_row);
     const uint32_t qoff = (uint32_t)(qblk * 64 * d * 2);
 #pragma unroll
     for (int c8i = 0; c8i < NCH; ++c8i) {
@@ -295,7 +324,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   f32x4 dk[CT], dv[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
-  u32x4 bcur[2];
   auto take_kv = [&](const DkdvStage<DP>& st) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
@@ -304,22 +332,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   };
 
-  // positions: (cb, cq) of the current iteration, (fb, fq) of the next fetch
-  int cb = b0, cq = 0, fb = b0, fq = 0;
-  auto advance = [&](int& b, int& q) {
-    if (++q == nqb) {
-      q = 0;
-      ++b;
-    }
-  };
+  // position of the current iteration (the next fetch is two ahead)
+  int cb = b0, cq = 0;
   if (T > 0) {
-    fetch(R[0], fb, fq);
-    advance(fb, fq);
-    fetch(R[1], fb, fq);
-    advance(fb, fq);
+    fetch(R[0], fq);
+    advance_fetch();
+    fetch(R[1], fq);
+    advance_fetch();
     commit(R[0], 0, 0);
-    bcur[0] = R[0].bias[0];
-    bcur[1] = R[0].bias[1];
     take_kv(R[0]);
   }
   __syncthreads();
@@ -328,50 +348,74 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     constexpr int S = decltype(S_c)::value;  // == it & 1: LDS buffer and register set of this iteration
     const int b = cb, qblk = cq;
     const bool last_q = qblk == nqb - 1;
-    fetch(R[S], fb, fq);  // iteration it+2
-    advance(fb, fq);
-
     const u16* tQ = sQA[S];
     const u16* tA = tQ + kTile;
-    // ---- two 16-query tiles per wave: P, dS
-    f32x4 pj[2], dsj[2];
+    // all LDS operands of the two 16-query tiles first, so that the four
+    // independent product chains (S and dP of both tiles) interleave
+    f32x4 sacc[2], dp[2];
+    bf16x8 qfr[2][KC], afr[2][KC];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int qtile = 2 * qh + j;
-      const f32x4 nl4 = *reinterpret_cast<const f32x4*>(&sLD[S][0][16 * qtile + 4 * g]);
-      f32x4 dp = *reinterpret_cast<const f32x4*>(&sLD[S][1][16 * qtile + 4 * g]);
-      f32x4 s = mfma32(as_bf8(bcur[j]), id_l2hi, nl4);
-      s = mfma32(as_bf8(bcur[j]), id_l2lo, s);
+      sacc[j] = *reinterpret_cast<const f32x4*>(&sLD[S][0][16 * qtile + 4 * g]);
+      dp[j] = *reinterpret_cast<const f32x4*>(&sLD[S][1][16 * qtile + 4 * g]);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        s = mfma32(as_bf8(*reinterpret_cast<const u32x4*>(&tQ[(16 * qtile + n) * RS + 32 * kc + 8 * g])), kf[kc], s);
-        dp = mfma32(as_bf8(*reinterpret_cast<const u32x4*>(&tA[(16 * qtile + n) * RS + 32 * kc + 8 * g])), vf[kc], dp);
+        qfr[j][kc] = as_bf8(*reinterpret_cast<const u32x4*>(&tQ[(16 * qtile + n) * RS + 32 * kc + 8 * g]));
+        afr[j][kc] = as_bf8(*reinterpret_cast<const u32x4*>(&tA[(16 * qtile + n) * RS + 32 * kc + 8 * g]));
       }
+    }
+    f32x4 slab0, slab1;
+    f32x4* const st = slab + ((qblk * 4 + 2 * qh) * 2 + kt) * 64 + lane;
+    if constexpr (SLAB) {
+      slab0 = st[0];
+      slab1 = st[128];
+    }
+    // the bias of this iteration is read from its register stage before the
+    // loads of iteration it+2 reuse the stage
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sacc[j] = mfma32(as_bf8(R[S].bias[j]), id_l2hi, sacc[j]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sacc[j] = mfma32(as_bf8(R[S].bias[j]), id_l2lo, sacc[j]);
+    fetch(R[S], fq);  // iteration it+2
+    advance_fetch();
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        sacc[j] = mfma32(qfr[j][kc], kf[kc], sacc[j]);
+        dp[j] = mfma32(afr[j][kc], vf[kc], dp[j]);
+      }
+    // P = exp2(S'), dS = P * (dP - D)
+    f32x4 pj[2], dsj[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float pr = exp2_fast(s[r]);
-        if (wave_masked && !keep_lane) pr = 0.f;
-        pj[j][r] = pr;
-        dsj[j][r] = pr * dp[r];
+        pj[j][r] = exp2_fast(sacc[j][r]);
+        dsj[j][r] = pj[j][r] * dp[j][r];
       }
-      if (!a.slab) {
-        float* part = a.partial + ((size_t)b * H + h) * N * N;
+    if (wave_masked && !keep_lane) {  // masked keys: P = dS = 0
+      pj[0] = pj[1] = dsj[0] = dsj[1] = zero4;
+    }
+    if constexpr (!SLAB) {
+      float* part = a.partial + ((size_t)b * H + h) * N * N;
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int q = qblk * 64 + 16 * qtile + 4 * g + r;
+          const int q = qblk * 64 + 16 * (2 * qh + j) + 4 * g + r;
           if (q < N && key < N) part[(size_t)q * N + key] = dsj[j][r];
         }
-      }
     }
     // P and dS as 16x16x32 operands: k slot (g, v) is query row
     // 32qh + 16(v/4) + 4g + v%4 of the block
     const bf16x8 pb = pack8(pj[0], pj[1]);
     const bf16x8 dsb = pack8(dsj[0], dsj[1]);
-    if (a.slab) {
+    if constexpr (SLAB) {
       // slab tiles (qblk, 2qh+j, kt) += dS rows of query tile 2qh+j
-      f32x4* st = slab + ((qblk * 4 + 2 * qh) * 2 + kt) * 64 + lane;
-      st[0] = mfma32(id_lo, dsb, st[0]);
-      st[128] = mfma32(id_hi, dsb, st[128]);
+      st[0] = mfma32(id_lo, dsb, slab0);
+      st[128] = mfma32(id_hi, dsb, slab1);
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -381,10 +425,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
     // ---- stage iteration it+1 into the other buffer (its loads were issued
     // one iteration ago)
-    advance(cb, cq);
+    if (++cq == nqb) {
+      cq = 0;
+      ++cb;
+    }
     commit(R[S ^ 1], S ^ 1, cq);
-    bcur[0] = R[S ^ 1].bias[0];
-    bcur[1] = R[S ^ 1].bias[1];
     if (last_q) take_kv(R[S ^ 1]);  // iteration it+1 starts the next row
     __syncthreads();
 
@@ -425,7 +470,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     if (it + 1 < T) step(std::integral_constant<int, 1>{});
   }
 
-  if (a.slab && key < N) {
+  if (SLAB && key < N) {
     // this chunk's dBias sums -> partial p (lane (g, n) of a tile holds rows 4g..4g+3)
     float* part = a.partial + ((size_t)p * H + h) * N * N;
     for (int qblk = 0; qblk < nqb; ++qblk)
@@ -456,7 +501,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   __shared__ uint32_t sKeep[2][16];
   __shared__ int sAny[2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int N = a.N, d = a.d;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -662,7 +707,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_f32_kernel(BwdArgs a) {
   extern __shared__ f32x4 slab_lds[];
   float* const slab = reinterpret_cast<float*>(slab_lds);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, n = lane & 15;
   const int kt = wave & 1, qh = wave >> 1;
   const int N = a.N, d = a.d, H = a.H;
@@ -804,7 +849,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_f32_kernel(BwdArgs a, int nqb
   __shared__ float sv[64 * RS];
   __shared__ uint8_t skeep[64];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int N = a.N, d = a.d;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -1011,10 +1056,15 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream) {
     const bool al = (a.N % 8) == 0;
     const void* fn;
     if (bf16) {
-      if (dp == 32) fn = al ? reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<32, true>)
-                            : reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<32, false>);
-      else fn = al ? reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<64, true>)
-                   : reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<64, false>);
+#define PBA_DKDV_FN(DPV, ALV, SLV) reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<DPV, ALV, SLV>)
+      if (a.slab) {
+        if (dp == 32) fn = al ? PBA_DKDV_FN(32, true, true) : PBA_DKDV_FN(32, false, true);
+        else fn = al ? PBA_DKDV_FN(64, true, true) : PBA_DKDV_FN(64, false, true);
+      } else {
+        if (dp == 32) fn = al ? PBA_DKDV_FN(32, true, false) : PBA_DKDV_FN(32, false, false);
+        else fn = al ? PBA_DKDV_FN(64, true, false) : PBA_DKDV_FN(64, false, false);
+      }
+#undef PBA_DKDV_FN
     } else {
       fn = dp == 32 ? reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<32>)
                     : reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<64>);

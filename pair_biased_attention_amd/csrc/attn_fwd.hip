@@ -63,7 +63,7 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
   __shared__ uint32_t sKeep[2][16];
   __shared__ int sAny[2];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int N = a.N, d = a.d;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -305,7 +305,7 @@ __global__ void __launch_bounds__(256) attn_fwd_f32_kernel(FwdArgs a) {
   constexpr int NCH = DP / 16;  // 16-byte chunks (4 floats) per thread per tensor
   __shared__ Sm sm;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int N = a.N, d = a.d;
   const int L = xcd_remap(blockIdx.x, gridDim.x);

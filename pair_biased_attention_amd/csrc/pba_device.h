@@ -169,6 +169,10 @@ __device__ __forceinline__ float max_over_groups(float x) {
   return fmaxf(__uint_as_float(s16[0]), __uint_as_float(s16[1]));
 }
 
+// Wave index within the workgroup, marked wave-uniform so that values
+// derived from it stay in scalar registers.
+__device__ __forceinline__ int wave_index() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 // Workgroup index remap so that consecutive logical tiles run on the same
 // XCD.  The dispatcher hands workgroup w to XCD (w mod 8); with this remap a
 // contiguous range of logical ids lands on one XCD and shares its L2.

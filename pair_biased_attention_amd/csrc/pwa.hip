@@ -81,7 +81,7 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
                                                        int S, int N, int H, int d, int ncolt, int nnt) {
   constexpr int SPT = 256 / DP;  // MSA rows per column tile
   __shared__ PwaGemmSmem<DP> sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int wc = wave & 3, wn = wave >> 2;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
@@ -258,7 +258,7 @@ __global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA,
   constexpr int KS = Sm::KS, SPS = Sm::SPS;
   constexpr int C8 = DP / 8;
   __shared__ Sm sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int wi = wave & 3, wj = wave >> 2;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
