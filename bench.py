@@ -39,6 +39,20 @@ def attn_fwd_flops(B, H, N, d):
     return 4.0 * B * H * N * N * d
 
 
+# Algorithmic work credited to each kernel of the attention path (flops), per
+# launch.  The backward's 10*B*H*N^2*d is split by where each product is
+# formed: the dK/dV kernel recomputes S and forms dP, dV and dK (8); the dQ
+# kernel forms dQ (2; its own recomputation of S and dP is not credited).
+def attn_kernel_flops(B, H, N, d):
+    u = float(B) * H * N * N * d
+    return {"attn_fwd": 4 * u, "bwd_pre": 0.0, "bwd_dkdv": 8 * u, "bwd_dq": 2 * u, "bwd_dbias_reduce": 0.0}
+
+
+ATTN_BWD_KERNELS = ["bwd_pre", "bwd_dkdv", "bwd_dq", "bwd_dbias_reduce"]
+PWA_FWD_KERNELS = ["pwa_softmax", "pwa_weighted_sum"]
+PWA_BWD_KERNELS = ["pwa_bwd_softmax", "pwa_bwd_pre", "pwa_bwd_dv", "pwa_bwd_dw", "pwa_bwd_db"]
+
+
 def pwa_bytes(S, N, H, d, elt=2):
     """Algorithmic HBM bytes of PWA forward + backward.
 
@@ -112,6 +126,42 @@ def cpu_baseline(cfg, target_s=15.0):
                       f"{cores} cores visible, BLAS threads {threads}"}
 
 
+COPY_BYTES = 256 << 20
+
+
+def counters_pass(args, torch, pba):
+    """Run each kernel of interest a few times under a counter profiler."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)  # calibration: reads and writes exactly COPY_BYTES
+    torch.cuda.synchronize()
+    print(f"copy {COPY_BYTES} bytes done", flush=True)
+    del src, dst
+    cfg = workloads.CONFIGS["tri_attn_n384"]
+    inp = workloads.attention_inputs(cfg, with_f64=False)
+    t = {n: to_dev(inp[n], torch) for n in ("q", "k", "v", "g", "bias", "dout")}
+    km = to_dev(inp["key_mask"], torch)
+    ws = torch.empty(pba.pba_backward_workspace_bytes(cfg.B, cfg.H, cfg.N, cfg.d, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    for _ in range(args.steps):
+        out, lse = pba.pba_forward(t["q"], t["k"], t["v"], t["g"], t["bias"], km)
+        pba.pba_backward(t["q"], t["k"], t["v"], t["g"], t["bias"], km, out, lse, t["dout"], workspace=ws)
+    torch.cuda.synchronize()
+    print(f"attention steps done: {args.steps}", flush=True)
+    if args.no_pwa:
+        return
+    del t, ws
+    pc = workloads.CONFIGS["msa_pwa"]
+    pin = workloads.pwa_inputs(pc, with_f64=False)
+    pt = {n: to_dev(pin[n], torch) for n in ("b", "v", "g", "dout")}
+    del pin
+    for _ in range(args.pwa_steps):
+        o, l = pba.pair_weighted_avg(pt["b"], pt["v"], pt["g"], None)
+        pba.pair_weighted_avg_backward(pt["b"], pt["v"], pt["g"], None, o, l, pt["dout"])
+    torch.cuda.synchronize()
+    print(f"pair-average steps done: {args.pwa_steps}", flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +170,9 @@ def main():
     ap.add_argument("--pwa-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pwa", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="hardware-counter pass: a 256 MiB device copy (calibration kernel of known size), then "
+                         "--steps attention steps and --pwa-steps pair-average steps; no timing, no JSON line")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (no sharding, no collectives); "
@@ -133,6 +186,9 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     _lib.load()  # fails loudly without the HIP library
+
+    if args.counters:
+        return counters_pass(args, torch, pba)
 
     cfg = workloads.CONFIGS["tri_attn_n384"]
     B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
@@ -154,7 +210,21 @@ def main():
     ms_fwd, _ = time_loop(fwd, args.steps, 2, torch)
     flops = attn_flops(B, H, N, d)
     value = flops / (ms_step * 1e-3) / 1e12
-    fwd_tflops = attn_fwd_flops(B, H, N, d) / (ms_fwd * 1e-3) / 1e12
+
+    # per-kernel durations: HIP events recorded between the backward's launches
+    # on the stream they are launched on (pba_backward_timed), averaged
+    grads = {n: torch.empty_like(t["q"]) for n in ("dq", "dk", "dv", "dg")}
+    grads["dbias"] = torch.empty_like(t["bias"])
+    timed_args = (t["q"], t["k"], t["v"], t["g"], t["bias"], km, state["out"], state["lse"], t["dout"], ws, grads)
+    pba.pba_backward_timed(*timed_args)
+    acc = [0.0] * len(ATTN_BWD_KERNELS)
+    for _ in range(args.steps):
+        acc = [a + b for a, b in zip(acc, pba.pba_backward_timed(*timed_args))]
+    kernel_ms = {"attn_fwd": ms_fwd}
+    kernel_ms.update({n: a / args.steps for n, a in zip(ATTN_BWD_KERNELS, acc)})
+    kflops = attn_kernel_flops(B, H, N, d)
+    dom = max(kernel_ms, key=kernel_ms.get)
+    dom_tflops = kflops[dom] / (kernel_ms[dom] * 1e-3) / 1e12
 
     result = {
         "metric": "fwd+bwd TFLOP/s & %MFMA peak (N=384 tri-attn); GB/s & %HBM (pair-avg)",
@@ -174,15 +244,16 @@ def main():
                    "B": B, "H": H, "N": N, "d": d, "global_batch": B, "seq_len": N, "parallelism": "single GPU"},
         "mfma_frac": round(value / PEAK_BF16_TFLOPS, 4),
         "wall_s_timed": round(wall, 3),
-        # the forward kernel is the one launch pba_forward makes, so HIP events
-        # around the call time that kernel alone
-        "roofline": {"kernel": "attn_fwd_bf16_kernel<32,2>", "bound": "mfma", "achieved": round(fwd_tflops, 2),
-                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
-                     "ms_per_launch": round(ms_fwd, 4), "traffic": None},
+        # dominant kernel of the step; algorithmic flops per launch as credited
+        # in attn_kernel_flops, over its HIP-event duration
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(dom_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
+                     "ms_per_launch": round(kernel_ms[dom], 4), "flops_per_launch": kflops[dom], "traffic": None},
+        "kernels_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
     }
 
     if not args.no_pwa:
-        del t, state, ws
+        del t, state, ws, timed_args, grads
         torch.cuda.empty_cache()
         pc = workloads.CONFIGS["msa_pwa"]
         pin = workloads.pwa_inputs(pc, with_f64=False)
@@ -206,6 +277,20 @@ def main():
         ms_pf, _ = time_loop(pfwd, args.pwa_steps, 2, torch)
         gbs = pwa_bytes(pc.S, pc.N, pc.H, pc.d) / (ms_p * 1e-3) / 1e9
         gbs_f = pwa_fwd_bytes(pc.S, pc.N, pc.H, pc.d) / (ms_pf * 1e-3) / 1e9
+        pgr = {"dv": torch.empty_like(pt["v"]), "dg": torch.empty_like(pt["g"]), "db": torch.empty_like(pt["b"])}
+        pout, plse = torch.empty_like(pt["v"]), torch.empty((pc.H, pc.N), dtype=torch.float32, device="cuda")
+        pk_f = [0.0] * len(PWA_FWD_KERNELS)
+        pk_b = [0.0] * len(PWA_BWD_KERNELS)
+        for i in range(args.pwa_steps + 1):
+            f = pba.pair_weighted_avg_timed(pt["b"], pt["v"], pt["g"], None, pout, plse, pws_f)
+            bk = pba.pair_weighted_avg_backward_timed(pt["b"], pt["v"], pt["g"], None, pout, plse, pt["dout"],
+                                                      pws_b, pgr)
+            if i:  # the first pass is a warm-up
+                pk_f = [a + b for a, b in zip(pk_f, f)]
+                pk_b = [a + b for a, b in zip(pk_b, bk)]
+        pkms = {n: a / args.pwa_steps for n, a in zip(PWA_FWD_KERNELS + PWA_BWD_KERNELS, pk_f + pk_b)}
+        # the weighted sum + gate kernel moves exactly the forward's algorithmic bytes (3T + b)
+        ws_gbs = pwa_fwd_bytes(pc.S, pc.N, pc.H, pc.d) / (pkms["pwa_weighted_sum"] * 1e-3) / 1e9
         result["pair_avg"] = {
             "workload": "msa_pwa: S=1024 MSA rows, N=768, H=8, d=32, bf16, fwd+bwd",
             "value": round(gbs, 1), "unit": "GB/s", "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
@@ -213,6 +298,11 @@ def main():
             "tflops": round(pwa_flops(pc.S, pc.N, pc.H, pc.d) / (ms_p * 1e-3) / 1e12, 2),
             "fwd": {"ms": round(ms_pf, 4), "value": round(gbs_f, 1), "unit": "GB/s",
                     "hbm_frac": round(gbs_f / PEAK_HBM_GBS, 4)},
+            "roofline": {"kernel": "pwa_weighted_sum", "bound": "hbm", "achieved": round(ws_gbs, 1),
+                         "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ws_gbs / PEAK_HBM_GBS, 4),
+                         "ms_per_launch": round(pkms["pwa_weighted_sum"], 4),
+                         "bytes_per_launch": pwa_fwd_bytes(pc.S, pc.N, pc.H, pc.d), "traffic": None},
+            "kernels_ms": {n: round(v, 4) for n, v in pkms.items()},
         }
 
     if not args.no_cpu_baseline:

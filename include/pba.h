@@ -27,7 +27,8 @@
  * Conventions for every entry point:
  *   - All tensor arguments are DEVICE pointers to contiguous row-major
  *     buffers owned by the caller, 16-byte aligned.  Outputs must not alias
- *     inputs.  The library never allocates, frees or synchronises.
+ *     inputs.  The library never allocates, frees or synchronises (except
+ *     the *_timed measurement entry points at the end of this header).
  *   - Element type: PBA_F32 (float) or PBA_BF16 (bfloat16 bit patterns,
  *     uint16).  Outputs and gradients use the input type; lse, lse_w and all
  *     workspace partials are float32.
@@ -141,6 +142,43 @@ int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype,
                                const void* out, const float* lse_w, const void* dout,
                                void* dv, void* dg, void* db,
                                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Measurement entry points.  Each takes the arguments of the call it names,
+ * enqueues exactly the same kernels on `stream`, records a HIP event before
+ * the first kernel and after every kernel, waits for the last event and
+ * writes each kernel's duration in milliseconds to kernel_ms[0..capacity-1]
+ * and the number of kernels to *n_kernels.  Unlike every other entry point
+ * they create and destroy HIP events and synchronise; they are meant for
+ * benchmarks and profiles, not for production loops.  Kernel order:
+ *   pba_backward_timed:                preprocess (dA, dG, D), dK/dV + dBias
+ *                                      partials, dQ, dBias reduction
+ *   pair_weighted_avg_timed:           weight softmax, weighted sum + gate
+ *   pair_weighted_avg_backward_timed:  weight softmax (w and w^T), preprocess
+ *                                      (dA, dG), dV product, dw partials, db
+ * kernel_ms or n_kernels NULL returns PBA_ERR_NULL; a runtime failure returns
+ * PBA_ERR_HIP.
+ */
+int pba_backward_timed(int B, int H, int N, int d, int dtype,
+                       const void* q, const void* k, const void* v, const void* g,
+                       const void* bias, const uint8_t* key_mask,
+                       const void* out, const float* lse, const void* dout,
+                       void* dq, void* dk, void* dv, void* dg, void* dbias,
+                       void* workspace, size_t workspace_bytes, void* stream,
+                       float* kernel_ms, int capacity, int* n_kernels);
+int pair_weighted_avg_timed(int S, int N, int H, int d, int dtype,
+                            const void* b, const uint8_t* key_mask,
+                            const void* v, const void* g,
+                            void* out, float* lse_w,
+                            void* workspace, size_t workspace_bytes, void* stream,
+                            float* kernel_ms, int capacity, int* n_kernels);
+int pair_weighted_avg_backward_timed(int S, int N, int H, int d, int dtype,
+                                     const void* b, const uint8_t* key_mask,
+                                     const void* v, const void* g,
+                                     const void* out, const float* lse_w, const void* dout,
+                                     void* dv, void* dg, void* db,
+                                     void* workspace, size_t workspace_bytes, void* stream,
+                                     float* kernel_ms, int capacity, int* n_kernels);
 
 #ifdef __cplusplus
 }

@@ -7,5 +7,6 @@ from .ops import (  # noqa: F401
     pba_forward, pba_backward, pba_backward_workspace_bytes,
     pair_weighted_avg, pair_weighted_avg_backward,
     pair_weighted_avg_workspace_bytes, pair_weighted_avg_backward_workspace_bytes,
+    pba_backward_timed, pair_weighted_avg_timed, pair_weighted_avg_backward_timed,
 )
 from ._lib import PbaError, LIB_PATH  # noqa: F401

@@ -33,6 +33,12 @@ SIGNATURES = {
     "pair_weighted_avg_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "pair_weighted_avg_backward": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
                                         _p, _p, _p, _p, _sz, _p]),
+    "pba_backward_timed": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                _p, _p, _p, _p, _p, _p, _sz, _p, _p, _i, _p]),
+    "pair_weighted_avg_timed": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _sz, _p,
+                                     _p, _i, _p]),
+    "pair_weighted_avg_backward_timed": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
+                                              _p, _p, _p, _p, _sz, _p, _p, _i, _p]),
 }
 
 _lib = None

@@ -1029,13 +1029,14 @@ BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16) {
   return pl;
 }
 
-hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream) {
+hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, KernelTimer* timer) {
   BwdArgs a = args;
   const int dp = a.d <= 32 ? 32 : 64;
   const long long rows = (long long)a.B * a.H * a.N;
   const long long bhs = (long long)a.B * a.H;
   hipError_t e;
 
+  timer_start(timer, stream);
   // 1. preprocess
   {
     if (bf16) {
@@ -1047,6 +1048,7 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream) {
       hipLaunchKernelGGL(attn_bwd_pre_f32_kernel, grid, dim3(256), 0, stream, a);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark(timer, stream);
   }
   // 2. dK, dV, dBias partials
   {
@@ -1075,7 +1077,7 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream) {
       return e;
     void* kargs[] = {&a};
     if ((e = hipLaunchKernel(fn, grid, dim3(256), kargs, shmem, stream)) != hipSuccess) return e;
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark(timer, stream);
   }
   // 3. dQ
   {
@@ -1101,6 +1103,7 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream) {
       else hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<64>, grid, dim3(256), 0, stream, a, nqb);
     }
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark(timer, stream);
   }
   // 4. dBias = sum of partials
   {
@@ -1109,6 +1112,7 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream) {
     if (bf16) hipLaunchKernelGGL(bias_grad_reduce_kernel<true>, grid, dim3(256), 0, stream, a.partial, a.P, count, a.dbias);
     else hipLaunchKernelGGL(bias_grad_reduce_kernel<false>, grid, dim3(256), 0, stream, a.partial, a.P, count, a.dbias);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark(timer, stream);
   }
   return hipSuccess;
 }

@@ -1,7 +1,8 @@
 // pba_api.hip - the C ABI declared in include/pba.h: argument validation,
 // workspace sizing and dispatch to the gfx950 kernels.  Every check runs on
-// the host before anything is enqueued; nothing here allocates, frees,
-// synchronises or prints.
+// the host before anything is enqueued; apart from the *_timed measurement
+// entry points (which create HIP events and wait for them), nothing here
+// allocates, frees, synchronises or prints.
 #include <math.h>
 
 #include "pba.h"
@@ -53,6 +54,59 @@ int all_aligned16(std::initializer_list<const void*> ps) {
 
 float attn_scale(int d) { return 1.0f / sqrtf((float)d); }
 
+int prep_backward(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                  const void* g, const void* bias, const uint8_t* key_mask, const void* out, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, void* dg, void* dbias, void* workspace,
+                  size_t workspace_bytes, pba::BwdArgs& a) {
+  int st = check_attn_sizes(B, H, N, d, dtype);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({q, k, v, g, bias, out, lse, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
+  if ((st = all_aligned16({q, k, v, g, bias, out, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
+  if (!aligned4(lse)) return PBA_ERR_ALIGN;
+  const bool bf16 = dtype == PBA_BF16;
+  const pba::BwdPlan pl = pba::plan_attn_bwd(B, H, N, d, bf16);
+  if (workspace == nullptr || workspace_bytes < pl.total) return PBA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PBA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  a.q = q; a.k = k; a.v = v; a.g = g; a.bias = bias; a.mask = key_mask;
+  a.out = out; a.lse = lse; a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbias = dbias;
+  a.da = ws + pl.off_da;
+  a.qs = bf16 ? ws + pl.off_qs : nullptr;
+  a.drow = reinterpret_cast<float*>(ws + pl.off_drow);
+  a.partial = reinterpret_cast<float*>(ws + pl.off_partial);
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.scale = attn_scale(d);
+  a.P = pl.P; a.C = pl.C; a.slab = pl.slab;
+  return PBA_OK;
+}
+
+// Measurement helper: runs `launch` with a kernel timer, waits for the last
+// event and reports each kernel's duration in milliseconds.
+template <typename F>
+int run_timed(F launch, hipStream_t stream, float* kernel_ms, int capacity, int* n_kernels) {
+  if (kernel_ms == nullptr || n_kernels == nullptr) return PBA_ERR_NULL;
+  pba::KernelTimer t;
+  int made = 0;
+  int st = PBA_OK;
+  for (; made <= pba::KernelTimer::kMax; ++made)
+    if (hipEventCreate(&t.ev[made]) != hipSuccess) {
+      st = PBA_ERR_HIP;
+      break;
+    }
+  if (st == PBA_OK) {
+    const hipError_t e = launch(&t, stream);
+    if (e != hipSuccess || !t.ok || hipEventSynchronize(t.ev[t.n]) != hipSuccess) st = PBA_ERR_HIP;
+  }
+  if (st == PBA_OK) {
+    *n_kernels = t.n;
+    for (int i = 0; i < t.n && i < capacity; ++i)
+      if (hipEventElapsedTime(&kernel_ms[i], t.ev[i], t.ev[i + 1]) != hipSuccess) st = PBA_ERR_HIP;
+  }
+  for (int i = 0; i < made; ++i) hipEventDestroy(t.ev[i]);
+  return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,29 +152,27 @@ int pba_backward(int B, int H, int N, int d, int dtype, const void* q, const voi
                  const void* g, const void* bias, const uint8_t* key_mask, const void* out,
                  const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dg, void* dbias,
                  void* workspace, size_t workspace_bytes, void* stream) {
-  int st = check_attn_sizes(B, H, N, d, dtype);
-  if (st != PBA_OK) return st;
-  if ((st = all_nonnull({q, k, v, g, bias, out, lse, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
-  if ((st = all_aligned16({q, k, v, g, bias, out, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
-  if (!aligned4(lse)) return PBA_ERR_ALIGN;
-  const bool bf16 = dtype == PBA_BF16;
-  const pba::BwdPlan pl = pba::plan_attn_bwd(B, H, N, d, bf16);
-  if (workspace == nullptr || workspace_bytes < pl.total) return PBA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return PBA_ERR_ALIGN;
-  char* ws = static_cast<char*>(workspace);
   pba::BwdArgs a{};
-  a.q = q; a.k = k; a.v = v; a.g = g; a.bias = bias; a.mask = key_mask;
-  a.out = out; a.lse = lse; a.dout = dout;
-  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbias = dbias;
-  a.da = ws + pl.off_da;
-  a.qs = bf16 ? ws + pl.off_qs : nullptr;
-  a.drow = reinterpret_cast<float*>(ws + pl.off_drow);
-  a.partial = reinterpret_cast<float*>(ws + pl.off_partial);
-  a.B = B; a.H = H; a.N = N; a.d = d;
-  a.scale = attn_scale(d);
-  a.P = pl.P; a.C = pl.C; a.slab = pl.slab;
-  const hipError_t e = pba::launch_attn_bwd(a, bf16, static_cast<hipStream_t>(stream));
+  const int st = prep_backward(B, H, N, d, dtype, q, k, v, g, bias, key_mask, out, lse, dout, dq, dk, dv, dg,
+                               dbias, workspace, workspace_bytes, a);
+  if (st != PBA_OK) return st;
+  const hipError_t e = pba::launch_attn_bwd(a, dtype == PBA_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+int pba_backward_timed(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                       const void* g, const void* bias, const uint8_t* key_mask, const void* out,
+                       const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dg, void* dbias,
+                       void* workspace, size_t workspace_bytes, void* stream, float* kernel_ms, int capacity,
+                       int* n_kernels) {
+  pba::BwdArgs a{};
+  const int st = prep_backward(B, H, N, d, dtype, q, k, v, g, bias, key_mask, out, lse, dout, dq, dk, dv, dg,
+                               dbias, workspace, workspace_bytes, a);
+  if (st != PBA_OK) return st;
+  const bool bf16 = dtype == PBA_BF16;
+  return run_timed(
+      [&](pba::KernelTimer* t, hipStream_t s) { return pba::launch_attn_bwd(a, bf16, s, t); },
+      static_cast<hipStream_t>(stream), kernel_ms, capacity, n_kernels);
 }
 
 size_t pair_weighted_avg_workspace_bytes(int S, int N, int H, int d, int dtype) {
@@ -128,9 +180,9 @@ size_t pair_weighted_avg_workspace_bytes(int S, int N, int H, int d, int dtype) 
   return ((size_t)H * N * N * 2 + 255) & ~size_t(255);
 }
 
-int pair_weighted_avg(int S, int N, int H, int d, int dtype, const void* b, const uint8_t* key_mask,
-                      const void* v, const void* g, void* out, float* lse_w, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+static int prep_pwa_fwd(int S, int N, int H, int d, int dtype, const void* b, const uint8_t* key_mask,
+                        const void* v, const void* g, void* out, float* lse_w, void* workspace,
+                        size_t workspace_bytes, pba::PwaArgs& a) {
   int st = check_pwa_sizes(S, N, H, d, dtype);
   if (st != PBA_OK) return st;
   if ((st = all_nonnull({b, v, g, out, lse_w})) != PBA_OK) return st;
@@ -139,12 +191,30 @@ int pair_weighted_avg(int S, int N, int H, int d, int dtype, const void* b, cons
   if (workspace == nullptr || workspace_bytes < pair_weighted_avg_workspace_bytes(S, N, H, d, dtype))
     return PBA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PBA_ERR_ALIGN;
-  pba::PwaArgs a{};
   a.b = b; a.mask = key_mask; a.v = v; a.g = g;
   a.o = out; a.lse_w = lse_w; a.w = workspace;
   a.S = S; a.N = N; a.H = H; a.d = d; a.P = 1;
+  return PBA_OK;
+}
+
+int pair_weighted_avg(int S, int N, int H, int d, int dtype, const void* b, const uint8_t* key_mask,
+                      const void* v, const void* g, void* out, float* lse_w, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  pba::PwaArgs a{};
+  const int st = prep_pwa_fwd(S, N, H, d, dtype, b, key_mask, v, g, out, lse_w, workspace, workspace_bytes, a);
+  if (st != PBA_OK) return st;
   const hipError_t e = pba::launch_pwa_fwd(a, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+int pair_weighted_avg_timed(int S, int N, int H, int d, int dtype, const void* b, const uint8_t* key_mask,
+                            const void* v, const void* g, void* out, float* lse_w, void* workspace,
+                            size_t workspace_bytes, void* stream, float* kernel_ms, int capacity, int* n_kernels) {
+  pba::PwaArgs a{};
+  const int st = prep_pwa_fwd(S, N, H, d, dtype, b, key_mask, v, g, out, lse_w, workspace, workspace_bytes, a);
+  if (st != PBA_OK) return st;
+  return run_timed([&](pba::KernelTimer* t, hipStream_t s) { return pba::launch_pwa_fwd(a, true, s, t); },
+                   static_cast<hipStream_t>(stream), kernel_ms, capacity, n_kernels);
 }
 
 size_t pair_weighted_avg_backward_workspace_bytes(int S, int N, int H, int d, int dtype) {
@@ -152,10 +222,9 @@ size_t pair_weighted_avg_backward_workspace_bytes(int S, int N, int H, int d, in
   return pba::plan_pwa_bwd(S, N, H, d, true).total;
 }
 
-int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype, const void* b,
-                               const uint8_t* key_mask, const void* v, const void* g, const void* out,
-                               const float* lse_w, const void* dout, void* dv, void* dg, void* db,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+static int prep_pwa_bwd(int S, int N, int H, int d, int dtype, const void* b, const uint8_t* key_mask,
+                        const void* v, const void* g, const void* out, const float* lse_w, const void* dout,
+                        void* dv, void* dg, void* db, void* workspace, size_t workspace_bytes, pba::PwaArgs& a) {
   int st = check_pwa_sizes(S, N, H, d, dtype);
   if (st != PBA_OK) return st;
   if ((st = all_nonnull({b, v, g, out, lse_w, dout, dv, dg, db})) != PBA_OK) return st;
@@ -165,15 +234,38 @@ int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype, const void
   if (workspace == nullptr || workspace_bytes < pl.total) return PBA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return PBA_ERR_ALIGN;
   char* ws = static_cast<char*>(workspace);
-  pba::PwaArgs a{};
   a.b = b; a.mask = key_mask; a.v = v; a.g = g; a.out = out; a.lse_w_in = lse_w; a.dout = dout;
   a.dv = dv; a.dg = dg; a.db = db;
   a.w = ws + pl.off_w;
   a.da = ws + pl.off_da;
   a.partial = reinterpret_cast<float*>(ws + pl.off_partial);
   a.S = S; a.N = N; a.H = H; a.d = d; a.P = pl.P;
+  return PBA_OK;
+}
+
+int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype, const void* b,
+                               const uint8_t* key_mask, const void* v, const void* g, const void* out,
+                               const float* lse_w, const void* dout, void* dv, void* dg, void* db,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  pba::PwaArgs a{};
+  const int st = prep_pwa_bwd(S, N, H, d, dtype, b, key_mask, v, g, out, lse_w, dout, dv, dg, db, workspace,
+                              workspace_bytes, a);
+  if (st != PBA_OK) return st;
   const hipError_t e = pba::launch_pwa_bwd(a, true, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+int pair_weighted_avg_backward_timed(int S, int N, int H, int d, int dtype, const void* b,
+                                     const uint8_t* key_mask, const void* v, const void* g, const void* out,
+                                     const float* lse_w, const void* dout, void* dv, void* dg, void* db,
+                                     void* workspace, size_t workspace_bytes, void* stream, float* kernel_ms,
+                                     int capacity, int* n_kernels) {
+  pba::PwaArgs a{};
+  const int st = prep_pwa_bwd(S, N, H, d, dtype, b, key_mask, v, g, out, lse_w, dout, dv, dg, db, workspace,
+                              workspace_bytes, a);
+  if (st != PBA_OK) return st;
+  return run_timed([&](pba::KernelTimer* t, hipStream_t s) { return pba::launch_pwa_bwd(a, true, s, t); },
+                   static_cast<hipStream_t>(stream), kernel_ms, capacity, n_kernels);
 }
 
 }  // extern "C"

@@ -82,9 +82,25 @@ struct PwaPlan {
 };
 PwaPlan plan_pwa_bwd(int S, int N, int H, int d, bool bf16);
 
+// Optional per-kernel timing for the measurement entry points: a launcher
+// given a timer records ev[0] on the stream before its first kernel and
+// ev[i] after its i-th kernel.
+struct KernelTimer {
+  static constexpr int kMax = 8;
+  hipEvent_t ev[kMax + 1];
+  int n = 0;
+  bool ok = true;
+};
+inline void timer_start(KernelTimer* t, hipStream_t s) {
+  if (t && hipEventRecord(t->ev[0], s) != hipSuccess) t->ok = false;
+}
+inline void timer_mark(KernelTimer* t, hipStream_t s) {
+  if (t && t->n < KernelTimer::kMax && hipEventRecord(t->ev[++t->n], s) != hipSuccess) t->ok = false;
+}
+
 hipError_t launch_attn_fwd(const FwdArgs& a, bool bf16, hipStream_t stream);
-hipError_t launch_attn_bwd(const BwdArgs& a, bool bf16, hipStream_t stream);
-hipError_t launch_pwa_fwd(const PwaArgs& a, bool bf16, hipStream_t stream);
-hipError_t launch_pwa_bwd(const PwaArgs& a, bool bf16, hipStream_t stream);
+hipError_t launch_attn_bwd(const BwdArgs& a, bool bf16, hipStream_t stream, KernelTimer* timer = nullptr);
+hipError_t launch_pwa_fwd(const PwaArgs& a, bool bf16, hipStream_t stream, KernelTimer* timer = nullptr);
+hipError_t launch_pwa_bwd(const PwaArgs& a, bool bf16, hipStream_t stream, KernelTimer* timer = nullptr);
 
 }  // namespace pba

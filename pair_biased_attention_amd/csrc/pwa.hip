@@ -418,14 +418,20 @@ static hipError_t launch_gemm(const u16* X, const u16* W, const u16* G, u16* out
   return hipGetLastError();
 }
 
-hipError_t launch_pwa_fwd(const PwaArgs& a, bool /*bf16*/, hipStream_t stream) {
+hipError_t launch_pwa_fwd(const PwaArgs& a, bool /*bf16*/, hipStream_t stream, KernelTimer* timer) {
+  timer_start(timer, stream);
   hipError_t e = launch_softmax(a, nullptr, stream);
   if (e != hipSuccess) return e;
-  return launch_gemm<true>(static_cast<const u16*>(a.v), static_cast<const u16*>(a.w), static_cast<const u16*>(a.g),
-                           static_cast<u16*>(a.o), a, stream);
+  timer_mark(timer, stream);
+  e = launch_gemm<true>(static_cast<const u16*>(a.v), static_cast<const u16*>(a.w), static_cast<const u16*>(a.g),
+                        static_cast<u16*>(a.o), a, stream);
+  if (e != hipSuccess) return e;
+  timer_mark(timer, stream);
+  return hipSuccess;
 }
 
-hipError_t launch_pwa_bwd(const PwaArgs& args, bool /*bf16*/, hipStream_t stream) {
+hipError_t launch_pwa_bwd(const PwaArgs& args, bool /*bf16*/, hipStream_t stream, KernelTimer* timer) {
+  timer_start(timer, stream);
   PwaArgs a = args;
   const size_t plane = (size_t)a.H * a.N * a.N;
   u16* w = static_cast<u16*>(a.w);
@@ -434,13 +440,16 @@ hipError_t launch_pwa_bwd(const PwaArgs& args, bool /*bf16*/, hipStream_t stream
   sa.lse_w = nullptr;  // the backward reuses the caller's lse_w; only w, w^T are rebuilt
   hipError_t e = launch_softmax(sa, wt, stream);
   if (e != hipSuccess) return e;
+  timer_mark(timer, stream);
   {
     const size_t n8 = (size_t)a.S * a.N * a.H * a.d / 8;
     hipLaunchKernelGGL(pwa_bwd_pre_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark(timer, stream);
   }
   e = launch_gemm<false>(static_cast<const u16*>(a.da), wt, nullptr, static_cast<u16*>(a.dv), a, stream);
   if (e != hipSuccess) return e;
+  timer_mark(timer, stream);
   {
     const int dp = a.d <= 32 ? 32 : 64;
     const int nt1 = (a.N + 255) / 256;
@@ -454,11 +463,13 @@ hipError_t launch_pwa_bwd(const PwaArgs& args, bool /*bf16*/, hipStream_t stream
       hipLaunchKernelGGL(pwa_dw_kernel<64>, grid, dim3(512), 0, stream, static_cast<const u16*>(a.da),
                          static_cast<const u16*>(a.v), a.partial, a.S, a.N, a.H, a.d, a.P, spc, nt1);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark(timer, stream);
   }
   {
     const long long rows = (long long)a.H * a.N;
     hipLaunchKernelGGL(pwa_db_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark(timer, stream);
   }
   return hipSuccess;
 }

@@ -8,6 +8,8 @@ computation runs in libpba's kernels.  Layouts (contiguous, row-major):
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -125,3 +127,41 @@ def pair_weighted_avg_backward(b, v, g, key_mask, out, lse_w, dout, workspace=No
                                         _ptr(db), _ptr(workspace), workspace.numel(), _stream(v.device))
     _lib.check("pair_weighted_avg_backward", st)
     return {"dv": dv, "dg": dg, "db": db}
+
+
+# ---- measurement entry points (create HIP events and synchronise) ----------
+
+def _timed_call(fn_name, args):
+    lib = _lib.load()
+    cap = 8
+    ms = (ctypes.c_float * cap)()
+    n = ctypes.c_int(0)
+    st = getattr(lib, fn_name)(*args, ctypes.cast(ms, ctypes.c_void_p), cap, ctypes.cast(ctypes.pointer(n), ctypes.c_void_p))
+    _lib.check(fn_name, st)
+    return [float(ms[i]) for i in range(min(n.value, cap))]
+
+
+def pba_backward_timed(q, k, v, g, bias, key_mask, out, lse, dout, workspace, grads):
+    """pba_backward into preallocated `grads` (dq, dk, dv, dg, dbias); returns per-kernel ms."""
+    B, H, N, d = q.shape
+    return _timed_call("pba_backward_timed", [
+        B, H, N, d, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bias), _ptr(key_mask), _ptr(out),
+        _ptr(lse), _ptr(dout), _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]),
+        _ptr(grads["dbias"]), _ptr(workspace), workspace.numel(), _stream(q.device)])
+
+
+def pair_weighted_avg_timed(b, v, g, key_mask, out, lse_w, workspace):
+    """pair_weighted_avg into preallocated out / lse_w; returns per-kernel ms."""
+    S, N, H, d = v.shape
+    return _timed_call("pair_weighted_avg_timed", [
+        S, N, H, d, _DT[v.dtype], _ptr(b), _ptr(key_mask), _ptr(v), _ptr(g), _ptr(out), _ptr(lse_w),
+        _ptr(workspace), workspace.numel(), _stream(v.device)])
+
+
+def pair_weighted_avg_backward_timed(b, v, g, key_mask, out, lse_w, dout, workspace, grads):
+    """pair_weighted_avg_backward into preallocated `grads` (dv, dg, db); returns per-kernel ms."""
+    S, N, H, d = v.shape
+    return _timed_call("pair_weighted_avg_backward_timed", [
+        S, N, H, d, _DT[v.dtype], _ptr(b), _ptr(key_mask), _ptr(v), _ptr(g), _ptr(out), _ptr(lse_w), _ptr(dout),
+        _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["db"]), _ptr(workspace), workspace.numel(),
+        _stream(v.device)])

@@ -130,6 +130,32 @@ def test_pwa_validation(lib):
     assert g(wsb=needb - 1) == ERR_WS
 
 
+def test_timed_entry_points_validate_like_their_calls(lib):
+    """The measurement variants run the same argument checks first and need
+    both output pointers; every case here returns before anything touches a GPU."""
+    B, H, N, d = 2, 2, 64, 32
+    need = lib.pba_backward_workspace_bytes(B, H, N, d, 1)
+    p = [FAKE] * 13
+    bwd = lambda ws=FAKE, ms=FAKE, n=FAKE, d_=d: lib.pba_backward_timed(
+        B, H, N, d_, 1, p[0], p[1], p[2], p[3], p[4], None, p[5], p[6], p[7], p[8], p[9], p[10], p[11], p[12],
+        ws, need, None, ms, 4, n)
+    assert bwd(d_=20) == ERR_UNSUP
+    assert bwd(ws=None) == ERR_WS
+    assert bwd(ms=None) == ERR_NULL
+    assert bwd(n=None) == ERR_NULL
+    S, N2, H2, d2 = 4, 64, 2, 32
+    needf = lib.pair_weighted_avg_workspace_bytes(S, N2, H2, d2, 1)
+    fwd = lambda ms=FAKE, dt=1: lib.pair_weighted_avg_timed(
+        S, N2, H2, d2, dt, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, needf, None, ms, 2, FAKE)
+    assert fwd(dt=0) == ERR_UNSUP
+    assert fwd(ms=None) == ERR_NULL
+    needb = lib.pair_weighted_avg_backward_workspace_bytes(S, N2, H2, d2, 1)
+    pb = lambda ws=FAKE, ms=FAKE: lib.pair_weighted_avg_backward_timed(
+        S, N2, H2, d2, 1, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, needb, None, ms, 8, FAKE)
+    assert pb(ws=None) == ERR_WS
+    assert pb(ms=None) == ERR_NULL
+
+
 def test_binding_rejects_cpu_tensors():
     torch = pytest.importorskip("torch")
     import pair_biased_attention_amd as pba
