@@ -67,96 +67,87 @@ __global__ void __launch_bounds__(256) pwa_softmax_kernel(PwaArgs a, u16* wt) {
 // out^T[(s,c)][n] = sum_k X[s,k,h,c] * W[h,n,k]
 //   forward:  X = V,  W = w   (n = i, k = j), epilogue * sigmoid(G)
 //   dV:       X = dA, W = w^T (n = j, k = i), no epilogue
-// Workgroup tile: 256 columns (s, c) x 256 rows n, K in chunks of 64; eight
-// waves, each 64 columns x 128 rows (4 x 8 accumulator tiles).
-template <int DP>
-struct PwaGemmSmem {
-  u32x4 xt[2][16 * 2 * 64];   // X^T fragments [ct][kh][lane]
-  u32x4 w[2][16 * 2 * 64];    // W fragments   [nt][kh][lane]
-};
-
+// Workgroup tile: 256 columns (s, c) x 256 rows n of one head, K in chunks
+// of 64 tokens; eight waves, each 64 columns x 128 rows (4 x 8 accumulator
+// tiles).  X is staged row-major ([token][(s,c)], 16-byte writes) and read
+// as the A operand through the transpose read; W is staged in operand order.
+// Within each 32-token step the k slot (g, v) of both operands is token
+// 4g + v (v < 4) or 16 + 4g + v - 4 (v >= 4): one transpose read then covers
+// 16 consecutive rows, and with a row stride of 8 (mod 64) dwords those rows
+// fall in distinct LDS banks.
+// Workgroup order: n tile fastest, then head, then column tile, so the
+// workgroups that share the 128-byte lines of X (all heads of the same MSA
+// rows and tokens) run together on one XCD and its L2.
 template <int DP, bool FWD>
 __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X, const u16* __restrict__ W,
                                                        const u16* __restrict__ G, u16* __restrict__ out,
                                                        int S, int N, int H, int d, int ncolt, int nnt) {
   constexpr int SPT = 256 / DP;  // MSA rows per column tile
-  __shared__ PwaGemmSmem<DP> sm;
+  constexpr int C8 = DP / 8;     // 16-byte chunks per (s, token) row
+  constexpr int RSX = 272;       // X tile row stride (elements): 136 dwords = 8 mod 64
+  __shared__ __attribute__((aligned(16))) u16 sx[2][64 * RSX];
+  __shared__ u32x4 sw[2][16 * 2 * 64];  // W operands [nt][kh][lane]
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int wc = wave & 3, wn = wave >> 2;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int nt_blk = L % nnt;
-  const int rest = L / nnt;
-  const int colt = rest % ncolt, h = rest / ncolt;
+  const int h = (L / nnt) % H;
+  const int colt = L / (nnt * H);
   const int s0 = colt * SPT, n0 = nt_blk * 256;
   const u16* Wh = W + (size_t)h * N * N;
   const size_t srow = (size_t)N * H * d;   // stride of s in [S,N,H,d]
   const size_t krow = (size_t)H * d;       // stride of the token index
+  const bool wvec = (N & 7) == 0;
 
-  // staging assignment
-  //   X: thread -> (s_local, k quad u, c8); 4 rows k = 4u..4u+3
-  //   W: 4 chunks per thread -> (n_local, k8)
-  constexpr int C8 = DP / 8;
-  u32x4 rx[4];
-  u32x4 rw[4];
-  auto fetch = [&](int k0) {
-    {
-      const int c8 = tid % C8;
-      const int u = (tid / C8) % 16;
-      const int sl = tid / (C8 * 16);
-      const int s = s0 + sl;
+  // X staging: chunk c = tid + 512 it -> token row c / 32, 16-byte column chunk c % 32
+  // W staging: pair p = tid + 512 it -> row n, k step kh, chunk pair (m, m+2)
+  u32x4 rx[4], rw[4];
+  auto wchunk = [&](int n, int k) -> u32x4 {
+    if (n < N && wvec && k + 8 <= N) return ld16(Wh + (size_t)n * N + k);
+    uint32_t w4[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int k = k0 + 4 * u + q;
-        rx[q] = (s < S && k < N && 8 * c8 < d) ? ld16(X + s * srow + (size_t)k * krow + (size_t)h * d + 8 * c8)
-                                               : u32x4{0, 0, 0, 0};
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int kk = k + 2 * e;
+      const uint32_t lo = (n < N && kk < N) ? Wh[(size_t)n * N + kk] : 0u;
+      const uint32_t hi = (n < N && kk + 1 < N) ? Wh[(size_t)n * N + kk + 1] : 0u;
+      w4[e] = lo | (hi << 16);
     }
+    return u32x4{w4[0], w4[1], w4[2], w4[3]};
+  };
+  auto fetch = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int c = tid + 512 * it;
-      const int nl = c >> 3, k8 = c & 7;
-      const int n = n0 + nl, k = k0 + 8 * k8;
-      if (n < N && k + 8 <= N && (N & 7) == 0) {
-        rw[it] = ld16(Wh + (size_t)n * N + k);
-      } else {
-        uint32_t w4[4];
+      const int row = c >> 5, cc = c & 31;
+      const int sl = cc / C8, c8 = cc % C8;
+      const int s = s0 + sl, k = k0 + row;
+      rx[it] = (s < S && k < N && 8 * c8 < d) ? ld16(X + s * srow + (size_t)k * krow + (size_t)h * d + 8 * c8)
+                                             : u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int kk = k + 2 * e;
-          const uint32_t lo = (n < N && kk < N) ? Wh[(size_t)n * N + kk] : 0u;
-          const uint32_t hi = (n < N && kk + 1 < N) ? Wh[(size_t)n * N + kk + 1] : 0u;
-          w4[e] = lo | (hi << 16);
-        }
-        rw[it] = u32x4{w4[0], w4[1], w4[2], w4[3]};
-      }
+    for (int it = 0; it < 2; ++it) {
+      const int pr = tid + 512 * it;
+      const int nn = pr & 15, m = (pr >> 4) & 1, kh = (pr >> 5) & 1, nt = pr >> 6;
+      const int n = n0 + 16 * nt + nn, k = k0 + 32 * kh + 8 * m;
+      rw[2 * it] = wchunk(n, k);
+      rw[2 * it + 1] = wchunk(n, k + 16);
     }
   };
   auto commit = [&](int buf) {
-    {
-      const int c8 = tid % C8;
-      const int u = (tid / C8) % 16;
-      const int sl = tid / (C8 * 16);
-      const int kl0 = 4 * u;
-      const int kh = kl0 >> 5, ga = (kl0 & 31) >> 3, v0 = kl0 & 7;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int col = sl * DP + 8 * c8 + e;
-        const int ct = col >> 4, ii = col & 15;
-        uint32_t x[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) x[q] = (e & 1) ? hi16(rx[q][e >> 1]) : lo16(rx[q][e >> 1]);
-        u32x2 pk = u32x2{x[0] | (x[1] << 16), x[2] | (x[3] << 16)};
-        char* base = reinterpret_cast<char*>(&sm.xt[buf][0]);
-        *reinterpret_cast<u32x2*>(base + ((size_t)((ct * 2 + kh) * 64 + ga * 16 + ii)) * 16 + v0 * 2) = pk;
-      }
-    }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int c = tid + 512 * it;
-      const int nl = c >> 3, k8 = c & 7;
-      const int nt = nl >> 4, nn = nl & 15, kh = k8 >> 2, gg = k8 & 3;
-      sm.w[buf][(nt * 2 + kh) * 64 + gg * 16 + nn] = rw[it];
+      *reinterpret_cast<u32x4*>(&sx[buf][(c >> 5) * RSX + 8 * (c & 31)]) = rx[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int pr = tid + 512 * it;
+      const int nn = pr & 15, m = (pr >> 4) & 1, kh = (pr >> 5) & 1, nt = pr >> 6;
+      const u32x4 lo = rw[2 * it], hi = rw[2 * it + 1];  // tokens 8m..8m+7 and 16+8m..16+8m+7
+      // lane group 2m takes tokens 8m..8m+3 | 16+8m..+3, group 2m+1 the next four of each
+      sw[buf][(nt * 2 + kh) * 64 + (2 * m) * 16 + nn] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      sw[buf][(nt * 2 + kh) * 64 + (2 * m + 1) * 16 + nn] = u32x4{lo[2], lo[3], hi[2], hi[3]};
     }
   };
 
@@ -177,10 +168,11 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       bf16x8 af[4], bfr[8];
+      const int r0 = 32 * kh + 4 * g;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) af[ct] = as_bf8(sm.xt[buf][((4 * wc + ct) * 2 + kh) * 64 + lane]);
+      for (int ct = 0; ct < 4; ++ct) af[ct] = tr_frag<RSX>(sx[buf], r0, r0 + 16, 64 * wc + 16 * ct, lane);
 #pragma unroll
-      for (int nt = 0; nt < 8; ++nt) bfr[nt] = as_bf8(sm.w[buf][((8 * wn + nt) * 2 + kh) * 64 + lane]);
+      for (int nt = 0; nt < 8; ++nt) bfr[nt] = as_bf8(sw[buf][((8 * wn + nt) * 2 + kh) * 64 + lane]);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
@@ -262,10 +254,12 @@ __global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA,
   const int g = lane >> 4, ln = lane & 15;
   const int wi = wave & 3, wj = wave >> 2;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
-  // logical order: (h, p) outer, the nt1 x nt1 tiles inner
+  // logical order: the nt1 x nt1 tiles fastest, then the head, then the
+  // chunk: workgroups reading the same 128-byte lines (neighbouring heads of
+  // the same rows) are adjacent and share an XCD's L2
   const int tile = L % (nt1 * nt1);
   const int hp = L / (nt1 * nt1);
-  const int p = hp % P, h = hp / P;
+  const int h = hp % H, p = hp / H;
   const int it0 = (tile / nt1) * 256, jt0 = (tile % nt1) * 256;
   const int sb = p * spc, se = min(S, sb + spc);
   const size_t srow = (size_t)N * H * d;
@@ -382,9 +376,10 @@ static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 PwaPlan plan_pwa_bwd(int S, int N, int H, int d, bool /*bf16*/) {
   PwaPlan pl{};
+  // dw chunks over S: as many as fit one round of 256 workgroups (one per CU)
   const int nt1 = (N + 255) / 256;
   const long long tiles = (long long)nt1 * nt1 * H;
-  int P = (int)std::max<long long>(1, std::min<long long>(S / 2 > 0 ? S / 2 : 1, (256 + tiles - 1) / tiles));
+  int P = (int)std::max<long long>(1, std::min<long long>(S / 2 > 0 ? S / 2 : 1, 256 / tiles));
   pl.P = P;
   size_t off = 0;
   pl.off_w = off;                                         // w and w^T
