@@ -34,10 +34,16 @@ int check_attn_sizes(int B, int H, int N, int d, int dtype) {
   return PBA_OK;
 }
 
+// The pair-weighted-average kernels address V, G, out and the [H,N,N]
+// planes through 32-bit buffer offsets and use offsets past 2^32 - 16 as
+// "outside the tensor": every tensor stays below 2^32 - 128 bytes.
+constexpr long long kMaxPwaElems = (1LL << 31) - 64;
+
 int check_pwa_sizes(int S, int N, int H, int d, int dtype) {
   int st = check_dims(S, N, H, d, dtype, true);
   if (st != PBA_OK) return st;
-  if ((long long)H * N * N > kMaxElems) return PBA_ERR_SHAPE;
+  if ((long long)S * N * H * d > kMaxPwaElems) return PBA_ERR_SHAPE;
+  if ((long long)H * N * N > kMaxPwaElems) return PBA_ERR_SHAPE;
   return PBA_OK;
 }
 

@@ -16,6 +16,8 @@
 //   pwa_bwd_pre   dA = dO*sigmoid(G), dG = dO*O*(1-sigmoid(G))
 //   pwa_dw        split-K GEMM dw_p[h,i,j] = sum_{s in chunk p, c} dA[s,i,h,c] V[s,j,h,c]
 //   pwa_db        dw = sum_p dw_p (index order), db = w*(dw - sum_j w*dw)
+#include <type_traits>
+
 #include "pba_device.h"
 #include "pba_kernels.h"
 
@@ -75,10 +77,12 @@ __global__ void __launch_bounds__(256) pwa_softmax_kernel(PwaArgs a, u16* wt) {
 // 4g + v (v < 4) or 16 + 4g + v - 4 (v >= 4): one transpose read then covers
 // 16 consecutive rows, and with a row stride of 8 (mod 64) dwords those rows
 // fall in distinct LDS banks.
-// Workgroup order: n tile fastest, then head, then column tile, so the
-// workgroups that share the 128-byte lines of X (all heads of the same MSA
-// rows and tokens) run together on one XCD and its L2.
-template <int DP, bool FWD>
+// Workgroup order: heads go in pairs (the two 64-byte halves of one
+// 128-byte line of X at d = 32); logical order is pair, then column tile,
+// then head within the pair, then n tile.  Contiguous logical ranges run on
+// one XCD, so each XCD works on one pair at a time: both halves of every X
+// line are consumed from its L2, and the pair's two w planes stay resident.
+template <int DP, bool FWD, bool WAL>
 __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X, const u16* __restrict__ W,
                                                        const u16* __restrict__ G, u16* __restrict__ out,
                                                        int S, int N, int H, int d, int ncolt, int nnt) {
@@ -92,19 +96,29 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
   const int wc = wave & 3, wn = wave >> 2;
   const int L = xcd_remap(blockIdx.x, gridDim.x);
   const int nt_blk = L % nnt;
-  const int h = (L / nnt) % H;
-  const int colt = L / (nnt * H);
+  const int hp = (L / nnt) & 1;
+  const int colt = (L / (2 * nnt)) % ncolt;
+  const int h = 2 * (L / (2 * nnt * ncolt)) + hp;
+  if (h >= H) return;  // odd H: the last pair has one head (whole workgroup, before any barrier)
   const int s0 = colt * SPT, n0 = nt_blk * 256;
   const u16* Wh = W + (size_t)h * N * N;
   const size_t srow = (size_t)N * H * d;   // stride of s in [S,N,H,d]
   const size_t krow = (size_t)H * d;       // stride of the token index
-  const bool wvec = (N & 7) == 0;
+  // Operand loads are buffer loads with no branch around them (so the
+  // compiler can count outstanding loads exactly); an element outside the
+  // tensors gets an offset past the resource's end and reads as zero.
+  // The host limits these tensors to fewer than 2^32 - 2^7 bytes.
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+  const __amdgpu_buffer_rsrc_t xrs = make_rsrc(X, (uint32_t)((size_t)S * srow * 2));
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(Wh, (uint32_t)((size_t)N * N * 2));
 
   // X staging: chunk c = tid + 512 it -> token row c / 32, 16-byte column chunk c % 32
   // W staging: pair p = tid + 512 it -> row n, k step kh, chunk pair (m, m+2)
   u32x4 rx[4], rw[4];
   auto wchunk = [&](int n, int k) -> u32x4 {
-    if (n < N && wvec && k + 8 <= N) return ld16(Wh + (size_t)n * N + k);
+    if constexpr (WAL) {  // N % 8 == 0: a chunk is either inside a row or past it
+      return buf_load16(wrs, (n < N && k < N) ? (uint32_t)(((size_t)n * N + k) * 2) : kOob);
+    }
     uint32_t w4[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -122,8 +136,9 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
       const int row = c >> 5, cc = c & 31;
       const int sl = cc / C8, c8 = cc % C8;
       const int s = s0 + sl, k = k0 + row;
-      rx[it] = (s < S && k < N && 8 * c8 < d) ? ld16(X + s * srow + (size_t)k * krow + (size_t)h * d + 8 * c8)
-                                             : u32x4{0, 0, 0, 0};
+      rx[it] = buf_load16(xrs, (s < S && k < N && 8 * c8 < d)
+                                   ? (uint32_t)((s * srow + (size_t)k * krow + (size_t)h * d + 8 * c8) * 2)
+                                   : kOob);
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -151,6 +166,18 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
     }
   };
 
+  // A operand (X^T) of column tile ct: lane (g, j) with j = 4e + a reads
+  // the 4 columns cb + 8a .. cb + 8a + 3 of token rows r0 + e and r0 + 16 + e,
+  // where cb = 64 wc + 32 (ct / 2) + 4 (ct mod 2).  Result lane (g, n) of
+  // tiles (2p, 2p + 1) then holds columns 64 wc + 32 p + 8g .. + 7: 8
+  // consecutive channels, so the epilogue moves 16 bytes per access.
+  auto xt_frag = [&](const u16* tile, int r0, int cb, int ln_) -> bf16x8 {
+    const int j = ln_ & 15;
+    const int e = j >> 2, a = j & 3;
+    const u32x2 lo = lds_tr16(tile + (r0 + e) * RSX + cb + 8 * a);
+    const u32x2 hi = lds_tr16(tile + (r0 + 16 + e) * RSX + cb + 8 * a);
+    return as_bf8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+  };
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 acc[4][8];
 #pragma unroll
@@ -158,19 +185,28 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[ct][nt] = zero4;
 
+  // The nnt workgroups of one column tile read the same X chunks; each
+  // starts at a different chunk (rotation by its n tile) so that at any time
+  // they request different lines and later find the others' chunks in L2.
+  // Each workgroup's summation order is fixed, so results repeat.
   const int nkc = (N + 63) / 64;
-  fetch(0);
+  const int rot = (nt_blk * nkc) / nnt;
+  auto chunk_k0 = [&](int kcix) {
+    const int c = kcix + rot;
+    return 64 * (c >= nkc ? c - nkc : c);
+  };
+  fetch(chunk_k0(0));
   commit(0);
   __syncthreads();
   for (int kcix = 0; kcix < nkc; ++kcix) {
     const int buf = kcix & 1;
-    if (kcix + 1 < nkc) fetch(64 * (kcix + 1));
+    if (kcix + 1 < nkc) fetch(chunk_k0(kcix + 1));
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       bf16x8 af[4], bfr[8];
       const int r0 = 32 * kh + 4 * g;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) af[ct] = tr_frag<RSX>(sx[buf], r0, r0 + 16, 64 * wc + 16 * ct, lane);
+      for (int ct = 0; ct < 4; ++ct) af[ct] = xt_frag(sx[buf], r0, 64 * wc + 32 * (ct >> 1) + 4 * (ct & 1), lane);
 #pragma unroll
       for (int nt = 0; nt < 8; ++nt) bfr[nt] = as_bf8(sw[buf][((8 * wn + nt) * 2 + kh) * 64 + lane]);
 #pragma unroll
@@ -182,11 +218,41 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
     __syncthreads();
   }
 
-  // epilogue: lane (g, n) of tile (ct, nt) holds columns 4g..4g+3 of row n
+  // epilogue: lane (g, n) of tiles (2p, 2p + 1, nt) holds columns
+  // 64 wc + 32 p + 8g .. + 7 of row n: one MSA row's channels 8g'..8g'+7.
+  // Tiles fully inside the tensors take a branch-free path that issues the
+  // gate loads of a column pair together; ragged tiles check every element.
+  auto gate8 = [&](const f32x4& a0, const f32x4& a1, u32x4 gr) -> u32x4 {
+    float o[8] = {a0[0], a0[1], a0[2], a0[3], a1[0], a1[1], a1[2], a1[3]};
+    if constexpr (FWD) {
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) {
-    const int col = 64 * wc + 16 * ct + 4 * g;
-    const int sl = col / DP, c = col % DP;
+      for (int e = 0; e < 4; ++e) {
+        o[2 * e] *= sigmoidf_fast(bf2f(lo16(gr[e])));
+        o[2 * e + 1] *= sigmoidf_fast(bf2f(hi16(gr[e])));
+      }
+    }
+    return u32x4{pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+  };
+  const bool full = s0 + SPT <= S && n0 + 256 <= N && d == DP;
+  if (full) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int col = 64 * wc + 32 * p + 8 * g;
+      const size_t base = (s0 + col / DP) * srow + (size_t)(n0 + 128 * wn + ln) * krow + (size_t)h * d + col % DP;
+      u32x4 gr[8];
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        gr[nt] = FWD ? *reinterpret_cast<const u32x4*>(G + base + (size_t)16 * nt * krow) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        *reinterpret_cast<u32x4*>(out + base + (size_t)16 * nt * krow) = gate8(acc[2 * p][nt], acc[2 * p + 1][nt], gr[nt]);
+    }
+    return;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int col = 64 * wc + 32 * p + 8 * g;
+    const int sl = col / DP, c = col % DP;  // d is a multiple of 8: all 8 channels are valid or none
     const int s = s0 + sl;
     if (s >= S || c >= d) continue;
 #pragma unroll
@@ -194,15 +260,8 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
       const int nrow = n0 + 128 * wn + 16 * nt + ln;
       if (nrow >= N) continue;
       const size_t off = s * srow + (size_t)nrow * krow + (size_t)h * d + c;
-      f32x4 o = acc[ct][nt];
-      if constexpr (FWD) {
-        const u32x2 gr = *reinterpret_cast<const u32x2*>(G + off);
-        o[0] *= sigmoidf_fast(bf2f(lo16(gr[0])));
-        o[1] *= sigmoidf_fast(bf2f(hi16(gr[0])));
-        o[2] *= sigmoidf_fast(bf2f(lo16(gr[1])));
-        o[3] *= sigmoidf_fast(bf2f(hi16(gr[1])));
-      }
-      *reinterpret_cast<u32x2*>(out + off) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+      const u32x4 gr = FWD ? *reinterpret_cast<const u32x4*>(G + off) : u32x4{0, 0, 0, 0};
+      *reinterpret_cast<u32x4*>(out + off) = gate8(acc[2 * p][nt], acc[2 * p + 1][nt], gr);
     }
   }
 }
@@ -265,31 +324,37 @@ __global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA,
   const size_t srow = (size_t)N * H * d;
   const size_t krow = (size_t)H * d;
 
-  // per stage: SPS MSA rows x 256 tokens x C8 chunks, for each operand
+  // per stage: SPS MSA rows x 256 tokens x C8 chunks, for each operand.
+  // Chunk q of a stage is written to LDS slot q (lane-contiguous 16-byte
+  // writes): slot (t, ks, ga, r) holds token 16t + r, MSA row ks / (DP/32)
+  // of the stage, channels 8 (4 (ks mod DP/32) + ga) .. +7.  Loads are
+  // branch-free buffer loads; elements past the tensors read as zero.
   constexpr int NCHUNK = SPS * 256 * C8;    // chunks of 16 B per operand
   constexpr int PER = NCHUNK / 512;         // per thread
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(dA, (uint32_t)((size_t)S * srow * 2));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, (uint32_t)((size_t)S * srow * 2));
   u32x4 ra[PER], rb[PER];
   auto fetch = [&](int s_begin) {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int c = tid + 512 * it;
-      const int c8 = c % C8, tok = (c / C8) % 256, sl = c / (C8 * 256);
-      const int s = s_begin + sl;
+      const int q = tid + 512 * it;
+      const int r = q & 15, ga = (q >> 4) & 3, ks = (q >> 6) % KS, t = (q >> 6) / KS;
+      const int sl = ks / (DP / 32), c8 = 4 * (ks % (DP / 32)) + ga;
+      const int s = s_begin + sl, tok = 16 * t + r;
       const int ia = it0 + tok, jb = jt0 + tok;
       const bool cok = s < se && 8 * c8 < d;
-      ra[it] = (cok && ia < N) ? ld16(dA + s * srow + (size_t)ia * krow + (size_t)h * d + 8 * c8) : u32x4{0, 0, 0, 0};
-      rb[it] = (cok && jb < N) ? ld16(V + s * srow + (size_t)jb * krow + (size_t)h * d + 8 * c8) : u32x4{0, 0, 0, 0};
+      const size_t base = s * srow + (size_t)h * d + 8 * c8;
+      ra[it] = buf_load16(ars, (cok && ia < N) ? (uint32_t)((base + (size_t)ia * krow) * 2) : kOob);
+      rb[it] = buf_load16(vrs, (cok && jb < N) ? (uint32_t)((base + (size_t)jb * krow) * 2) : kOob);
     }
   };
   auto commit = [&](int buf) {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
-      const int c = tid + 512 * it;
-      const int c8 = c % C8, tok = (c / C8) % 256, sl = c / (C8 * 256);
-      const int ks = sl * (DP / 32) + (c8 >> 2), ga = c8 & 3;
-      const int t = tok >> 4, r = tok & 15;
-      sm.a[buf][(t * KS + ks) * 64 + ga * 16 + r] = ra[it];
-      sm.b[buf][(t * KS + ks) * 64 + ga * 16 + r] = rb[it];
+      const int q = tid + 512 * it;
+      sm.a[buf][q] = ra[it];
+      sm.b[buf][q] = rb[it];
     }
   };
 
@@ -301,14 +366,15 @@ __global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA,
     for (int b8 = 0; b8 < 8; ++b8) acc[a4][b8] = zero4;
 
   const int nst = se > sb ? (se - sb + SPS - 1) / SPS : 0;
+  auto stage_s = [&](int st) { return sb + SPS * st; };
   if (nst > 0) {
-    fetch(sb);
+    fetch(stage_s(0));
     commit(0);
   }
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
     const int buf = st & 1;
-    if (st + 1 < nst) fetch(sb + SPS * (st + 1));
+    if (st + 1 < nst) fetch(stage_s(st + 1));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 af[4], bfr[8];
@@ -405,11 +471,18 @@ static hipError_t launch_gemm(const u16* X, const u16* W, const u16* G, u16* out
   const int spt = 256 / dp;
   const int ncolt = (a.S + spt - 1) / spt;
   const int nnt = (a.N + 255) / 256;
-  const dim3 grid((unsigned)((long long)ncolt * nnt * a.H));
-  if (dp == 32)
-    hipLaunchKernelGGL((pwa_gemm_kernel<32, FWD>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, a.H, a.d, ncolt, nnt);
-  else
-    hipLaunchKernelGGL((pwa_gemm_kernel<64, FWD>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, a.H, a.d, ncolt, nnt);
+  const int pairs = (a.H + 1) / 2;
+  const dim3 grid((unsigned)((long long)ncolt * nnt * 2 * pairs));
+  const bool wal = (a.N & 7) == 0;
+#define PBA_GEMM_LAUNCH(DPV, WALV) \
+  hipLaunchKernelGGL((pwa_gemm_kernel<DPV, FWD, WALV>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, a.H, \
+                     a.d, ncolt, nnt)
+  if (dp == 32) {
+    if (wal) PBA_GEMM_LAUNCH(32, true); else PBA_GEMM_LAUNCH(32, false);
+  } else {
+    if (wal) PBA_GEMM_LAUNCH(64, true); else PBA_GEMM_LAUNCH(64, false);
+  }
+#undef PBA_GEMM_LAUNCH
   return hipGetLastError();
 }
 
