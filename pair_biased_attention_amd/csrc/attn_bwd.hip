@@ -490,7 +490,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 // Same decomposition as the forward kernel: 4 waves x 16*QT queries of one
 // (b, h), 64-key blocks of K and V double-buffered in LDS in row-major form.
 // S^T = K Q^T and dP^T = V dA^T read K and V row-wise; dQ^T = K^T dS^T reads
-// K through the transpose read.
+// K through the transpose read.  As in the dK/dV kernel, Q comes pre-scaled
+// by log2(e)/sqrt(d), the bias enters through two identity products (log2(e)
+// split into bf16 hi + lo) and the accumulators start at -log2(e)*LSE and -D,
+// so P = exp2(S') and dS = P * (dP - D) cost one exponential and one multiply.
+// The bias of the next key block is fetched one block ahead; masked keys get
+// the most negative bias (exp2 of it is 0) without a branch.
 template <int DP, int QT, bool ALIGNED>
 __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nqblocks) {
   constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
@@ -499,7 +504,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   __shared__ __attribute__((aligned(16))) u16 sK[2][64 * RS];
   __shared__ __attribute__((aligned(16))) u16 sV[2][64 * RS];
   __shared__ uint32_t sKeep[2][16];
-  __shared__ int sAny[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
@@ -509,7 +513,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   const int bh_lin = L / nqblocks;
   const int h = bh_lin / a.B, b = bh_lin % a.B;
   const size_t bh = (size_t)b * a.H + h;
-  const u16* Q = static_cast<const u16*>(a.q) + bh * N * d;
+  const u16* Qs = static_cast<const u16*>(a.qs) + bh * N * d;
   const u16* K = static_cast<const u16*>(a.k) + bh * N * d;
   const u16* V = static_cast<const u16*>(a.v) + bh * N * d;
   const u16* dA = static_cast<const u16*>(a.da) + bh * N * d;
@@ -549,42 +553,51 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
       *reinterpret_cast<u32x4*>(&sK[buf][kappa * RS + 8 * c8]) = rk[it];
       *reinterpret_cast<u32x4*>(&sV[buf][kappa * RS + 8 * c8]) = rv[it];
     }
-    if (tid < 64) {
-      reinterpret_cast<uint8_t*>(&sKeep[buf][0])[tid] = rkeep ? 1 : 0;
-      const unsigned long long bal = __ballot(!rkeep);
-      if (tid == 0) sAny[buf] = bal != 0ull;
+    if (tid < 64) reinterpret_cast<uint8_t*>(&sKeep[buf][0])[tid] = rkeep ? 1 : 0;
+  };
+  u32x4 bnext[QT][2];
+  auto fetch_bias = [&](int kb) {
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+      const int qrow = q0 + 16 * s + ln;
+      if constexpr (ALIGNED) {  // N % 8 == 0: 16-byte aligned rows; reads past the plane give 0
+        const uint32_t boff = (uint32_t)(((size_t)qrow * N + kb + 16 * g) * 2);
+        bnext[s][0] = buf_load16(brs, boff);
+        bnext[s][1] = buf_load16(brs, boff + 16);
+      } else {
+        bias_row16(BiasH, qrow, kb + 16 * g, N, bnext[s][0], bnext[s][1]);
+      }
     }
   };
 
   bf16x8 qf[QT][KC], daf[QT][KC];
-  float l2[QT], dd[QT];
+  f32x4 nl4[QT], nd4[QT];  // -log2(e) LSE and -D of the lane's query, as accumulator seeds
 #pragma unroll
   for (int s = 0; s < QT; ++s) {
     const int qrow = q0 + 16 * s + ln;
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
       const int c0 = 32 * kc + 8 * g;
-      u32x4 raw = u32x4{0, 0, 0, 0}, rda = u32x4{0, 0, 0, 0};
+      u32x4 rq = u32x4{0, 0, 0, 0}, rda = u32x4{0, 0, 0, 0};
       if (qrow < N && c0 < d) {
-        raw = ld16(Q + (size_t)qrow * d + c0);
+        rq = ld16(Qs + (size_t)qrow * d + c0);
         rda = ld16(dA + (size_t)qrow * d + c0);
       }
-      u32x4 sc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[e] = pack2(bf2f(lo16(raw[e])) * a.scale, bf2f(hi16(raw[e])) * a.scale);
-      qf[s][kc] = as_bf8(sc);
+      qf[s][kc] = as_bf8(rq);
       daf[s][kc] = as_bf8(rda);
     }
-    float l = kNegInf, dv = 0.f;
+    float nl = kNegInf, nd = 0.f;
     if (qrow < N) {
-      l = lse[qrow];
-      dv = drow[qrow];
+      const float l = lse[qrow];
+      nl = (l == kNegInf) ? kNegInf : -l * kLog2e;  // rows without keys: P = exp2(-inf) = 0
+      nd = -drow[qrow];
     }
-    l2[s] = (l == kNegInf) ? kPosInf : l * kLog2e;  // rows without keys: P = 0
-    dd[s] = dv;
+    nl4[s] = f32x4{nl, nl, nl, nl};
+    nd4[s] = f32x4{nd, nd, nd, nd};
   }
 
-  const bf16x8 id_lo = ident_rows_frag(lane, 0), id_hi = ident_rows_frag(lane, 1);
+  const bf16x8 id2h_lo = ident_rows_frag(lane, 0, kLog2eHiBf16), id2h_hi = ident_rows_frag(lane, 1, kLog2eHiBf16);
+  const bf16x8 id2l_lo = ident_rows_frag(lane, 0, kLog2eLoBf16), id2l_hi = ident_rows_frag(lane, 1, kLog2eLoBf16);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 dq[QT][CT];
 #pragma unroll
@@ -595,12 +608,22 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
 
   const int nkb = (N + 63) / 64;
   fetch(0);
+  fetch_bias(0);
   commit(0);
   __syncthreads();
   for (int blk = 0; blk < nkb; ++blk) {
     const int buf = blk & 1;
     const int kb = blk * 64;
-    if (blk + 1 < nkb) fetch(kb + 64);
+    u32x4 bcur[QT][2];
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+      bcur[s][0] = bnext[s][0];
+      bcur[s][1] = bnext[s][1];
+    }
+    if (blk + 1 < nkb) {
+      fetch(kb + 64);
+      fetch_bias(kb + 64);
+    }
 
     bf16x8 kf[4][KC], vf[4][KC], kt[CT][2];
     const u16* tK = sK[buf];
@@ -617,59 +640,48 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
 #pragma unroll
       for (int m = 0; m < 2; ++m) kt[ct][m] = tr_frag<RS>(tK, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
 
-    const bool masked_blk = sAny[buf] != 0;
-    u32x4 mlo = u32x4{0, 0, 0, 0}, mhi = u32x4{0, 0, 0, 0};
-    if (masked_blk) {
+    u32x4 mlo, mhi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t kw = sKeep[buf][4 * g + e];
+      const uint32_t m01 = ((kw & 0xFFu) ? 0u : 0xFFFFu) | ((kw & 0xFF00u) ? 0u : 0xFFFF0000u);
+      const uint32_t m23 = ((kw & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw & 0xFF000000u) ? 0u : 0xFFFF0000u);
+      if (e < 2) { mlo[2 * e] = m01; mlo[2 * e + 1] = m23; }
+      else { mhi[2 * (e - 2)] = m01; mhi[2 * (e - 2) + 1] = m23; }
+    }
+    // S'^T and (dP - D)^T of every sub-tile first, then the elementwise work
+    // and the dQ products as one block of code
+    f32x4 acc[QT][4], dp[QT][4];
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+      u32x4 blo = bcur[s][0], bhi = bcur[s][1];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t kw = sKeep[buf][4 * g + e];
-        const uint32_t m01 = ((kw & 0xFFu) ? 0u : 0xFFFFu) | ((kw & 0xFF00u) ? 0u : 0xFFFF0000u);
-        const uint32_t m23 = ((kw & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw & 0xFF000000u) ? 0u : 0xFFFF0000u);
-        if (e < 2) { mlo[2 * e] = m01; mlo[2 * e + 1] = m23; }
-        else { mhi[2 * (e - 2)] = m01; mhi[2 * (e - 2) + 1] = m23; }
+        blo[e] = (blo[e] & ~mlo[e]) | (kMaskedBias2 & mlo[e]);
+        bhi[e] = (bhi[e] & ~mhi[e]) | (kMaskedBias2 & mhi[e]);
+      }
+      acc[s][0] = mfma32(id2l_lo, as_bf8(blo), mfma32(id2h_lo, as_bf8(blo), nl4[s]));
+      acc[s][1] = mfma32(id2l_hi, as_bf8(blo), mfma32(id2h_hi, as_bf8(blo), nl4[s]));
+      acc[s][2] = mfma32(id2l_lo, as_bf8(bhi), mfma32(id2h_lo, as_bf8(bhi), nl4[s]));
+      acc[s][3] = mfma32(id2l_hi, as_bf8(bhi), mfma32(id2h_hi, as_bf8(bhi), nl4[s]));
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        dp[s][t] = nd4[s];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          acc[s][t] = mfma32(kf[t][kc], qf[s][kc], acc[s][t]);
+          dp[s][t] = mfma32(vf[t][kc], daf[s][kc], dp[s][t]);
+        }
       }
     }
 #pragma unroll
     for (int s = 0; s < QT; ++s) {
-      const int qrow = q0 + 16 * s + ln;
-      u32x4 blo, bhi;
-      if constexpr (ALIGNED) {
-        const uint32_t boff = (uint32_t)(((size_t)qrow * N + kb + 16 * g) * 2);
-        blo = buf_load16(brs, boff);
-        bhi = buf_load16(brs, boff + 16);
-      } else {
-        bias_row16(BiasH, qrow, kb + 16 * g, N, blo, bhi);
-      }
-      if (masked_blk) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          blo[e] = (blo[e] & ~mlo[e]) | (kMaskedBias2 & mlo[e]);
-          bhi[e] = (bhi[e] & ~mhi[e]) | (kMaskedBias2 & mhi[e]);
-        }
-      }
-      f32x4 acc[4], dp[4];
-      acc[0] = mfma32(id_lo, as_bf8(blo), zero4);
-      acc[1] = mfma32(id_hi, as_bf8(blo), zero4);
-      acc[2] = mfma32(id_lo, as_bf8(bhi), zero4);
-      acc[3] = mfma32(id_hi, as_bf8(bhi), zero4);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        dp[t] = zero4;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          acc[t] = mfma32(kf[t][kc], qf[s][kc], acc[t]);
-          dp[t] = mfma32(vf[t][kc], daf[s][kc], dp[t]);
-        }
-      }
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pr = exp2_fast(fmaf(acc[t][r], kLog2e, -l2[s]));
-          acc[t][r] = pr * (dp[t][r] - dd[s]);
-        }
-      const bf16x8 s0 = pack8(acc[0], acc[1]);
-      const bf16x8 s1 = pack8(acc[2], acc[3]);
+        for (int r = 0; r < 4; ++r) acc[s][t][r] = exp2_fast(acc[s][t][r]) * dp[s][t][r];
+      const bf16x8 s0 = pack8(acc[s][0], acc[s][1]);
+      const bf16x8 s1 = pack8(acc[s][2], acc[s][3]);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         dq[s][ct] = mfma32(kt[ct][0], s0, dq[s][ct]);

@@ -154,15 +154,43 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
   // 16 keys of lane group g are 16g..16g+15 (one 32-byte bias read per lane)
   const int krow = 16 * (ln >> 2) + (ln & 3);
 
+  // bias fragments of a key block for the wave's query sub-tiles, fetched one
+  // block ahead (16 keys 16g..16g+15 of query row q0 + 16s + ln per lane)
+  u32x4 bnext[QT][2];
+  auto fetch_bias = [&](int kb) {
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+      const int qrow = q0 + 16 * s + ln;
+      if constexpr (ALIGNED) {  // N % 8 == 0: 16-byte aligned rows; reads past the plane give 0
+        const uint32_t boff = (uint32_t)(((size_t)qrow * N + kb + 16 * g) * 2);
+        bnext[s][0] = buf_load16(brs, boff);
+        bnext[s][1] = buf_load16(brs, boff + 16);
+      } else {
+        bias_row16(static_cast<const u16*>(a.bias) + (size_t)h * N * N, qrow, kb + 16 * g, N, bnext[s][0],
+                   bnext[s][1]);
+      }
+    }
+  };
+
   const int nkb = (N + 63) / 64;
   fetch(0);
+  fetch_bias(0);
   commit(0);
   __syncthreads();
 
   for (int blk = 0; blk < nkb; ++blk) {
     const int buf = blk & 1;
     const int kb = blk * 64;
-    if (blk + 1 < nkb) fetch(kb + 64);
+    u32x4 bcur[QT][2];
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+      bcur[s][0] = bnext[s][0];
+      bcur[s][1] = bnext[s][1];
+    }
+    if (blk + 1 < nkb) {
+      fetch(kb + 64);
+      fetch_bias(kb + 64);
+    }
 
     // key-block operands shared by the wave's query sub-tiles
     bf16x8 kf[4][KC], vt[CT][2];
@@ -178,74 +206,83 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) vt[ct][m] = tr_frag<RS>(tV, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
 
-    // masked keys (and keys past N) get the most negative bias
-    const bool masked_blk = sAny[buf] != 0;
-    u32x4 mlo = u32x4{0, 0, 0, 0}, mhi = u32x4{0, 0, 0, 0};
-    if (masked_blk) {
+    // masked keys (and keys past N) get the most negative bias; the select
+    // runs on every block (all-zero masks leave the bias unchanged), so the
+    // block body has no branch and the sub-tiles' work can interleave
+    u32x4 mlo, mhi;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t kw = sKeep[buf][4 * g + e];  // keep bytes of keys 16g+4e .. +3
-        const uint32_t m01 = ((kw & 0xFFu) ? 0u : 0xFFFFu) | ((kw & 0xFF00u) ? 0u : 0xFFFF0000u);
-        const uint32_t m23 = ((kw & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw & 0xFF000000u) ? 0u : 0xFFFF0000u);
-        if (e < 2) { mlo[2 * e] = m01; mlo[2 * e + 1] = m23; }
-        else { mhi[2 * (e - 2)] = m01; mhi[2 * (e - 2) + 1] = m23; }
-      }
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t kw = sKeep[buf][4 * g + e];  // keep bytes of keys 16g+4e .. +3
+      const uint32_t m01 = ((kw & 0xFFu) ? 0u : 0xFFFFu) | ((kw & 0xFF00u) ? 0u : 0xFFFF0000u);
+      const uint32_t m23 = ((kw & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw & 0xFF000000u) ? 0u : 0xFFFF0000u);
+      if (e < 2) { mlo[2 * e] = m01; mlo[2 * e + 1] = m23; }
+      else { mhi[2 * (e - 2)] = m01; mhi[2 * (e - 2) + 1] = m23; }
     }
 
+    // scores S^T (rows: keys, columns: this wave's queries) for every
+    // sub-tile first; the bias enters through the identity product
+    f32x4 acc[QT][4];
 #pragma unroll
     for (int s = 0; s < QT; ++s) {
-      const int qrow = q0 + 16 * s + ln;
-      u32x4 blo, bhi;
-      if constexpr (ALIGNED) {  // N % 8 == 0: 16-byte aligned rows
-        const uint32_t boff = (uint32_t)(((size_t)qrow * N + kb + 16 * g) * 2);
-        blo = buf_load16(brs, boff);
-        bhi = buf_load16(brs, boff + 16);
-      } else {
-        bias_row16(static_cast<const u16*>(a.bias) + (size_t)h * N * N, qrow, kb + 16 * g, N, blo, bhi);
-      }
-      if (masked_blk) {
+      u32x4 blo = bcur[s][0], bhi = bcur[s][1];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          blo[e] = (blo[e] & ~mlo[e]) | (kMaskedBias2 & mlo[e]);
-          bhi[e] = (bhi[e] & ~mhi[e]) | (kMaskedBias2 & mhi[e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        blo[e] = (blo[e] & ~mlo[e]) | (kMaskedBias2 & mlo[e]);
+        bhi[e] = (bhi[e] & ~mhi[e]) | (kMaskedBias2 & mhi[e]);
       }
-      // scores S^T (rows: keys, columns: this wave's queries); the bias enters
-      // through the identity product so no VALU work converts it
-      f32x4 acc[4];
-      acc[0] = mfma32(id_lo, as_bf8(blo), zero4);  // keys 16g + 0..3
-      acc[1] = mfma32(id_hi, as_bf8(blo), zero4);  // keys 16g + 4..7
-      acc[2] = mfma32(id_lo, as_bf8(bhi), zero4);  // keys 16g + 8..11
-      acc[3] = mfma32(id_hi, as_bf8(bhi), zero4);  // keys 16g + 12..15
+      acc[s][0] = mfma32(id_lo, as_bf8(blo), zero4);  // keys 16g + 0..3
+      acc[s][1] = mfma32(id_hi, as_bf8(blo), zero4);  // keys 16g + 4..7
+      acc[s][2] = mfma32(id_lo, as_bf8(bhi), zero4);  // keys 16g + 8..11
+      acc[s][3] = mfma32(id_hi, as_bf8(bhi), zero4);  // keys 16g + 12..15
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) acc[t] = mfma32(kf[t][kc], qf[s][kc], acc[t]);
+        for (int kc = 0; kc < KC; ++kc) acc[s][t] = mfma32(kf[t][kc], qf[s][kc], acc[s][t]);
+    }
 
-      float mx = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
-                       fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
-      mx = fmaxf(mx, fmaxf(fmaxf(fmaxf(acc[2][0], acc[2][1]), fmaxf(acc[2][2], acc[2][3])),
-                           fmaxf(fmaxf(acc[3][0], acc[3][1]), fmaxf(acc[3][2], acc[3][3]))));
-      mx = max_over_groups(mx);
-      const float mnew = fmaxf(mrun[s], mx);
-      if (__any(mnew > mrun[s])) {
-        const float alpha = exp2_fast((mrun[s] - mnew) * kLog2e);  // 0 when mrun is -inf or masked
-        if (mnew > mrun[s]) {
+    // block maxima of every sub-tile, then one (rarely taken) rescale branch,
+    // so that the exp / pack / PV work of all sub-tiles forms one block of
+    // code the compiler can interleave (PV products of one sub-tile under the
+    // exponentials of the next).
+    // Lazy rescaling: the reference maximum moves only when a block's
+    // maximum exceeds it by more than 8 in log2 units, so P <= 2^8 between
+    // rescales (exact enough in fp32, and in bf16 for the PV product); the
+    // LSE uses the same reference.
+    float mx[QT];
+    bool grow = false;
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+      float m = fmaxf(fmaxf(fmaxf(acc[s][0][0], acc[s][0][1]), fmaxf(acc[s][0][2], acc[s][0][3])),
+                      fmaxf(fmaxf(acc[s][1][0], acc[s][1][1]), fmaxf(acc[s][1][2], acc[s][1][3])));
+      m = fmaxf(m, fmaxf(fmaxf(fmaxf(acc[s][2][0], acc[s][2][1]), fmaxf(acc[s][2][2], acc[s][2][3])),
+                         fmaxf(fmaxf(acc[s][3][0], acc[s][3][1]), fmaxf(acc[s][3][2], acc[s][3][3]))));
+      mx[s] = max_over_groups(m);
+      grow = grow || (mx[s] * kLog2e > mrun[s] * kLog2e + 8.f);
+    }
+    if (__any(grow)) {
+#pragma unroll
+      for (int s = 0; s < QT; ++s) {
+        if (mx[s] * kLog2e > mrun[s] * kLog2e + 8.f) {
+          const float mnew = fmaxf(mrun[s], mx[s]);
+          const float alpha = exp2_fast((mrun[s] - mnew) * kLog2e);  // 0 when mrun is -inf or masked
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) oacc[s][ct] *= alpha;
           lacc[s] *= alpha;
           mrun[s] = mnew;
         }
       }
+    }
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
       // a row whose keys so far are all masked keeps P = 0
       const float msc = (mrun[s] < kMaskedThreshold) ? kPosInf : mrun[s] * kLog2e;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[t][r] = exp2_fast(fmaf(acc[t][r], kLog2e, -msc));
+        for (int r = 0; r < 4; ++r) acc[s][t][r] = exp2_fast(fmaf(acc[s][t][r], kLog2e, -msc));
       // P^T as the B operand: k slot (g, v) <-> key 16g + 8m + v
-      const bf16x8 p0 = pack8(acc[0], acc[1]);
-      const bf16x8 p1 = pack8(acc[2], acc[3]);
+      const bf16x8 p0 = pack8(acc[s][0], acc[s][1]);
+      const bf16x8 p1 = pack8(acc[s][2], acc[s][3]);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) {
         oacc[s][ct] = mfma32(vt[ct][0], p0, oacc[s][ct]);
@@ -283,6 +320,302 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
       *reinterpret_cast<u32x2*>(O + off) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
     }
     if (g == 0) LSE[qrow] = l > 0.f ? mrun[s] + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
+  }
+}
+
+// ---------------------------------------------------------------- K/V-resident variant
+// For moderate N the whole K and V of one (b, h) fit in LDS: the workgroup
+// (8 waves, 128*QT queries) stages them once, synchronises once, and then
+// every wave walks all key blocks on its own -- no per-block staging, waits
+// or barriers.  Only the wave's bias fragments stream from memory,
+// prefetched one block ahead; its Q and gate rows are requested before the
+// staging barrier.
+//
+// Softmax in log2 units with a reference maximum.  Q is scaled by
+// log2(e)/sqrt(d) and the bias is multiplied by log2(e) on the matrix core
+// (two identity products, log2(e) split into bf16 hi + lo), so scores are
+// S' = log2(e) * L.  The first key block sets each query's reference r to its
+// block maximum; every later block starts its accumulators at -r, so
+// P = exp2(S') is one exponential per score.  The block's row sums (ones
+// product on the matrix core) show whether any P may exceed 2^8 (sum above
+// 2^14, or not finite); only then does the block take the slow path: true maximum, new
+// reference, rescale of the running sums, P recomputed -- the same lazy
+// rescaling the streaming kernel uses.  Rows whose reference is still -inf
+// (every key so far masked) also take the slow path.
+constexpr int kResThreads = 512;
+
+template <int DP, int QT, bool ALIGNED>
+__global__ void __launch_bounds__(kResThreads) attn_fwd_res_kernel(FwdArgs a) {
+  constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
+  constexpr int QW = 16 * QT, QBLK = 8 * QW;
+  constexpr int C8 = DP / 8;
+  constexpr int RIT = DP == 32 ? 4 : 8;  // staging chunks per thread (N up to 512)
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+  constexpr float kGrowLimit = 16384.f;  // largest block row sum of P (64 keys x 2^8) kept without rescaling
+  extern __shared__ __attribute__((aligned(16))) u16 res_lds[];
+  const int N = a.N, d = a.d;
+  const int nkb = (N + 63) / 64, NP = nkb * 64;
+  u16* const sK = res_lds;               // [NP][RS]
+  u16* const sV = sK + NP * RS;          // [NP][RS]
+  uint32_t* const sKeep = reinterpret_cast<uint32_t*>(sV + NP * RS);  // keep bytes [NP]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int g = lane >> 4, ln = lane & 15;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int qb = L % a.nqb;
+  const int bh_lin = L / a.nqb;
+  const int h = bh_lin / a.B, b = bh_lin % a.B;
+  const size_t bh = (size_t)b * a.H + h;
+  const u16* Q = static_cast<const u16*>(a.q) + bh * N * d;
+  const u16* G = static_cast<const u16*>(a.g) + bh * N * d;
+  u16* O = static_cast<u16*>(a.out) + bh * N * d;
+  float* LSE = a.lse + bh * N;
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(static_cast<const u16*>(a.bias) + (size_t)h * N * N,
+                                               (uint32_t)((size_t)N * N * 2));
+  const int q0 = qb * QBLK + wave * QW;
+  const uint32_t pb = (uint32_t)((size_t)N * d * 2);
+
+  // this wave's Q and gate rows (zero past N or d), requested first
+  const __amdgpu_buffer_rsrc_t qrs = make_rsrc(Q, pb);
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(G, pb);
+  u32x4 qraw[QT][KC];
+  u32x2 graw[QT][CT];
+#pragma unroll
+  for (int s = 0; s < QT; ++s) {
+    const int qrow = q0 + 16 * s + ln;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      const int c0 = 32 * kc + 8 * g;
+      qraw[s][kc] = buf_load16(qrs, (qrow < N && c0 < d) ? (uint32_t)((qrow * d + c0) * 2) : kOob);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int c = 16 * ct + 4 * g;
+      graw[s][ct] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                   grs, (qrow < N && c < d) ? (uint32_t)((qrow * d + c) * 2) : kOob, 0, 0));
+    }
+  }
+  {
+    // stage K and V of (b, h): buffer loads over the (b, h) plane, zero past N
+    // and past d, all issued before the first LDS store
+    const __amdgpu_buffer_rsrc_t krs = make_rsrc(static_cast<const u16*>(a.k) + bh * N * d, pb);
+    const __amdgpu_buffer_rsrc_t vrs = make_rsrc(static_cast<const u16*>(a.v) + bh * N * d, pb);
+    u32x4 rk[RIT], rv[RIT];
+#pragma unroll
+    for (int it = 0; it < RIT; ++it) {
+      const int c = tid + kResThreads * it;
+      const int key = c / C8, c8 = c % C8;
+      const uint32_t off = (8 * c8 < d) ? (uint32_t)((key * d + 8 * c8) * 2) : kOob;
+      rk[it] = buf_load16(krs, off);
+      rv[it] = buf_load16(vrs, off);
+    }
+#pragma unroll
+    for (int it = 0; it < RIT; ++it) {
+      const int c = tid + kResThreads * it;
+      const int key = c / C8, c8 = c % C8;
+      if (key < NP) {
+        *reinterpret_cast<u32x4*>(&sK[key * RS + 8 * c8]) = rk[it];
+        *reinterpret_cast<u32x4*>(&sV[key * RS + 8 * c8]) = rv[it];
+      }
+    }
+    for (int k = tid; k < NP; k += kResThreads)
+      reinterpret_cast<uint8_t*>(sKeep)[k] = (k < N && (a.mask == nullptr || a.mask[k] != 0)) ? 1 : 0;
+  }
+  __syncthreads();  // the only barrier: from here on every wave runs alone
+  if (q0 >= N) return;
+
+  const float qscale = a.scale * kLog2e;
+  bf16x8 qf[QT][KC];
+#pragma unroll
+  for (int s = 0; s < QT; ++s)
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      u32x4 sc;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        sc[e] = pack2(bf2f((u16)(qraw[s][kc][e] & 0xFFFFu)) * qscale, bf2f((u16)(qraw[s][kc][e] >> 16)) * qscale);
+      qf[s][kc] = as_bf8(sc);
+    }
+
+  const bf16x8 i2h_lo = ident_rows_frag(lane, 0, kLog2eHiBf16), i2h_hi = ident_rows_frag(lane, 1, kLog2eHiBf16);
+  const bf16x8 i2l_lo = ident_rows_frag(lane, 0, kLog2eLoBf16), i2l_hi = ident_rows_frag(lane, 1, kLog2eLoBf16);
+  const bf16x8 ones = ones_frag();
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 oacc[QT][CT];
+  f32x4 lacc[QT];
+  float ref[QT];  // reference maximum in log2 units (-inf: none yet)
+#pragma unroll
+  for (int s = 0; s < QT; ++s) {
+    lacc[s] = zero4;
+    ref[s] = kNegInf;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) oacc[s][ct] = zero4;
+  }
+  const int krow = 16 * (ln >> 2) + (ln & 3);
+
+  u32x4 bn[QT][2];
+  auto fetch_bias = [&](int kb) {  // kb < NP always (the last block is refetched at the end)
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+      const int qrow = q0 + 16 * s + ln;
+      if constexpr (ALIGNED) {
+        const uint32_t boff = (uint32_t)(((size_t)qrow * N + kb + 16 * g) * 2);
+        bn[s][0] = buf_load16(brs, boff);
+        bn[s][1] = buf_load16(brs, boff + 16);
+      } else {
+        bias_row16(static_cast<const u16*>(a.bias) + (size_t)h * N * N, qrow, kb + 16 * g, N, bn[s][0],
+                   bn[s][1]);
+      }
+    }
+  };
+  fetch_bias(0);
+
+  for (int blk = 0; blk < nkb; ++blk) {
+    const int kb = blk * 64;
+    u32x4 bcur[QT][2];
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+      bcur[s][0] = bn[s][0];
+      bcur[s][1] = bn[s][1];
+    }
+    fetch_bias(blk + 1 < nkb ? kb + 64 : kb);
+
+    bf16x8 kf[4][KC], vt[CT][2];
+    const u16* tK = sK + kb * RS;
+    const u16* tV = sV + kb * RS;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+        kf[t][kc] = as_bf8(*reinterpret_cast<const u32x4*>(tK + (krow + 4 * t) * RS + 32 * kc + 8 * g));
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) vt[ct][m] = tr_frag<RS>(tV, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
+
+    // masked keys get the most negative bias (x log2(e): -inf); only blocks
+    // that contain masked keys pay for the select
+    const uint32_t kw0 = sKeep[(kb >> 2) + 4 * g + 0], kw1 = sKeep[(kb >> 2) + 4 * g + 1];
+    const uint32_t kw2 = sKeep[(kb >> 2) + 4 * g + 2], kw3 = sKeep[(kb >> 2) + 4 * g + 3];
+    if (__any((kw0 & kw1 & kw2 & kw3) != 0x01010101u)) {
+      const uint32_t kws[4] = {kw0, kw1, kw2, kw3};
+      u32x4 mlo, mhi;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kw = kws[e];
+        const uint32_t m01 = ((kw & 0xFFu) ? 0u : 0xFFFFu) | ((kw & 0xFF00u) ? 0u : 0xFFFF0000u);
+        const uint32_t m23 = ((kw & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw & 0xFF000000u) ? 0u : 0xFFFF0000u);
+        if (e < 2) { mlo[2 * e] = m01; mlo[2 * e + 1] = m23; }
+        else { mhi[2 * (e - 2)] = m01; mhi[2 * (e - 2) + 1] = m23; }
+      }
+#pragma unroll
+      for (int s = 0; s < QT; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bcur[s][0][e] = (bcur[s][0][e] & ~mlo[e]) | (kMaskedBias2 & mlo[e]);
+          bcur[s][1][e] = (bcur[s][1][e] & ~mhi[e]) | (kMaskedBias2 & mhi[e]);
+        }
+    }
+
+    // S' (log2 units) minus the reference; rows without a reference start at 0
+    f32x4 acc[QT][4];
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+      const float seed = ref[s] == kNegInf ? 0.f : -ref[s];
+      const f32x4 c4 = {seed, seed, seed, seed};
+      const bf16x8 blo = as_bf8(bcur[s][0]), bhi = as_bf8(bcur[s][1]);
+      acc[s][0] = mfma32(i2l_lo, blo, mfma32(i2h_lo, blo, c4));  // keys 16g + 0..3
+      acc[s][1] = mfma32(i2l_hi, blo, mfma32(i2h_hi, blo, c4));  // keys 16g + 4..7
+      acc[s][2] = mfma32(i2l_lo, bhi, mfma32(i2h_lo, bhi, c4));  // keys 16g + 8..11
+      acc[s][3] = mfma32(i2l_hi, bhi, mfma32(i2h_hi, bhi, c4));  // keys 16g + 12..15
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) acc[s][t] = mfma32(kf[t][kc], qf[s][kc], acc[s][t]);
+    }
+    // fast path: P = exp2(acc) and the block row sums
+    f32x4 pv[QT][4];
+    bf16x8 p0[QT], p1[QT];
+    f32x4 bsum[QT];
+    bool slow = false;
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[s][t][r] = exp2_fast(acc[s][t][r]);
+      p0[s] = pack8(pv[s][0], pv[s][1]);
+      p1[s] = pack8(pv[s][2], pv[s][3]);
+      bsum[s] = mfma32(ones, p1[s], mfma32(ones, p0[s], zero4));
+      // not (sum <= limit) also catches NaN and +inf
+      slow = slow || ref[s] == kNegInf || !(bsum[s][0] <= kGrowLimit);
+    }
+    if (__any(slow)) {
+      // slow path: true block maxima, reference moves up (lazily, by more
+      // than 8), running sums rescaled, P and its row sums recomputed
+#pragma unroll
+      for (int s = 0; s < QT; ++s) {
+        float m = fmaxf(fmaxf(fmaxf(acc[s][0][0], acc[s][0][1]), fmaxf(acc[s][0][2], acc[s][0][3])),
+                        fmaxf(fmaxf(acc[s][1][0], acc[s][1][1]), fmaxf(acc[s][1][2], acc[s][1][3])));
+        m = fmaxf(m, fmaxf(fmaxf(fmaxf(acc[s][2][0], acc[s][2][1]), fmaxf(acc[s][2][2], acc[s][2][3])),
+                           fmaxf(fmaxf(acc[s][3][0], acc[s][3][1]), fmaxf(acc[s][3][2], acc[s][3][3]))));
+        m = max_over_groups(m);  // block maximum relative to the seed
+        const float seed = ref[s] == kNegInf ? 0.f : ref[s];
+        const float bmax = m + seed;  // absolute block maximum (-inf: every key masked so far)
+        float shift = 0.f;  // subtracted from acc
+        if (bmax > kMaskedThreshold && (ref[s] == kNegInf || bmax > ref[s] + 8.f)) {
+          if (ref[s] != kNegInf) {
+            const float alpha = exp2_fast(ref[s] - bmax);
+#pragma unroll
+            for (int ct = 0; ct < CT; ++ct) oacc[s][ct] *= alpha;
+            lacc[s] *= alpha;
+          }
+          shift = bmax - seed;
+          ref[s] = bmax;
+        } else if (ref[s] == kNegInf) {
+          shift = kPosInf;  // still no kept key: P = 0
+        }
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) pv[s][t][r] = exp2_fast(acc[s][t][r] - shift);
+        p0[s] = pack8(pv[s][0], pv[s][1]);
+        p1[s] = pack8(pv[s][2], pv[s][3]);
+        bsum[s] = mfma32(ones, p1[s], mfma32(ones, p0[s], zero4));
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < QT; ++s) {
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) {
+        oacc[s][ct] = mfma32(vt[ct][0], p0[s], oacc[s][ct]);
+        oacc[s][ct] = mfma32(vt[ct][1], p1[s], oacc[s][ct]);
+      }
+      lacc[s] += bsum[s];
+    }
+  }
+
+#pragma unroll
+  for (int s = 0; s < QT; ++s) {
+    const int qrow = q0 + 16 * s + ln;
+    if (qrow >= N) continue;
+    const float l = lacc[s][0];
+    const float inv = l > 0.f ? __builtin_amdgcn_rcpf(l) : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int c = 16 * ct + 4 * g;
+      if (c >= d) continue;
+      float o[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t w = graw[s][ct][r >> 1];
+        const float gv = bf2f((u16)((r & 1) ? (w >> 16) : (w & 0xFFFFu)));
+        o[r] = oacc[s][ct][r] * inv * sigmoidf_fast(gv);
+      }
+      *reinterpret_cast<u32x2*>(O + (size_t)qrow * d + c) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+    }
+    // natural-log LSE from the log2-unit reference
+    if (g == 0) LSE[qrow] = l > 0.f ? (ref[s] + __builtin_amdgcn_logf(l)) * kLn2 : kNegInf;
   }
 }
 
@@ -474,9 +807,31 @@ hipError_t launch_attn_fwd(const FwdArgs& args, bool bf16, hipStream_t stream) {
     else hipLaunchKernelGGL(attn_fwd_f32_kernel<64>, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
   }
+  const bool al = (a.N % 8) == 0;
+  // K/V-resident kernel when K and V of one (b, h) fit (N <= 512) and the
+  // grid still fills the chip
+  {
+    const int qt = dp == 32 ? 3 : 2;
+    const int np = (a.N + 63) / 64 * 64;
+    const int nqb = (a.N + 128 * qt - 1) / (128 * qt);
+    const size_t lds = (size_t)2 * np * (dp + 8) * 2 + np;
+    if (a.N <= 512 && bhs * nqb >= 512) {
+      a.nqb = nqb;
+      const dim3 grid((unsigned)(bhs * nqb));
+      const void* fn = dp == 32 ? (al ? reinterpret_cast<const void*>(&attn_fwd_res_kernel<32, 3, true>)
+                                      : reinterpret_cast<const void*>(&attn_fwd_res_kernel<32, 3, false>))
+                                : (al ? reinterpret_cast<const void*>(&attn_fwd_res_kernel<64, 2, true>)
+                                      : reinterpret_cast<const void*>(&attn_fwd_res_kernel<64, 2, false>));
+      hipError_t e;
+      if (lds > 64 * 1024 &&
+          (e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
+        return e;
+      void* kargs[] = {&a};
+      return hipLaunchKernel(fn, grid, dim3(kResThreads), kargs, lds, stream);
+    }
+  }
   // two query sub-tiles per wave when that still leaves enough workgroups
   const bool qt2 = dp == 32 && bhs * ((a.N + 127) / 128) >= 1024;
-  const bool al = (a.N % 8) == 0;
   a.nqb = qt2 ? (a.N + 127) / 128 : (a.N + 63) / 64;
   const dim3 grid((unsigned)(bhs * a.nqb));
 #define PBA_FWD_LAUNCH(DPV, QTV, ALV) \

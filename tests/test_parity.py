@@ -83,6 +83,9 @@ SMALL_ATTN = [
     (4, 2, 100, 32, "f32", "random:9"),
     (2, 2, 65, 48, "f32", "none"),
     (3, 1, 33, 64, "f32", "random:2"),
+    # grids of >= 512 (b, h) workgroups take the K/V-resident forward kernel
+    (128, 4, 200, 24, "bf16", "tail:7"),     # ragged N, padded d, idle waves past N
+    (64, 8, 136, 48, "bf16", "random:5"),    # d = 48 in the 64-wide template
 ]
 
 
