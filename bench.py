@@ -127,13 +127,92 @@ def cpu_baseline(cfg, target_s=15.0):
 
 
 COPY_BYTES = 256 << 20
+CALIBRATION_KERNEL = "neg"  # torch's elementwise negation: one dispatch, reads and writes COPY_BYTES
+
+# kernel of each timed phase: (symbol prefix in the HIP library, source file)
+KERNEL_SOURCES = {
+    "attn_fwd": ("attn_fwd_res_kernel", "attn_fwd.hip"),
+    "bwd_pre": ("attn_bwd_pre_bf16_kernel", "attn_bwd.hip"),
+    "bwd_dkdv": ("attn_bwd_dkdv_bf16_kernel", "attn_bwd.hip"),
+    "bwd_dq": ("attn_bwd_dq_bf16_kernel", "attn_bwd.hip"),
+    "bwd_dbias_reduce": ("bias_grad_reduce_kernel", "attn_bwd.hip"),
+    "pwa_weighted_sum": ("pwa_gemm_kernel<32, true", "pwa.hip"),
+    "pwa_bwd_pre": ("pwa_bwd_pre_kernel", "pwa.hip"),
+    "pwa_bwd_dv": ("pwa_gemm_kernel<32, false", "pwa.hip"),
+    "pwa_bwd_dw": ("pwa_dw_kernel", "pwa.hip"),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def source_digest(fname):
+    import hashlib
+    path = os.path.join(ROOT, "pair_biased_attention_amd", "csrc", fname)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_from(fetch_dir, write_dir):
+    """Per-dispatch HBM bytes from a FETCH_SIZE pass and a WRITE_SIZE pass of
+    `bench.py --counters`, each scaled by what the counter reads for the
+    calibration copy of COPY_BYTES; written to profiles/traffic.json with the
+    digest of each kernel's source file."""
+    import csv
+    import glob
+
+    def per_dispatch(d, counter):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            raise SystemExit(f"no counter_collection.csv under {d}")
+        vals, disp = {}, {}
+        for row in csv.DictReader(open(files[0])):
+            if row["Counter_Name"] != counter:
+                continue
+            name = row["Kernel_Name"].replace("void ", "")
+            vals[name] = vals.get(name, 0.0) + float(row["Counter_Value"])
+            disp.setdefault(name, set()).add(row["Dispatch_Id"])
+        return {n: vals[n] / len(disp[n]) for n in vals}
+
+    fetch = per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = per_dispatch(write_dir, "WRITE_SIZE")
+    cal = [n for n in fetch if CALIBRATION_KERNEL in n.split("(")[0].lower()]
+    if not cal:
+        raise SystemExit("calibration copy kernel not found in the FETCH_SIZE pass")
+    ff = COPY_BYTES / (fetch[cal[0]] * 1024.0)
+    fw = COPY_BYTES / (write[cal[0]] * 1024.0)
+    out = {"calibration": {"kernel": cal[0][:120], "bytes": COPY_BYTES,
+                           "fetch_size_kib": fetch[cal[0]], "write_size_kib": write[cal[0]],
+                           "fetch_factor": ff, "write_factor": fw},
+           "kernels": {}}
+    for phase, (prefix, src) in KERNEL_SOURCES.items():
+        names = [n for n in fetch if n.startswith("pba::" + prefix) or n.startswith(prefix)]
+        if not names:
+            continue
+        n = names[0]
+        out["kernels"][phase] = {"kernel": n.split("(")[0], "source": src, "source_digest": source_digest(src),
+                                 "fetch_bytes": fetch[n] * 1024.0 * ff, "write_bytes": write.get(n, 0.0) * 1024.0 * fw}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def traffic_for(phase):
+    """HBM bytes per launch of a phase's kernel from profiles/traffic.json, or
+    None when none were taken or the kernel's source changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)["kernels"][phase]
+    except (OSError, KeyError, ValueError):
+        return None
+    if t.get("source_digest") != source_digest(t["source"]):
+        return None
+    return round(t["fetch_bytes"] + t["write_bytes"])
 
 
 def counters_pass(args, torch, pba):
     """Run each kernel of interest a few times under a counter profiler."""
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
     dst = torch.empty_like(src)
-    dst.copy_(src)  # calibration: reads and writes exactly COPY_BYTES
+    torch.neg(src, out=dst)  # calibration: reads and writes exactly COPY_BYTES
     torch.cuda.synchronize()
     print(f"copy {COPY_BYTES} bytes done", flush=True)
     del src, dst
@@ -170,10 +249,14 @@ def main():
     ap.add_argument("--pwa-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pwa", action="store_true")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn a FETCH_SIZE and a WRITE_SIZE pass of --counters into profiles/traffic.json")
     ap.add_argument("--counters", action="store_true",
                     help="hardware-counter pass: a 256 MiB device copy (calibration kernel of known size), then "
                          "--steps attention steps and --pwa-steps pair-average steps; no timing, no JSON line")
     args = ap.parse_args()
+    if args.traffic_from:
+        return traffic_from(*args.traffic_from)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (no sharding, no collectives); "
               "run it with --gpus 1", file=sys.stderr)
@@ -248,7 +331,8 @@ def main():
         # in attn_kernel_flops, over its HIP-event duration
         "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(dom_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(dom_tflops / PEAK_BF16_TFLOPS, 4),
-                     "ms_per_launch": round(kernel_ms[dom], 4), "flops_per_launch": kflops[dom], "traffic": None},
+                     "ms_per_launch": round(kernel_ms[dom], 4), "flops_per_launch": kflops[dom],
+                     "traffic": traffic_for(dom)},
         "kernels_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
     }
 
@@ -301,7 +385,8 @@ def main():
             "roofline": {"kernel": "pwa_weighted_sum", "bound": "hbm", "achieved": round(ws_gbs, 1),
                          "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(ws_gbs / PEAK_HBM_GBS, 4),
                          "ms_per_launch": round(pkms["pwa_weighted_sum"], 4),
-                         "bytes_per_launch": pwa_fwd_bytes(pc.S, pc.N, pc.H, pc.d), "traffic": None},
+                         "bytes_per_launch": pwa_fwd_bytes(pc.S, pc.N, pc.H, pc.d),
+                         "traffic": traffic_for("pwa_weighted_sum")},
             "kernels_ms": {n: round(v, 4) for n, v in pkms.items()},
         }
 

@@ -185,16 +185,11 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[ct][nt] = zero4;
 
-  // The nnt workgroups of one column tile read the same X chunks; each
-  // starts at a different chunk (rotation by its n tile) so that at any time
-  // they request different lines and later find the others' chunks in L2.
-  // Each workgroup's summation order is fixed, so results repeat.
+  // The nnt workgroups of one column tile (and the two heads of a pair) take
+  // the K chunks in the same order, so each X chunk is fetched once from HBM
+  // and read by the others from L2 while it is still resident.
   const int nkc = (N + 63) / 64;
-  const int rot = (nt_blk * nkc) / nnt;
-  auto chunk_k0 = [&](int kcix) {
-    const int c = kcix + rot;
-    return 64 * (c >= nkc ? c - nkc : c);
-  };
+  auto chunk_k0 = [&](int kcix) { return 64 * kcix; };
   fetch(chunk_k0(0));
   commit(0);
   __syncthreads();
