@@ -178,9 +178,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   constexpr int NCH = DP / 32;
   constexpr int kTile = 64 * RS;
   constexpr int kCombF4 = 2 * 2 * CT * 64;
-  static_assert(kCombF4 * 16 <= 2 * kTile * 2, "combine area must fit in one staging buffer");
   __shared__ __attribute__((aligned(16))) u16 sQA[2][2 * kTile];  // [buffer][Q tile | dA tile]
   __shared__ __attribute__((aligned(16))) float sLD[2][2][64];    // [buffer][-log2(e) LSE | -D]
+  // query-half combine area of dK, dV at the end of a row; written again
+  // only nqb >= 1 iterations (and barriers) later, so one barrier suffices
+  __shared__ f32x4 comb[kCombF4];
   extern __shared__ f32x4 slab_lds[];
   f32x4* const slab = slab_lds;  // [nqb][4 query tiles][2 key tiles][64 lanes] when SLAB
 
@@ -434,9 +436,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     __syncthreads();
 
     if (last_q) {
-      // ---- combine the two query halves and store dK, dV of row b; the
-      // buffer this iteration read is free until the next iteration commits
-      f32x4* comb = reinterpret_cast<f32x4*>(sQA[S]);
+      // ---- combine the two query halves and store dK, dV of row b.  The
+      // next write of `comb` comes a row later, after at least one more
+      // barrier, so the readers below need no closing barrier.
       if (qh == 1) {
 #pragma unroll
         for (int ct = 0; ct < CT; ++ct) {
@@ -462,7 +464,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
-      __syncthreads();  // the combine area is the next commit's buffer
     }
   };
   for (int it = 0; it < T; it += 2) {
@@ -988,7 +989,8 @@ constexpr size_t kMaxSlabBytes = 112 * 1024;
 // Resident dK/dV workgroups per CU (160 KiB of LDS; at most 3 by registers).
 static int dkdv_wgs_per_cu(int N, int d, bool bf16, bool slab) {
   const size_t dp = d <= 32 ? 32 : 64;
-  size_t lds = bf16 ? 2 * 2 * 64 * (dp + 8) * 2 + 1024 : 2 * 64 * (dp + 1) * 4 + 512 + 2 * 2 * (dp / 16) * 64 * 16;
+  size_t lds = bf16 ? 2 * 2 * 64 * (dp + 8) * 2 + 1024 + 2 * 2 * (dp / 16) * 64 * 16
+                    : 2 * 64 * (dp + 1) * 4 + 512 + 2 * 2 * (dp / 16) * 64 * 16;
   if (slab) lds += slab_bytes(N, bf16);
   return (int)std::max<size_t>(1, std::min<size_t>(3, 160 * 1024 / lds));
 }
