@@ -9,7 +9,8 @@
 // Four launches on the caller's stream, no host synchronisation:
 //   1. attn_bwd_pre      dA = dO*sigmoid(G), dG = dO*O*(1-sigmoid(G)),
 //                        D = rowsum(dO*O)  (= rowsum(P*dP), so dS = P*(dP-D)),
-//                        and (bf16) Q * log2(e) / sqrt(d) for the dK/dV kernel
+//                        and (bf16) Q * log2(e) / sqrt(d) and the row seeds
+//                        (-log2(e) * LSE, -D) for the two gradient kernels
 //   2. attn_bwd_dkdv     key-stationary: each workgroup owns 32 keys of one
 //                        head for a chunk of C batch rows; per row it walks all
 //                        queries, accumulates dK, dV in registers, and adds dS
@@ -120,7 +121,9 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int r
   if (tid < rows_per_wg && row0 + tid < rows) {
     float s = 0.f;
     for (int j = 0; j < L; ++j) s += sPart[tid * L + j];
-    a.drow[row0 + tid] = s;
+    const float l = a.lse[row0 + tid];
+    // rows without keys (LSE = -inf) get the seed -inf, so P = exp2(-inf) = 0
+    a.seed[row0 + tid] = make_float2(l == kNegInf ? kNegInf : -l * kLog2e, -s);
   }
 }
 
@@ -167,9 +170,9 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_f32_kernel(BwdArgs a) {
 template <int DP>
 struct DkdvStage {
   u32x4 q[DP / 32], da[DP / 32];  // Q and dA chunks of the staged tile
-  u32x4 k[DP / 32], v[DP / 32];   // this lane's K and V row of the tile's batch row
-  u32x4 bias[2];                  // bias fragments of the wave's two query tiles
-  float l, dd;                    // LSE and D of query (tid mod 64) of the block
+  u32x4 k[DP / 32], v[DP / 32];   // this lane's K and V row (fetched with a row's first query block)
+  u32x4 bias;                     // bias of the wave's query tiles: lane groups 0-1 tile 0, 2-3 tile 1
+  float2 seed;                    // (-log2(e) LSE, -D) of query `lane` of the block (wave 0)
 };
 
 template <int DP, bool ALIGNED, bool SLAB>
@@ -229,37 +232,35 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     col[c8i] = 8 * (c % (DP / 8));
     chunk_off[c8i] = (uint32_t)((kap[c8i] * d + col[c8i]) * 2);
   }
-  // this lane's bias rows: queries 16(2qh+j)+n of the block, keys k0..k0+7
-  // (lanes g and g+2 fetch the same values; the identity keeps groups 0-1)
+  // this lane's bias: query row 16(2qh+j)+n of the block with j = g/2, keys
+  // k0..k0+7.  One 16-byte load per lane covers both query tiles of the wave;
+  // the identity product of tile j reads lane groups 2j and 2j+1.
   const int k0 = kb + 16 * kt + 8 * (g & 1);
-  uint32_t bias_off[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) bias_off[j] = (uint32_t)(((16 * (2 * qh + j) + n) * N + k0) * 2);
+  const int bq = 16 * (2 * qh + (g >> 1)) + n;
+  const uint32_t bias_off = (uint32_t)((bq * N + k0) * 2);
   bool colok[KC];
 #pragma unroll
   for (int kc = 0; kc < KC; ++kc) colok[kc] = 32 * kc + 8 * g < d;
 
   DkdvStage<DP> R[2];
-  // Buffer resources of the next fetch's (b, h) plane, rebuilt only when that
-  // row changes.  Past the chunk they are empty (zeros, no traffic); the LSE
-  // and D rows are fetched by wave 0 only, K and V rows only for the first
-  // query block of a row: the other waves and steps issue the same loads
-  // against empty resources.
+  // Buffer resources of the next fetch's (b, h) plane.  Past the chunk they
+  // are empty (zeros, no traffic).  Every buffer load costs address-unit time
+  // whatever it moves, so only the loads a step needs are issued: K and V
+  // rows with a row's first query block, the row seeds by wave 0.  Both
+  // conditions are uniform across the wave.
   const size_t row_step = (size_t)H * plane;
   const u16* fK = static_cast<const u16*>(a.k) + ((size_t)b0 * H + h) * plane;
   const u16* fV = static_cast<const u16*>(a.v) + ((size_t)b0 * H + h) * plane;
   const u16* fQs = static_cast<const u16*>(a.qs) + ((size_t)b0 * H + h) * plane;
   const u16* fdA = static_cast<const u16*>(a.da) + ((size_t)b0 * H + h) * plane;
-  const float* fL = a.lse + ((size_t)b0 * H + h) * N;
-  const float* fD = a.drow + ((size_t)b0 * H + h) * N;
-  uint32_t rec_plane = plane_bytes, rec_row = wave == 0 ? (uint32_t)N * 4u : 0u;
+  const float2* fS = a.seed + ((size_t)b0 * H + h) * N;
+  uint32_t rec_plane = plane_bytes, rec_row = (uint32_t)N * 8u;
   auto next_row = [&]() {
     fQs += row_step;
     fdA += row_step;
     fK += row_step;
     fV += row_step;
-    fL += (size_t)H * N;
-    fD += (size_t)H * N;
+    fS += (size_t)H * N;
   };
   int fb = b0, fq = 0;
   auto advance_fetch = [&]() {
@@ -273,33 +274,28 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   auto fetch = [&](DkdvStage<DP>& st, int qblk) {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(fQs, rec_plane);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(fdA, rec_plane);
-    const uint32_t rec_kv = qblk == 0 ? rec_plane : 0u;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(fK, rec_kv);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(fV, rec_kv);
-    const __amdgpu_buffer_rsrc_t rl = make_rsrc(fL, rec_row);
-    const __amdgpu_buffer_rsrc_t rd = make_rsrc(fD, rec_row);
     const uint32_t qoff = (uint32_t)(qblk * 64 * d * 2);
 #pragma unroll
     for (int c8i = 0; c8i < NCH; ++c8i) {
       st.q[c8i] = buf_load16(rq, chunk_off[c8i] + qoff);
       st.da[c8i] = buf_load16(ra, chunk_off[c8i] + qoff);
     }
+    if (qblk == 0) {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(fK, rec_plane);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(fV, rec_plane);
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const uint32_t off = (uint32_t)((key * d + 32 * kc + 8 * g) * 2);
-      st.k[kc] = buf_load16(rk, off);
-      st.v[kc] = buf_load16(rv, off);
-    }
-    st.l = buf_load_f32(rl, (uint32_t)((qblk * 64 + lane) * 4));
-    st.dd = buf_load_f32(rd, (uint32_t)((qblk * 64 + lane) * 4));
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if constexpr (ALIGNED) {
-        st.bias[j] = buf_load16(brs, bias_off[j] + (uint32_t)(qblk * 64 * N * 2));
-      } else {
-        const int qa = qblk * 64 + 16 * (2 * qh + j) + n;
-        st.bias[j] = (qa < N) ? load_bias8(BiasH + (size_t)qa * N, k0, N, false) : u32x4{0, 0, 0, 0};
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint32_t off = (uint32_t)((key * d + 32 * kc + 8 * g) * 2);
+        st.k[kc] = buf_load16(rk, off);
+        st.v[kc] = buf_load16(rv, off);
       }
+    }
+    if (wave == 0) st.seed = buf_load_f32x2(make_rsrc(fS, rec_row), (uint32_t)((qblk * 64 + lane) * 8));
+    if constexpr (ALIGNED) {
+      st.bias = buf_load16(brs, bias_off + (uint32_t)(qblk * 64 * N * 2));
+    } else {
+      const int qa = qblk * 64 + bq;
+      st.bias = (qa < N) ? load_bias8(BiasH + (size_t)qa * N, k0, N, false) : u32x4{0, 0, 0, 0};
     }
   };
   auto commit = [&](const DkdvStage<DP>& st, int buf, int qblk) {
@@ -310,15 +306,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
       *reinterpret_cast<u32x4*>(&tQ[kTile + kap[c8i] * RS + col[c8i]]) = st.da[c8i];
     }
     if (tid < 64) {
-      // queries past N and rows without keys (LSE = -inf) get P = exp2(-inf) = 0
-      const bool live = qblk * 64 + tid < N && st.l != kNegInf;
-      sLD[buf][0][tid] = live ? -st.l * kLog2e : kNegInf;
-      sLD[buf][1][tid] = -st.dd;
+      // queries past N get P = exp2(-inf) = 0 (rows without keys carry a -inf seed)
+      sLD[buf][0][tid] = qblk * 64 + tid < N ? st.seed.x : kNegInf;
+      sLD[buf][1][tid] = st.seed.y;
     }
   };
 
-  const bf16x8 id_l2hi = ident_cols_frag(lane, kLog2eHiBf16);
-  const bf16x8 id_l2lo = ident_cols_frag(lane, kLog2eLoBf16);
+  const bf16x8 id_l2hi[2] = {ident_cols_frag(lane, kLog2eHiBf16, 0), ident_cols_frag(lane, kLog2eHiBf16, 2)};
+  const bf16x8 id_l2lo[2] = {ident_cols_frag(lane, kLog2eLoBf16, 0), ident_cols_frag(lane, kLog2eLoBf16, 2)};
   const bf16x8 id_lo = ident_rows_frag(lane, 0), id_hi = ident_rows_frag(lane, 1);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const u32x4 zero_u4 = {0u, 0u, 0u, 0u};
@@ -376,9 +371,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     // the bias of this iteration is read from its register stage before the
     // loads of iteration it+2 reuse the stage
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sacc[j] = mfma32(as_bf8(R[S].bias[j]), id_l2hi, sacc[j]);
+    for (int j = 0; j < 2; ++j) sacc[j] = mfma32(as_bf8(R[S].bias), id_l2hi[j], sacc[j]);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sacc[j] = mfma32(as_bf8(R[S].bias[j]), id_l2lo, sacc[j]);
+    for (int j = 0; j < 2; ++j) sacc[j] = mfma32(as_bf8(R[S].bias), id_l2lo[j], sacc[j]);
     fetch(R[S], fq);  // iteration it+2
     advance_fetch();
 #pragma unroll
@@ -462,6 +457,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
           *reinterpret_cast<u32x2*>(dV + (size_t)key * d + c) = u32x2{pack2(sv[0], sv[1]), pack2(sv[2], sv[3])};
         }
       }
+      // Stores share the vector-memory counter with loads.  With stores
+      // outstanding the compiler cannot count loads in order and waits for
+      // the counter to drain before every later use of a fetched stage;
+      // draining it here once per row keeps those waits exact.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 #pragma unroll
       for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
     }
@@ -519,8 +519,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   const u16* V = static_cast<const u16*>(a.v) + bh * N * d;
   const u16* dA = static_cast<const u16*>(a.da) + bh * N * d;
   const u16* BiasH = static_cast<const u16*>(a.bias) + (size_t)h * N * N;
-  const float* lse = a.lse + bh * N;
-  const float* drow = a.drow + bh * N;
+  const float2* seed = a.seed + bh * N;
   u16* dQ = static_cast<u16*>(a.dq) + bh * N * d;
   const int q0 = qb * QBLK + wave * QW;
   const __amdgpu_buffer_rsrc_t brs = make_rsrc(BiasH, (uint32_t)((size_t)N * N * 2));
@@ -587,11 +586,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
       qf[s][kc] = as_bf8(rq);
       daf[s][kc] = as_bf8(rda);
     }
-    float nl = kNegInf, nd = 0.f;
+    float nl = kNegInf, nd = 0.f;  // rows without keys carry a -inf seed: P = exp2(-inf) = 0
     if (qrow < N) {
-      const float l = lse[qrow];
-      nl = (l == kNegInf) ? kNegInf : -l * kLog2e;  // rows without keys: P = exp2(-inf) = 0
-      nd = -drow[qrow];
+      const float2 sd = seed[qrow];
+      nl = sd.x;
+      nd = sd.y;
     }
     nl4[s] = f32x4{nl, nl, nl, nl};
     nd4[s] = f32x4{nd, nd, nd, nd};
@@ -1035,8 +1034,8 @@ BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16) {
   off = align256(off + rows * d * (bf16 ? 2 : 4));
   pl.off_qs = off;
   if (bf16) off = align256(off + rows * d * 2);
-  pl.off_drow = off;
-  off = align256(off + rows * 4);
+  pl.off_drow = off;  // fp32: D per row; bf16: (-log2(e) LSE, -D) pairs
+  off = align256(off + rows * (bf16 ? 8 : 4));
   pl.off_partial = off;
   off = align256(off + (size_t)pl.P * H * N * N * 4);
   pl.total = off;

@@ -79,7 +79,8 @@ int prep_backward(int B, int H, int N, int d, int dtype, const void* q, const vo
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbias = dbias;
   a.da = ws + pl.off_da;
   a.qs = bf16 ? ws + pl.off_qs : nullptr;
-  a.drow = reinterpret_cast<float*>(ws + pl.off_drow);
+  a.drow = bf16 ? nullptr : reinterpret_cast<float*>(ws + pl.off_drow);
+  a.seed = bf16 ? reinterpret_cast<float2*>(ws + pl.off_drow) : nullptr;
   a.partial = reinterpret_cast<float*>(ws + pl.off_partial);
   a.B = B; a.H = H; a.N = N; a.d = d;
   a.scale = attn_scale(d);

@@ -91,14 +91,15 @@ __device__ __forceinline__ bf16x8 ident_rows_frag(int lane, int half, uint32_t o
   }
   return as_bf8(r);
 }
-// B operand, lane (g, n), register v: 1 where g < 2 and n == 8g + v.  With
-// A lane (g, i) holding row i's entries 8g..8g+7 (lanes g >= 2 may hold any
-// finite values), D[i][n] = A[i][n]: the transpose of the A tile lands in the
-// result layout.
-__device__ __forceinline__ bf16x8 ident_cols_frag(int lane, uint32_t one = 0x3F80u) {
+// B operand, lane (g, n), register v: 1 where g0 <= g < g0 + 2 and
+// n == 8(g - g0) + v (g0 = 0 or 2).  With A lane (g, i) holding row i's
+// entries 8g..8g+7 (the lanes of the other two groups may hold any finite
+// values), D[i][n] = A[i][8 g0 + n]: the transpose of the half of the A
+// tile that groups g0, g0+1 hold lands in the result layout.
+__device__ __forceinline__ bf16x8 ident_cols_frag(int lane, uint32_t one = 0x3F80u, int g0 = 0) {
   const int g = lane >> 4, n = lane & 15;
   u32x4 r = {0u, 0u, 0u, 0u};
-  if (g < 2 && (n >> 3) == g) {
+  if (g >= g0 && g < g0 + 2 && (n >> 3) == g - g0) {
     const int v = n & 7;
     r[v >> 1] = one << (16 * (v & 1));
   }
@@ -143,6 +144,13 @@ __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t b
 __device__ __forceinline__ float buf_load_f32(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0));
 }
+__device__ __forceinline__ float2 buf_load_f32x2(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
+}
+
+// s_waitcnt immediate: vmcnt = 0, expcnt and lgkmcnt left at their maxima
+// (no wait on them).
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 // Most negative finite bf16 (-3.39e38), packed twice: the bias value given to
 // masked keys so their scores stay finite through the identity product

@@ -40,7 +40,9 @@ struct BwdArgs {
   // workspace views
   void* da;         // dA = dout * sigmoid(G), [B,H,N,d] (bf16 for bf16 inputs, fp32 otherwise)
   void* qs;         // Q / sqrt(d) rounded to bf16, [B,H,N,d] (bf16 inputs only)
-  float* drow;      // D = rowsum(dout * out), [B,H,N]
+  float* drow;      // fp32 inputs: D = rowsum(dout * out), [B,H,N]
+  float2* seed;     // bf16 inputs: per query row (-log2(e) * LSE, or -inf for a row
+                    // without keys; -D), [B,H,N]: the accumulator seeds of S' and dP - D
   float* partial;   // dBias partial sums, [P,H,N,N]
   int B, H, N, d;
   float scale;
