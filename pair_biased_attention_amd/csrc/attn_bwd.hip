@@ -504,7 +504,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   constexpr int NCH = DP / 32;
   __shared__ __attribute__((aligned(16))) u16 sK[2][64 * RS];
   __shared__ __attribute__((aligned(16))) u16 sV[2][64 * RS];
-  __shared__ uint32_t sKeep[2][16];
+  // keep bytes of every key (dynamic, 64 per key block): filled once, so the
+  // key loop issues no mask loads
+  extern __shared__ uint32_t keep_lds[];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
@@ -524,25 +526,22 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   const int q0 = qb * QBLK + wave * QW;
   const __amdgpu_buffer_rsrc_t brs = make_rsrc(BiasH, (uint32_t)((size_t)N * N * 2));
 
+  // K and V go through buffer resources spanning their plane: keys past N
+  // read as zeros, so every load of a fetch is issued unconditionally and the
+  // compiler waits for exactly the block it commits.  Columns d..DP-1 of a
+  // chunk hold the next key's leading values; they meet only zero Q / dA
+  // columns or land in dQ columns that are never stored.
+  const uint32_t kv_bytes = (uint32_t)((size_t)N * d * 2);
+  const __amdgpu_buffer_rsrc_t rsK = make_rsrc(K, kv_bytes), rsV = make_rsrc(V, kv_bytes);
   u32x4 rk[NCH], rv[NCH];
-  bool rkeep = true;
   auto fetch = [&](int kb) {
 #pragma unroll
     for (int it = 0; it < NCH; ++it) {
       const int c = tid + 256 * it;
       const int kappa = c / (DP / 8), c8 = c % (DP / 8);
-      const int key = kb + kappa;
-      if (key < N && 8 * c8 < d) {
-        rk[it] = ld16(K + (size_t)key * d + 8 * c8);
-        rv[it] = ld16(V + (size_t)key * d + 8 * c8);
-      } else {
-        rk[it] = u32x4{0, 0, 0, 0};
-        rv[it] = u32x4{0, 0, 0, 0};
-      }
-    }
-    if (tid < 64) {
-      const int key = kb + tid;
-      rkeep = key < N && (a.mask == nullptr || a.mask[key] != 0);
+      const uint32_t off = (uint32_t)(((kb + kappa) * d + 8 * c8) * 2);
+      rk[it] = buf_load16(rsK, off);
+      rv[it] = buf_load16(rsV, off);
     }
   };
   auto commit = [&](int buf) {
@@ -553,7 +552,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
       *reinterpret_cast<u32x4*>(&sK[buf][kappa * RS + 8 * c8]) = rk[it];
       *reinterpret_cast<u32x4*>(&sV[buf][kappa * RS + 8 * c8]) = rv[it];
     }
-    if (tid < 64) reinterpret_cast<uint8_t*>(&sKeep[buf][0])[tid] = rkeep ? 1 : 0;
   };
   u32x4 bnext[QT][2];
   auto fetch_bias = [&](int kb) {
@@ -607,6 +605,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   const int krow = 16 * (ln >> 2) + (ln & 3);
 
   const int nkb = (N + 63) / 64;
+  for (int k = tid; k < nkb * 64; k += 256)
+    reinterpret_cast<uint8_t*>(keep_lds)[k] = (k < N && (a.mask == nullptr || a.mask[k] != 0)) ? 1 : 0;
   fetch(0);
   fetch_bias(0);
   commit(0);
@@ -620,10 +620,13 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
       bcur[s][0] = bnext[s][0];
       bcur[s][1] = bnext[s][1];
     }
-    if (blk + 1 < nkb) {
-      fetch(kb + 64);
-      fetch_bias(kb + 64);
-    }
+    // the next block's loads (past the last block they read zeros and are
+    // never used; issuing them anyway keeps every iteration's loads alike)
+    fetch(kb + 64);
+    fetch_bias(kb + 64);
+    // keep these loads here, a whole iteration ahead of their use (the
+    // scheduler would otherwise sink them next to the commit)
+    __builtin_amdgcn_sched_barrier(0);
 
     bf16x8 kf[4][KC], vf[4][KC], kt[CT][2];
     const u16* tK = sK[buf];
@@ -643,7 +646,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     u32x4 mlo, mhi;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t kw = sKeep[buf][4 * g + e];
+      const uint32_t kw = keep_lds[(kb >> 2) + 4 * g + e];
       const uint32_t m01 = ((kw & 0xFFu) ? 0u : 0xFFFFu) | ((kw & 0xFF00u) ? 0u : 0xFFFF0000u);
       const uint32_t m23 = ((kw & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw & 0xFF000000u) ? 0u : 0xFFFF0000u);
       if (e < 2) { mlo[2 * e] = m01; mlo[2 * e + 1] = m23; }
@@ -688,7 +691,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
         dq[s][ct] = mfma32(kt[ct][1], s1, dq[s][ct]);
       }
     }
-    if (blk + 1 < nkb) commit(buf ^ 1);
+    commit(buf ^ 1);
     __syncthreads();
   }
 
@@ -1099,8 +1102,9 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
       const bool al = (a.N % 8) == 0;
       const int nqb = qt2 ? (a.N + 127) / 128 : (a.N + 63) / 64;
       const dim3 grid((unsigned)(bhs * nqb));
+      const size_t keep_bytes = (size_t)((a.N + 63) / 64) * 64;
 #define PBA_DQ_LAUNCH(DPV, QTV, ALV) \
-  hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<DPV, QTV, ALV>), grid, dim3(256), 0, stream, a, nqb)
+  hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<DPV, QTV, ALV>), grid, dim3(256), keep_bytes, stream, a, nqb)
       if (dp == 32) {
         if (qt2) { if (al) PBA_DQ_LAUNCH(32, 2, true); else PBA_DQ_LAUNCH(32, 2, false); }
         else { if (al) PBA_DQ_LAUNCH(32, 1, true); else PBA_DQ_LAUNCH(32, 1, false); }
