@@ -9,8 +9,8 @@
 // Four launches on the caller's stream, no host synchronisation:
 //   1. attn_bwd_pre      dA = dO*sigmoid(G), dG = dO*O*(1-sigmoid(G)),
 //                        D = rowsum(dO*O)  (= rowsum(P*dP), so dS = P*(dP-D)),
-//                        and (bf16) Q * log2(e) / sqrt(d) and the row seeds
-//                        (-log2(e) * LSE, -D) for the two gradient kernels
+//                        and (bf16) the row seeds (-log2(e) * LSE, -D) of the
+//                        two gradient kernels
 //   2. attn_bwd_dkdv     key-stationary: each workgroup owns 32 keys of one
 //                        head for a chunk of C batch rows; per row it walks all
 //                        queries, accumulates dK, dV in registers, and adds dS
@@ -87,15 +87,13 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int r
   const long long row0 = (long long)blockIdx.x * rows_per_wg;
   const int r = tid / L, c = tid % L;
   const long long row = row0 + r;
-  const float qscale = a.scale * kLog2e;
   float D = 0.f;
   if (r < rows_per_wg && row < rows) {
     const size_t off = (size_t)row * a.d + 8 * c;
     const u32x4 xo = ld16(static_cast<const u16*>(a.dout) + off);
     const u32x4 xv = ld16(static_cast<const u16*>(a.out) + off);
     const u32x4 xg = ld16(static_cast<const u16*>(a.g) + off);
-    const u32x4 xq = ld16(static_cast<const u16*>(a.q) + off);
-    u32x4 ra, rg, rq;
+    u32x4 ra, rg;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float f[2], s[2], o[2], ga[2], gg[2];
@@ -110,11 +108,9 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int r
       }
       ra[e] = pack2(ga[0], ga[1]);
       rg[e] = pack2(gg[0], gg[1]);
-      rq[e] = pack2(bf2f(lo16(xq[e])) * qscale, bf2f(hi16(xq[e])) * qscale);
     }
     *reinterpret_cast<u32x4*>(static_cast<u16*>(a.da) + off) = ra;
     *reinterpret_cast<u32x4*>(static_cast<u16*>(a.dg) + off) = rg;
-    *reinterpret_cast<u32x4*>(static_cast<u16*>(a.qs) + off) = rq;
   }
   sPart[tid] = D;
   __syncthreads();
@@ -150,17 +146,17 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_f32_kernel(BwdArgs a) {
 // ------------------------------------------------------------------ 2. dK, dV, dBias (bf16)
 // One workgroup = 4 waves = 32 keys of one head, for a chunk of C batch rows.
 // Wave (kt, qh) owns keys kb+16kt..+15 and query half qh of every 64-query
-// block.  Iteration `it` covers (row b, query block); its Q tile (pre-scaled
-// by log2(e)/sqrt(d) in the preprocess step), dA tile, -log2(e)*LSE and -D
-// rows sit in one of two LDS buffers, and the loads of iteration it+2 are in
+// block.  Iteration `it` covers (row b, query block); its Q tile, dA tile,
+// -log2(e)*LSE and -D rows sit in one of two LDS buffers, and the loads of iteration it+2 are in
 // flight in registers while iteration it computes, so one barrier per
 // iteration suffices and HBM latency is hidden behind two iterations.
-//   S' = log2(e) * (Q K^T / sqrt(d) + bias) - log2(e) * LSE: the bias enters
-//        through two identity products (log2(e) split into bf16 hi + lo) and
+//   S' = log2(e) * (Q K^T / sqrt(d) + bias) - log2(e) * LSE: K is held
+//        pre-multiplied by log2(e)/sqrt(d), the bias enters through two
+//        identity products (log2(e) split into bf16 hi + lo) and
 //        -log2(e) * LSE as the accumulator's initial value, so P = exp2(S').
 //   dP - D = dA V^T accumulated onto -D;  dS = P * (dP - D).
 //   dV^T += dA^T P and dK^T += Q^T dS read the staged tiles through the
-//   transpose read; dK is rescaled by ln 2 / 1 at the end (Q carried log2(e)).
+//   transpose read; dK takes the 1/sqrt(d) factor at the store.
 // dBias: with `slab`, each wave adds dS of every row of the chunk into an LDS
 // slab kept in accumulator layout (16 bytes per lane per tile, so no bank
 // conflicts), through an identity product that reads the slab tile as its
@@ -251,12 +247,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   const size_t row_step = (size_t)H * plane;
   const u16* fK = static_cast<const u16*>(a.k) + ((size_t)b0 * H + h) * plane;
   const u16* fV = static_cast<const u16*>(a.v) + ((size_t)b0 * H + h) * plane;
-  const u16* fQs = static_cast<const u16*>(a.qs) + ((size_t)b0 * H + h) * plane;
+  const u16* fQ = static_cast<const u16*>(a.q) + ((size_t)b0 * H + h) * plane;
   const u16* fdA = static_cast<const u16*>(a.da) + ((size_t)b0 * H + h) * plane;
   const float2* fS = a.seed + ((size_t)b0 * H + h) * N;
   uint32_t rec_plane = plane_bytes, rec_row = (uint32_t)N * 8u;
   auto next_row = [&]() {
-    fQs += row_step;
+    fQ += row_step;
     fdA += row_step;
     fK += row_step;
     fV += row_step;
@@ -272,7 +268,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
     }
   };
   auto fetch = [&](DkdvStage<DP>& st, int qblk) {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(fQs, rec_plane);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(fQ, rec_plane);
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(fdA, rec_plane);
     const uint32_t qoff = (uint32_t)(qblk * 64 * d * 2);
 #pragma unroll
@@ -321,10 +317,16 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   f32x4 dk[CT], dv[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
+  // K enters the score product pre-multiplied by log2(e)/sqrt(d) (rounded
+  // once to bf16), so the products give S' in log2 units directly
+  const float kscale = a.scale * kLog2e;
   auto take_kv = [&](const DkdvStage<DP>& st) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      kf[kc] = as_bf8(colok[kc] ? st.k[kc] : zero_u4);
+      u32x4 ks;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ks[e] = pack2(bf2f(lo16(st.k[kc][e])) * kscale, bf2f(hi16(st.k[kc][e])) * kscale);
+      kf[kc] = as_bf8(colok[kc] ? ks : zero_u4);
       vf[kc] = as_bf8(colok[kc] ? st.v[kc] : zero_u4);
     }
   };
@@ -450,8 +452,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
         for (int ct = 0; ct < CT; ++ct) {
           const int c = 16 * ct + 4 * g;
           if (c >= d) continue;
-          // the staged Q carried log2(e) / sqrt(d); dK needs 1 / sqrt(d)
-          const f32x4 sk = (dk[ct] + comb[((kt * 2 + 0) * CT + ct) * 64 + lane]) * kLn2;
+          const f32x4 sk = (dk[ct] + comb[((kt * 2 + 0) * CT + ct) * 64 + lane]) * a.scale;
           const f32x4 sv = dv[ct] + comb[((kt * 2 + 1) * CT + ct) * 64 + lane];
           *reinterpret_cast<u32x2*>(dK + (size_t)key * d + c) = u32x2{pack2(sk[0], sk[1]), pack2(sk[2], sk[3])};
           *reinterpret_cast<u32x2*>(dV + (size_t)key * d + c) = u32x2{pack2(sv[0], sv[1]), pack2(sv[2], sv[3])};
@@ -491,9 +492,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 // Same decomposition as the forward kernel: 4 waves x 16*QT queries of one
 // (b, h), 64-key blocks of K and V double-buffered in LDS in row-major form.
 // S^T = K Q^T and dP^T = V dA^T read K and V row-wise; dQ^T = K^T dS^T reads
-// K through the transpose read.  As in the dK/dV kernel, Q comes pre-scaled
-// by log2(e)/sqrt(d), the bias enters through two identity products (log2(e)
-// split into bf16 hi + lo) and the accumulators start at -log2(e)*LSE and -D,
+// K through the transpose read.  The wave's Q rows are scaled by
+// log2(e)/sqrt(d) once in registers, the bias enters through two identity
+// products (log2(e) split into bf16 hi + lo) and the accumulators start at -log2(e)*LSE and -D,
 // so P = exp2(S') and dS = P * (dP - D) cost one exponential and one multiply.
 // The bias of the next key block is fetched one block ahead; masked keys get
 // the most negative bias (exp2 of it is 0) without a branch.
@@ -516,7 +517,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   const int bh_lin = L / nqblocks;
   const int h = bh_lin / a.B, b = bh_lin % a.B;
   const size_t bh = (size_t)b * a.H + h;
-  const u16* Qs = static_cast<const u16*>(a.qs) + bh * N * d;
+  const u16* Q = static_cast<const u16*>(a.q) + bh * N * d;
   const u16* K = static_cast<const u16*>(a.k) + bh * N * d;
   const u16* V = static_cast<const u16*>(a.v) + bh * N * d;
   const u16* dA = static_cast<const u16*>(a.da) + bh * N * d;
@@ -570,6 +571,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
 
   bf16x8 qf[QT][KC], daf[QT][KC];
   f32x4 nl4[QT], nd4[QT];  // -log2(e) LSE and -D of the lane's query, as accumulator seeds
+  const float qscale = a.scale * kLog2e;  // Q enters the products as Q log2(e) / sqrt(d)
 #pragma unroll
   for (int s = 0; s < QT; ++s) {
     const int qrow = q0 + 16 * s + ln;
@@ -578,9 +580,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
       const int c0 = 32 * kc + 8 * g;
       u32x4 rq = u32x4{0, 0, 0, 0}, rda = u32x4{0, 0, 0, 0};
       if (qrow < N && c0 < d) {
-        rq = ld16(Qs + (size_t)qrow * d + c0);
+        rq = ld16(Q + (size_t)qrow * d + c0);
         rda = ld16(dA + (size_t)qrow * d + c0);
       }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rq[e] = pack2(bf2f(lo16(rq[e])) * qscale, bf2f(hi16(rq[e])) * qscale);
       qf[s][kc] = as_bf8(rq);
       daf[s][kc] = as_bf8(rda);
     }
@@ -1035,8 +1039,6 @@ BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16) {
   size_t off = 0;
   pl.off_da = off;
   off = align256(off + rows * d * (bf16 ? 2 : 4));
-  pl.off_qs = off;
-  if (bf16) off = align256(off + rows * d * 2);
   pl.off_drow = off;  // fp32: D per row; bf16: (-log2(e) LSE, -D) pairs
   off = align256(off + rows * (bf16 ? 8 : 4));
   pl.off_partial = off;

@@ -78,7 +78,6 @@ int prep_backward(int B, int H, int N, int d, int dtype, const void* q, const vo
   a.out = out; a.lse = lse; a.dout = dout;
   a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbias = dbias;
   a.da = ws + pl.off_da;
-  a.qs = bf16 ? ws + pl.off_qs : nullptr;
   a.drow = bf16 ? nullptr : reinterpret_cast<float*>(ws + pl.off_drow);
   a.seed = bf16 ? reinterpret_cast<float2*>(ws + pl.off_drow) : nullptr;
   a.partial = reinterpret_cast<float*>(ws + pl.off_partial);

@@ -39,7 +39,6 @@ struct BwdArgs {
   void* dbias;
   // workspace views
   void* da;         // dA = dout * sigmoid(G), [B,H,N,d] (bf16 for bf16 inputs, fp32 otherwise)
-  void* qs;         // Q / sqrt(d) rounded to bf16, [B,H,N,d] (bf16 inputs only)
   float* drow;      // fp32 inputs: D = rowsum(dout * out), [B,H,N]
   float2* seed;     // bf16 inputs: per query row (-log2(e) * LSE, or -inf for a row
                     // without keys; -D), [B,H,N]: the accumulator seeds of S' and dP - D
@@ -73,7 +72,7 @@ struct PwaArgs {
 
 // Workspace plan of the attention backward (byte offsets into one buffer).
 struct BwdPlan {
-  size_t off_da, off_qs, off_drow, off_partial, total;
+  size_t off_da, off_drow, off_partial, total;
   int P, C, slab;
 };
 BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16);
