@@ -114,7 +114,9 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
 
   // X staging: chunk c = tid + 512 it -> token row c / 32, 16-byte column chunk c % 32
   // W staging: pair p = tid + 512 it -> row n, k step kh, chunk pair (m, m+2)
-  u32x4 rx[4], rw[4];
+  // X (streamed from HBM) is fetched two K chunks ahead through a ring of two
+  // register stages; W (a few MB, resident in L2) one chunk ahead.
+  u32x4 rx[2][4], rw[4];
   auto wchunk = [&](int n, int k) -> u32x4 {
     if constexpr (WAL) {  // N % 8 == 0: a chunk is either inside a row or past it
       return buf_load16(wrs, (n < N && k < N) ? (uint32_t)(((size_t)n * N + k) * 2) : kOob);
@@ -129,17 +131,20 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
     }
     return u32x4{w4[0], w4[1], w4[2], w4[3]};
   };
-  auto fetch = [&](int k0) {
+  // chunks past the last one read as zeros (every fetch is issued)
+  auto fetch_x = [&](u32x4 (&dst)[4], int k0) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int c = tid + 512 * it;
       const int row = c >> 5, cc = c & 31;
       const int sl = cc / C8, c8 = cc % C8;
       const int s = s0 + sl, k = k0 + row;
-      rx[it] = buf_load16(xrs, (s < S && k < N && 8 * c8 < d)
-                                   ? (uint32_t)((s * srow + (size_t)k * krow + (size_t)h * d + 8 * c8) * 2)
-                                   : kOob);
+      dst[it] = buf_load16(xrs, (s < S && k < N && 8 * c8 < d)
+                                    ? (uint32_t)((s * srow + (size_t)k * krow + (size_t)h * d + 8 * c8) * 2)
+                                    : kOob);
     }
+  };
+  auto fetch_w = [&](int k0) {
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
       const int pr = tid + 512 * it;
@@ -149,11 +154,11 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
       rw[2 * it + 1] = wchunk(n, k + 16);
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](const u32x4 (&src)[4], int buf) {
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int c = tid + 512 * it;
-      *reinterpret_cast<u32x4*>(&sx[buf][(c >> 5) * RSX + 8 * (c & 31)]) = rx[it];
+      *reinterpret_cast<u32x4*>(&sx[buf][(c >> 5) * RSX + 8 * (c & 31)]) = src[it];
     }
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
@@ -189,13 +194,18 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
   // the K chunks in the same order, so each X chunk is fetched once from HBM
   // and read by the others from L2 while it is still resident.
   const int nkc = (N + 63) / 64;
-  auto chunk_k0 = [&](int kcix) { return 64 * kcix; };
-  fetch(chunk_k0(0));
-  commit(0);
+  fetch_x(rx[0], 0);
+  fetch_w(0);
+  fetch_x(rx[1], 64);
+  commit(rx[0], 0);
   __syncthreads();
-  for (int kcix = 0; kcix < nkc; ++kcix) {
-    const int buf = kcix & 1;
-    if (kcix + 1 < nkc) fetch(chunk_k0(kcix + 1));
+  // step kcix (parity S): X of chunk kcix + 2 into register stage S, W of
+  // chunk kcix + 1; products of chunk kcix from LDS buffer S; then chunk
+  // kcix + 1 (X from stage S ^ 1) into LDS buffer S ^ 1
+  auto step = [&](auto S_c, int kcix) {
+    constexpr int buf = decltype(S_c)::value;
+    fetch_w(64 * (kcix + 1));
+    fetch_x(rx[buf], 64 * (kcix + 2));
 #pragma unroll
     for (int kh = 0; kh < 2; ++kh) {
       bf16x8 af[4], bfr[8];
@@ -209,8 +219,12 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) acc[ct][nt] = mfma32(af[ct], bfr[nt], acc[ct][nt]);
     }
-    if (kcix + 1 < nkc) commit(buf ^ 1);
+    commit(rx[buf ^ 1], buf ^ 1);
     __syncthreads();
+  };
+  for (int kcix = 0; kcix < nkc; kcix += 2) {
+    step(std::integral_constant<int, 0>{}, kcix);
+    if (kcix + 1 < nkc) step(std::integral_constant<int, 1>{}, kcix + 1);
   }
 
   // epilogue: lane (g, n) of tiles (2p, 2p + 1, nt) holds columns
