@@ -337,14 +337,16 @@ __global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA,
   // Chunk q of a stage is written to LDS slot q (lane-contiguous 16-byte
   // writes): slot (t, ks, ga, r) holds token 16t + r, MSA row ks / (DP/32)
   // of the stage, channels 8 (4 (ks mod DP/32) + ga) .. +7.  Loads are
-  // branch-free buffer loads; elements past the tensors read as zero.
+  // branch-free buffer loads; elements past the tensors (and stages past
+  // the chunk) read as zero.  Both operands stream from HBM, so they are
+  // fetched two stages ahead through a ring of two register stages.
   constexpr int NCHUNK = SPS * 256 * C8;    // chunks of 16 B per operand
   constexpr int PER = NCHUNK / 512;         // per thread
   constexpr uint32_t kOob = 0xFFFFFFF0u;
   const __amdgpu_buffer_rsrc_t ars = make_rsrc(dA, (uint32_t)((size_t)S * srow * 2));
   const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, (uint32_t)((size_t)S * srow * 2));
-  u32x4 ra[PER], rb[PER];
-  auto fetch = [&](int s_begin) {
+  u32x4 ra[2][PER], rb[2][PER];
+  auto fetch = [&](u32x4 (&da)[PER], u32x4 (&db)[PER], int s_begin) {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
       const int q = tid + 512 * it;
@@ -354,16 +356,16 @@ __global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA,
       const int ia = it0 + tok, jb = jt0 + tok;
       const bool cok = s < se && 8 * c8 < d;
       const size_t base = s * srow + (size_t)h * d + 8 * c8;
-      ra[it] = buf_load16(ars, (cok && ia < N) ? (uint32_t)((base + (size_t)ia * krow) * 2) : kOob);
-      rb[it] = buf_load16(vrs, (cok && jb < N) ? (uint32_t)((base + (size_t)jb * krow) * 2) : kOob);
+      da[it] = buf_load16(ars, (cok && ia < N) ? (uint32_t)((base + (size_t)ia * krow) * 2) : kOob);
+      db[it] = buf_load16(vrs, (cok && jb < N) ? (uint32_t)((base + (size_t)jb * krow) * 2) : kOob);
     }
   };
-  auto commit = [&](int buf) {
+  auto commit = [&](const u32x4 (&da)[PER], const u32x4 (&db)[PER], int buf) {
 #pragma unroll
     for (int it = 0; it < PER; ++it) {
       const int q = tid + 512 * it;
-      sm.a[buf][q] = ra[it];
-      sm.b[buf][q] = rb[it];
+      sm.a[buf][q] = da[it];
+      sm.b[buf][q] = db[it];
     }
   };
 
@@ -376,14 +378,15 @@ __global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA,
 
   const int nst = se > sb ? (se - sb + SPS - 1) / SPS : 0;
   auto stage_s = [&](int st) { return sb + SPS * st; };
-  if (nst > 0) {
-    fetch(stage_s(0));
-    commit(0);
-  }
+  fetch(ra[0], rb[0], stage_s(0));
+  fetch(ra[1], rb[1], stage_s(1));
+  commit(ra[0], rb[0], 0);
   __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nst) fetch(stage_s(st + 1));
+  // stage st (parity S): loads of stage st + 2 into register stage S,
+  // products of stage st from LDS buffer S, stage st + 1 into buffer S ^ 1
+  auto step = [&](auto S_c, int st) {
+    constexpr int buf = decltype(S_c)::value;
+    fetch(ra[buf], rb[buf], stage_s(st + 2));
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       bf16x8 af[4], bfr[8];
@@ -396,8 +399,12 @@ __global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA,
 #pragma unroll
         for (int b8 = 0; b8 < 8; ++b8) acc[a4][b8] = mfma32(af[a4], bfr[b8], acc[a4][b8]);
     }
-    if (st + 1 < nst) commit(buf ^ 1);
+    commit(ra[buf ^ 1], rb[buf ^ 1], buf ^ 1);
     __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 2) {
+    step(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nst) step(std::integral_constant<int, 1>{}, st + 1);
   }
 
   // lane (g, n) of tile (a4, b8) holds rows i = 4g..4g+3 of column j = n
