@@ -325,9 +325,10 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
 
 // ---------------------------------------------------------------- K/V-resident variant
 // For moderate N the whole K and V of one (b, h) fit in LDS: the workgroup
-// (8 waves, 128*QT queries) stages them once, synchronises once, and then
-// every wave walks all key blocks on its own -- no per-block staging, waits
-// or barriers.  Only the wave's bias fragments stream from memory,
+// (NW waves, 16*QT queries each) stages them once, synchronises once, and
+// then every wave walks all key blocks on its own -- no per-block staging,
+// waits or barriers.  With four waves two workgroups share a CU, so one's
+// staging overlaps the other's products.  Only the wave's bias fragments stream from memory,
 // prefetched one block ahead; its Q and gate rows are requested before the
 // staging barrier.
 //
@@ -342,14 +343,13 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
 // reference, rescale of the running sums, P recomputed -- the same lazy
 // rescaling the streaming kernel uses.  Rows whose reference is still -inf
 // (every key so far masked) also take the slow path.
-constexpr int kResThreads = 512;
-
-template <int DP, int QT, bool ALIGNED>
-__global__ void __launch_bounds__(kResThreads) attn_fwd_res_kernel(FwdArgs a) {
+template <int DP, int QT, bool ALIGNED, int NW>
+__global__ void __launch_bounds__(NW * 64) attn_fwd_res_kernel(FwdArgs a) {
+  constexpr int kResThreads = NW * 64;
   constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
-  constexpr int QW = 16 * QT, QBLK = 8 * QW;
+  constexpr int QW = 16 * QT, QBLK = NW * QW;
   constexpr int C8 = DP / 8;
-  constexpr int RIT = DP == 32 ? 4 : 8;  // staging chunks per thread (N up to 512)
+  constexpr int RIT = 512 * C8 / kResThreads;  // staging chunks per thread (N up to 512)
   constexpr uint32_t kOob = 0xFFFFFFF0u;
   constexpr float kGrowLimit = 16384.f;  // largest block row sum of P (64 keys x 2^8) kept without rescaling
   extern __shared__ __attribute__((aligned(16))) u16 res_lds[];
@@ -810,24 +810,27 @@ hipError_t launch_attn_fwd(const FwdArgs& args, bool bf16, hipStream_t stream) {
   const bool al = (a.N % 8) == 0;
   // K/V-resident kernel when K and V of one (b, h) fit (N <= 512) and the
   // grid still fills the chip
+  // (d <= 32: 4 waves x 48 queries; d <= 64: 8 waves x 32 queries)
   {
     const int qt = dp == 32 ? 3 : 2;
+    const int nw = dp == 32 ? 4 : 8;
     const int np = (a.N + 63) / 64 * 64;
-    const int nqb = (a.N + 128 * qt - 1) / (128 * qt);
+    const int qblk = nw * 16 * qt;
+    const int nqb = (a.N + qblk - 1) / qblk;
     const size_t lds = (size_t)2 * np * (dp + 8) * 2 + np;
     if (a.N <= 512 && bhs * nqb >= 512) {
       a.nqb = nqb;
       const dim3 grid((unsigned)(bhs * nqb));
-      const void* fn = dp == 32 ? (al ? reinterpret_cast<const void*>(&attn_fwd_res_kernel<32, 3, true>)
-                                      : reinterpret_cast<const void*>(&attn_fwd_res_kernel<32, 3, false>))
-                                : (al ? reinterpret_cast<const void*>(&attn_fwd_res_kernel<64, 2, true>)
-                                      : reinterpret_cast<const void*>(&attn_fwd_res_kernel<64, 2, false>));
+      const void* fn = dp == 32 ? (al ? reinterpret_cast<const void*>(&attn_fwd_res_kernel<32, 3, true, 4>)
+                                      : reinterpret_cast<const void*>(&attn_fwd_res_kernel<32, 3, false, 4>))
+                                : (al ? reinterpret_cast<const void*>(&attn_fwd_res_kernel<64, 2, true, 8>)
+                                      : reinterpret_cast<const void*>(&attn_fwd_res_kernel<64, 2, false, 8>));
       hipError_t e;
       if (lds > 64 * 1024 &&
           (e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) != hipSuccess)
         return e;
       void* kargs[] = {&a};
-      return hipLaunchKernel(fn, grid, dim3(kResThreads), kargs, lds, stream);
+      return hipLaunchKernel(fn, grid, dim3(nw * 64), kargs, lds, stream);
     }
   }
   // two query sub-tiles per wave when that still leaves enough workgroups
