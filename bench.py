@@ -50,7 +50,7 @@ def attn_kernel_flops(B, H, N, d):
 
 ATTN_BWD_KERNELS = ["bwd_pre", "bwd_dkdv", "bwd_dq", "bwd_dbias_reduce"]
 PWA_FWD_KERNELS = ["pwa_softmax", "pwa_weighted_sum"]
-PWA_BWD_KERNELS = ["pwa_bwd_softmax", "pwa_bwd_pre", "pwa_bwd_dv", "pwa_bwd_dw", "pwa_bwd_db"]
+PWA_BWD_KERNELS = ["pwa_bwd_softmax", "pwa_bwd_pre", "pwa_bwd_dv_dw", "pwa_bwd_db"]
 
 
 def pwa_bytes(S, N, H, d, elt=2):
@@ -138,8 +138,7 @@ KERNEL_SOURCES = {
     "bwd_dbias_reduce": ("bias_grad_reduce_kernel", "attn_bwd.hip"),
     "pwa_weighted_sum": ("pwa_gemm_kernel<32, true", "pwa.hip"),
     "pwa_bwd_pre": ("pwa_bwd_pre_kernel", "pwa.hip"),
-    "pwa_bwd_dv": ("pwa_gemm_kernel<32, false", "pwa.hip"),
-    "pwa_bwd_dw": ("pwa_dw_kernel", "pwa.hip"),
+    "pwa_bwd_dv_dw": ("pwa_gemm_kernel<32, false", "pwa.hip"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 

@@ -155,7 +155,8 @@ int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype,
  *                                      partials, dQ, dBias reduction
  *   pair_weighted_avg_timed:           weight softmax, weighted sum + gate
  *   pair_weighted_avg_backward_timed:  weight softmax (w and w^T), preprocess
- *                                      (dA, dG), dV product, dw partials, db
+ *                                      (dA, dG), dV product together with the
+ *                                      dw partials (one launch), db
  * kernel_ms or n_kernels NULL returns PBA_ERR_NULL; a runtime failure returns
  * PBA_ERR_HIP.
  */

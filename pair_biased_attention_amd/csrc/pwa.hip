@@ -65,10 +65,143 @@ __global__ void __launch_bounds__(256) pwa_softmax_kernel(PwaArgs a, u16* wt) {
   if (lane == 0 && a.lse_w) a.lse_w[row] = l > 0.f ? msafe + logf(l) : kNegInf;
 }
 
+// ------------------------------------------------------------------ dw split-K GEMM
+// dw_p[h][i][j] = sum_{s in chunk p} sum_c dA[s,i,h,c] V[s,j,h,c].  Both operands
+// keep their natural layout (channels contiguous = the MFMA k axis).
+// Workgroup tile 256 i x 256 j, eight waves of 64 i x 128 j; 64 k values
+// (64/DP MSA rows) staged per iteration.
+template <int DP>
+struct PwaDwSmem {
+  static constexpr int SPS = 64 / DP;        // MSA rows per stage (64 k values)
+  static constexpr int KS = 2;               // k steps of 32 per stage
+  // [buffer][operand]: dA fragments [it][ks][lane], then V fragments
+  // [jt][ks][lane]; one buffer spans 64 KB, so every read of a buffer is an
+  // immediate offset from one base address
+  u32x4 ab[2][2][16 * KS * 64];
+};
+
+// One workgroup's tile: wg is its index among the nwg dw workgroups, which
+// occupy the first grid slots (the dispatcher sends slot w to XCD w mod 8).
+template <int DP>
+__device__ __forceinline__ void pwa_dw_tile(int wg, int nwg, PwaDwSmem<DP>& sm, const u16* __restrict__ dA,
+                                            const u16* __restrict__ V, float* __restrict__ partial, int S, int N,
+                                            int H, int d, int P, int spc, int nt1) {
+  using Sm = PwaDwSmem<DP>;
+  constexpr int KS = Sm::KS, SPS = Sm::SPS;
+  constexpr int C8 = DP / 8;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int g = lane >> 4, ln = lane & 15;
+  const int wi = wave & 3, wj = wave >> 2;
+  const int L = xcd_remap(wg, nwg);
+  // logical order: the nt1 x nt1 tiles fastest, then the head, then the
+  // chunk: workgroups reading the same 128-byte lines (neighbouring heads of
+  // the same rows) are adjacent and share an XCD's L2
+  const int tile = L % (nt1 * nt1);
+  const int hp = L / (nt1 * nt1);
+  const int h = hp % H, p = hp / H;
+  const int it0 = (tile / nt1) * 256, jt0 = (tile % nt1) * 256;
+  const int sb = p * spc, se = min(S, sb + spc);
+  const size_t srow = (size_t)N * H * d;
+  const size_t krow = (size_t)H * d;
+
+  // per stage: SPS MSA rows x 256 tokens x C8 chunks, for each operand.
+  // Chunk q of a stage is written to LDS slot q (lane-contiguous 16-byte
+  // writes): slot (t, ks, ga, r) holds token 16t + r, MSA row ks / (DP/32)
+  // of the stage, channels 8 (4 (ks mod DP/32) + ga) .. +7.  Loads are
+  // branch-free buffer loads; elements past the tensors (and stages past
+  // the chunk) read as zero.  Both operands stream from HBM, so they are
+  // fetched two stages ahead through a ring of two register stages.
+  constexpr int NCHUNK = SPS * 256 * C8;    // chunks of 16 B per operand
+  constexpr int PER = NCHUNK / 512;         // per thread
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+  const __amdgpu_buffer_rsrc_t ars = make_rsrc(dA, (uint32_t)((size_t)S * srow * 2));
+  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, (uint32_t)((size_t)S * srow * 2));
+  u32x4 ra[2][PER], rb[2][PER];
+  auto fetch = [&](u32x4 (&da)[PER], u32x4 (&db)[PER], int s_begin) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int q = tid + 512 * it;
+      const int r = q & 15, ga = (q >> 4) & 3, ks = (q >> 6) % KS, t = (q >> 6) / KS;
+      const int sl = ks / (DP / 32), c8 = 4 * (ks % (DP / 32)) + ga;
+      const int s = s_begin + sl, tok = 16 * t + r;
+      const int ia = it0 + tok, jb = jt0 + tok;
+      const bool cok = s < se && 8 * c8 < d;
+      const size_t base = s * srow + (size_t)h * d + 8 * c8;
+      da[it] = buf_load16(ars, (cok && ia < N) ? (uint32_t)((base + (size_t)ia * krow) * 2) : kOob);
+      db[it] = buf_load16(vrs, (cok && jb < N) ? (uint32_t)((base + (size_t)jb * krow) * 2) : kOob);
+    }
+  };
+  auto commit = [&](const u32x4 (&da)[PER], const u32x4 (&db)[PER], int buf) {
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      const int q = tid + 512 * it;
+      sm.ab[buf][0][q] = da[it];
+      sm.ab[buf][1][q] = db[it];
+    }
+  };
+
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+    for (int b8 = 0; b8 < 8; ++b8) acc[a4][b8] = zero4;
+
+  const int nst = se > sb ? (se - sb + SPS - 1) / SPS : 0;
+  auto stage_s = [&](int st) { return sb + SPS * st; };
+  fetch(ra[0], rb[0], stage_s(0));
+  fetch(ra[1], rb[1], stage_s(1));
+  commit(ra[0], rb[0], 0);
+  __syncthreads();
+  // stage st (parity S): loads of stage st + 2 into register stage S,
+  // products of stage st from LDS buffer S, stage st + 1 into buffer S ^ 1
+  auto step = [&](auto S_c, int st) {
+    constexpr int buf = decltype(S_c)::value;
+    fetch(ra[buf], rb[buf], stage_s(st + 2));
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      bf16x8 af[4], bfr[8];
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4) af[a4] = as_bf8(sm.ab[buf][0][((4 * wi + a4) * KS + ks) * 64 + lane]);
+#pragma unroll
+      for (int b8 = 0; b8 < 8; ++b8) bfr[b8] = as_bf8(sm.ab[buf][1][((8 * wj + b8) * KS + ks) * 64 + lane]);
+#pragma unroll
+      for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+        for (int b8 = 0; b8 < 8; ++b8) acc[a4][b8] = mfma32(af[a4], bfr[b8], acc[a4][b8]);
+    }
+    commit(ra[buf ^ 1], rb[buf ^ 1], buf ^ 1);
+    __syncthreads();
+  };
+  for (int st = 0; st < nst; st += 2) {
+    step(std::integral_constant<int, 0>{}, st);
+    if (st + 1 < nst) step(std::integral_constant<int, 1>{}, st + 1);
+  }
+
+  // lane (g, n) of tile (a4, b8) holds rows i = 4g..4g+3 of column j = n
+  float* part = partial + ((size_t)p * H + h) * N * N;
+#pragma unroll
+  for (int a4 = 0; a4 < 4; ++a4)
+#pragma unroll
+    for (int b8 = 0; b8 < 8; ++b8) {
+      const int j = jt0 + 128 * wj + 16 * b8 + ln;
+      if (j >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = it0 + 64 * wi + 16 * a4 + 4 * g + r;
+        if (i < N) part[(size_t)i * N + j] = acc[a4][b8][r];
+      }
+    }
+}
+
 // ------------------------------------------------------------------ GEMM with transposed X
 // out^T[(s,c)][n] = sum_k X[s,k,h,c] * W[h,n,k]
 //   forward:  X = V,  W = w   (n = i, k = j), epilogue * sigmoid(G)
-//   dV:       X = dA, W = w^T (n = j, k = i), no epilogue
+//   dV:       X = dA, W = w^T (n = j, k = i), no epilogue; this launch also
+//             carries the dw partials (DW): they read the same dA and do not
+//             depend on dV, so the first ndw_slots workgroups (rounded up to
+//             a multiple of 8 so both parts keep their XCD mapping) run the
+//             long dw tiles and the dV tiles fill the CUs they leave free
 // Workgroup tile: 256 columns (s, c) x 256 rows n of one head, K in chunks
 // of 64 tokens; eight waves, each 64 columns x 128 rows (4 x 8 accumulator
 // tiles).  X is staged row-major ([token][(s,c)], 16-byte writes) and read
@@ -82,19 +215,43 @@ __global__ void __launch_bounds__(256) pwa_softmax_kernel(PwaArgs a, u16* wt) {
 // then head within the pair, then n tile.  Contiguous logical ranges run on
 // one XCD, so each XCD works on one pair at a time: both halves of every X
 // line are consumed from its L2, and the pair's two w planes stay resident.
-template <int DP, bool FWD, bool WAL>
+struct PwaDwArgs {
+  const u16* V;
+  float* partial;
+  int P, spc, nt1, ndw, ndw_slots;
+};
+
+template <int DP, bool FWD, bool WAL, bool DW>
 __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X, const u16* __restrict__ W,
                                                        const u16* __restrict__ G, u16* __restrict__ out,
-                                                       int S, int N, int H, int d, int ncolt, int nnt) {
+                                                       int S, int N, int H, int d, int ncolt, int nnt,
+                                                       PwaDwArgs dw) {
   constexpr int SPT = 256 / DP;  // MSA rows per column tile
   constexpr int C8 = DP / 8;     // 16-byte chunks per (s, token) row
   constexpr int RSX = 272;       // X tile row stride (elements): 136 dwords = 8 mod 64
-  __shared__ __attribute__((aligned(16))) u16 sx[2][64 * RSX];
-  __shared__ u32x4 sw[2][16 * 2 * 64];  // W operands [nt][kh][lane]
+  struct Smem {
+    u16 sx[2][64 * RSX];       // X tiles [token][(s, c)]
+    u32x4 sw[2][16 * 2 * 64];  // W operands [nt][kh][lane]
+  };
+  static_assert(sizeof(PwaDwSmem<DP>) <= sizeof(Smem), "dw tiles reuse the product's LDS");
+  __shared__ Smem sm;
+  int wg = blockIdx.x, nwg = gridDim.x;
+  if constexpr (DW) {
+    if (wg < dw.ndw_slots) {
+      if (wg < dw.ndw)
+        pwa_dw_tile<DP>(wg, dw.ndw, *reinterpret_cast<PwaDwSmem<DP>*>(&sm), X, dw.V, dw.partial, S, N, H, d, dw.P,
+                        dw.spc, dw.nt1);
+      return;
+    }
+    wg -= dw.ndw_slots;
+    nwg -= dw.ndw_slots;
+  }
+  auto& sx = sm.sx;
+  auto& sw = sm.sw;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int wc = wave & 3, wn = wave >> 2;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int L = xcd_remap(wg, nwg);
   const int nt_blk = L % nnt;
   const int hp = (L / nnt) & 1;
   const int colt = (L / (2 * nnt)) % ncolt;
@@ -297,132 +454,6 @@ __global__ void __launch_bounds__(256) pwa_bwd_pre_kernel(PwaArgs a) {
   *reinterpret_cast<u32x4*>(static_cast<u16*>(a.dg) + 8 * i8) = rg;
 }
 
-// ------------------------------------------------------------------ dw split-K GEMM
-// dw_p[h][i][j] = sum_{s in chunk p} sum_c dA[s,i,h,c] V[s,j,h,c].  Both operands
-// keep their natural layout (channels contiguous = the MFMA k axis).
-// Workgroup tile 256 i x 256 j, eight waves of 64 i x 128 j; 64 k values
-// (64/DP MSA rows) staged per iteration.
-template <int DP>
-struct PwaDwSmem {
-  static constexpr int SPS = 64 / DP;        // MSA rows per stage (64 k values)
-  static constexpr int KS = 2;               // k steps of 32 per stage
-  u32x4 a[2][16 * KS * 64];  // dA fragments [it][ks][lane]
-  u32x4 b[2][16 * KS * 64];  // V  fragments [jt][ks][lane]
-};
-
-template <int DP>
-__global__ void __launch_bounds__(512) pwa_dw_kernel(const u16* __restrict__ dA, const u16* __restrict__ V,
-                                                     float* __restrict__ partial, int S, int N, int H, int d,
-                                                     int P, int spc, int nt1) {
-  using Sm = PwaDwSmem<DP>;
-  constexpr int KS = Sm::KS, SPS = Sm::SPS;
-  constexpr int C8 = DP / 8;
-  __shared__ Sm sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
-  const int g = lane >> 4, ln = lane & 15;
-  const int wi = wave & 3, wj = wave >> 2;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
-  // logical order: the nt1 x nt1 tiles fastest, then the head, then the
-  // chunk: workgroups reading the same 128-byte lines (neighbouring heads of
-  // the same rows) are adjacent and share an XCD's L2
-  const int tile = L % (nt1 * nt1);
-  const int hp = L / (nt1 * nt1);
-  const int h = hp % H, p = hp / H;
-  const int it0 = (tile / nt1) * 256, jt0 = (tile % nt1) * 256;
-  const int sb = p * spc, se = min(S, sb + spc);
-  const size_t srow = (size_t)N * H * d;
-  const size_t krow = (size_t)H * d;
-
-  // per stage: SPS MSA rows x 256 tokens x C8 chunks, for each operand.
-  // Chunk q of a stage is written to LDS slot q (lane-contiguous 16-byte
-  // writes): slot (t, ks, ga, r) holds token 16t + r, MSA row ks / (DP/32)
-  // of the stage, channels 8 (4 (ks mod DP/32) + ga) .. +7.  Loads are
-  // branch-free buffer loads; elements past the tensors (and stages past
-  // the chunk) read as zero.  Both operands stream from HBM, so they are
-  // fetched two stages ahead through a ring of two register stages.
-  constexpr int NCHUNK = SPS * 256 * C8;    // chunks of 16 B per operand
-  constexpr int PER = NCHUNK / 512;         // per thread
-  constexpr uint32_t kOob = 0xFFFFFFF0u;
-  const __amdgpu_buffer_rsrc_t ars = make_rsrc(dA, (uint32_t)((size_t)S * srow * 2));
-  const __amdgpu_buffer_rsrc_t vrs = make_rsrc(V, (uint32_t)((size_t)S * srow * 2));
-  u32x4 ra[2][PER], rb[2][PER];
-  auto fetch = [&](u32x4 (&da)[PER], u32x4 (&db)[PER], int s_begin) {
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int q = tid + 512 * it;
-      const int r = q & 15, ga = (q >> 4) & 3, ks = (q >> 6) % KS, t = (q >> 6) / KS;
-      const int sl = ks / (DP / 32), c8 = 4 * (ks % (DP / 32)) + ga;
-      const int s = s_begin + sl, tok = 16 * t + r;
-      const int ia = it0 + tok, jb = jt0 + tok;
-      const bool cok = s < se && 8 * c8 < d;
-      const size_t base = s * srow + (size_t)h * d + 8 * c8;
-      da[it] = buf_load16(ars, (cok && ia < N) ? (uint32_t)((base + (size_t)ia * krow) * 2) : kOob);
-      db[it] = buf_load16(vrs, (cok && jb < N) ? (uint32_t)((base + (size_t)jb * krow) * 2) : kOob);
-    }
-  };
-  auto commit = [&](const u32x4 (&da)[PER], const u32x4 (&db)[PER], int buf) {
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int q = tid + 512 * it;
-      sm.a[buf][q] = da[it];
-      sm.b[buf][q] = db[it];
-    }
-  };
-
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc[4][8];
-#pragma unroll
-  for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-    for (int b8 = 0; b8 < 8; ++b8) acc[a4][b8] = zero4;
-
-  const int nst = se > sb ? (se - sb + SPS - 1) / SPS : 0;
-  auto stage_s = [&](int st) { return sb + SPS * st; };
-  fetch(ra[0], rb[0], stage_s(0));
-  fetch(ra[1], rb[1], stage_s(1));
-  commit(ra[0], rb[0], 0);
-  __syncthreads();
-  // stage st (parity S): loads of stage st + 2 into register stage S,
-  // products of stage st from LDS buffer S, stage st + 1 into buffer S ^ 1
-  auto step = [&](auto S_c, int st) {
-    constexpr int buf = decltype(S_c)::value;
-    fetch(ra[buf], rb[buf], stage_s(st + 2));
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      bf16x8 af[4], bfr[8];
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4) af[a4] = as_bf8(sm.a[buf][((4 * wi + a4) * KS + ks) * 64 + lane]);
-#pragma unroll
-      for (int b8 = 0; b8 < 8; ++b8) bfr[b8] = as_bf8(sm.b[buf][((8 * wj + b8) * KS + ks) * 64 + lane]);
-#pragma unroll
-      for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-        for (int b8 = 0; b8 < 8; ++b8) acc[a4][b8] = mfma32(af[a4], bfr[b8], acc[a4][b8]);
-    }
-    commit(ra[buf ^ 1], rb[buf ^ 1], buf ^ 1);
-    __syncthreads();
-  };
-  for (int st = 0; st < nst; st += 2) {
-    step(std::integral_constant<int, 0>{}, st);
-    if (st + 1 < nst) step(std::integral_constant<int, 1>{}, st + 1);
-  }
-
-  // lane (g, n) of tile (a4, b8) holds rows i = 4g..4g+3 of column j = n
-  float* part = partial + ((size_t)p * H + h) * N * N;
-#pragma unroll
-  for (int a4 = 0; a4 < 4; ++a4)
-#pragma unroll
-    for (int b8 = 0; b8 < 8; ++b8) {
-      const int j = jt0 + 128 * wj + 16 * b8 + ln;
-      if (j >= N) continue;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = it0 + 64 * wi + 16 * a4 + 4 * g + r;
-        if (i < N) part[(size_t)i * N + j] = acc[a4][b8][r];
-      }
-    }
-}
-
 // ------------------------------------------------------------------ db
 // One wave per (h, i) row: dw = sum_p partial (index order); w recomputed in
 // fp32 from b and lse_w; db = w * (dw - sum_j w dw).
@@ -490,9 +521,9 @@ static hipError_t launch_gemm(const u16* X, const u16* W, const u16* G, u16* out
   const int pairs = (a.H + 1) / 2;
   const dim3 grid((unsigned)((long long)ncolt * nnt * 2 * pairs));
   const bool wal = (a.N & 7) == 0;
-#define PBA_GEMM_LAUNCH(DPV, WALV) \
-  hipLaunchKernelGGL((pwa_gemm_kernel<DPV, FWD, WALV>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, a.H, \
-                     a.d, ncolt, nnt)
+#define PBA_GEMM_LAUNCH(DPV, WALV)                                                                              \
+  hipLaunchKernelGGL((pwa_gemm_kernel<DPV, FWD, WALV, false>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, \
+                     a.H, a.d, ncolt, nnt, PwaDwArgs{})
   if (dp == 32) {
     if (wal) PBA_GEMM_LAUNCH(32, true); else PBA_GEMM_LAUNCH(32, false);
   } else {
@@ -531,21 +562,36 @@ hipError_t launch_pwa_bwd(const PwaArgs& args, bool /*bf16*/, hipStream_t stream
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
-  e = launch_gemm<false>(static_cast<const u16*>(a.da), wt, nullptr, static_cast<u16*>(a.dv), a, stream);
-  if (e != hipSuccess) return e;
-  timer_mark(timer, stream);
   {
+    // dV = w^T dA and the dw partials in one grid (dw tiles first)
     const int dp = a.d <= 32 ? 32 : 64;
-    const int nt1 = (a.N + 255) / 256;
-    const int spc = ((a.S + a.P - 1) / a.P + 1) & ~1;  // even number of MSA rows per chunk
+    const int spt = 256 / dp;
+    const int ncolt = (a.S + spt - 1) / spt;
+    const int nnt = (a.N + 255) / 256;
+    const int pairs = (a.H + 1) / 2;
+    const long long ngemm = (long long)ncolt * nnt * 2 * pairs;
+    PwaDwArgs dw{};
+    dw.V = static_cast<const u16*>(a.v);
+    dw.partial = a.partial;
+    dw.P = a.P;
+    dw.nt1 = (a.N + 255) / 256;
+    dw.spc = ((a.S + a.P - 1) / a.P + 1) & ~1;  // even number of MSA rows per chunk
     // chunks past the end write zero partials, so every one of the P slots is defined
-    const dim3 grid((unsigned)((long long)nt1 * nt1 * a.H * a.P));
-    if (dp == 32)
-      hipLaunchKernelGGL(pwa_dw_kernel<32>, grid, dim3(512), 0, stream, static_cast<const u16*>(a.da),
-                         static_cast<const u16*>(a.v), a.partial, a.S, a.N, a.H, a.d, a.P, spc, nt1);
-    else
-      hipLaunchKernelGGL(pwa_dw_kernel<64>, grid, dim3(512), 0, stream, static_cast<const u16*>(a.da),
-                         static_cast<const u16*>(a.v), a.partial, a.S, a.N, a.H, a.d, a.P, spc, nt1);
+    dw.ndw = dw.nt1 * dw.nt1 * a.H * a.P;
+    dw.ndw_slots = (dw.ndw + 7) & ~7;
+    const dim3 grid((unsigned)(dw.ndw_slots + ngemm));
+    const bool wal = (a.N & 7) == 0;
+    const u16* dA = static_cast<const u16*>(a.da);
+    u16* dV = static_cast<u16*>(a.dv);
+#define PBA_PROD_LAUNCH(DPV, WALV)                                                                           \
+  hipLaunchKernelGGL((pwa_gemm_kernel<DPV, false, WALV, true>), grid, dim3(512), 0, stream, dA, wt, nullptr, dV, \
+                     a.S, a.N, a.H, a.d, ncolt, nnt, dw)
+    if (dp == 32) {
+      if (wal) PBA_PROD_LAUNCH(32, true); else PBA_PROD_LAUNCH(32, false);
+    } else {
+      if (wal) PBA_PROD_LAUNCH(64, true); else PBA_PROD_LAUNCH(64, false);
+    }
+#undef PBA_PROD_LAUNCH
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
