@@ -40,15 +40,15 @@ def attn_fwd_flops(B, H, N, d):
 
 
 # Algorithmic work credited to each kernel of the attention path (flops), per
-# launch.  The backward's 10*B*H*N^2*d is split by where each product is
-# formed: the dK/dV kernel recomputes S and forms dP, dV and dK (8); the dQ
-# kernel forms dQ (2; its own recomputation of S and dP is not credited).
+# launch.  The backward's 10*B*H*N^2*d runs in one launch that carries the
+# dK/dV tiles (S recomputed; dP, dV and dK formed) and the dQ tiles (dQ; their
+# own recomputation of S and dP is not credited).
 def attn_kernel_flops(B, H, N, d):
     u = float(B) * H * N * N * d
-    return {"attn_fwd": 4 * u, "bwd_pre": 0.0, "bwd_dkdv": 8 * u, "bwd_dq": 2 * u, "bwd_dbias_reduce": 0.0}
+    return {"attn_fwd": 4 * u, "bwd_pre": 0.0, "bwd_dkdv_dq": 10 * u, "bwd_dbias_reduce": 0.0}
 
 
-ATTN_BWD_KERNELS = ["bwd_pre", "bwd_dkdv", "bwd_dq", "bwd_dbias_reduce"]
+ATTN_BWD_KERNELS = ["bwd_pre", "bwd_dkdv_dq", "bwd_dbias_reduce"]
 PWA_FWD_KERNELS = ["pwa_softmax", "pwa_weighted_sum"]
 PWA_BWD_KERNELS = ["pwa_bwd_softmax", "pwa_bwd_pre", "pwa_bwd_dv_dw", "pwa_bwd_db"]
 
@@ -133,8 +133,7 @@ CALIBRATION_KERNEL = "neg"  # torch's elementwise negation: one dispatch, reads 
 KERNEL_SOURCES = {
     "attn_fwd": ("attn_fwd_res_kernel", "attn_fwd.hip"),
     "bwd_pre": ("attn_bwd_pre_bf16_kernel", "attn_bwd.hip"),
-    "bwd_dkdv": ("attn_bwd_dkdv_bf16_kernel", "attn_bwd.hip"),
-    "bwd_dq": ("attn_bwd_dq_bf16_kernel", "attn_bwd.hip"),
+    "bwd_dkdv_dq": ("attn_bwd_dq_bf16_kernel", "attn_bwd.hip"),
     "bwd_dbias_reduce": ("bias_grad_reduce_kernel", "attn_bwd.hip"),
     "pwa_weighted_sum": ("pwa_gemm_kernel<32, true", "pwa.hip"),
     "pwa_bwd_pre": ("pwa_bwd_pre_kernel", "pwa.hip"),

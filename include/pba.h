@@ -151,8 +151,10 @@ int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype,
  * and the number of kernels to *n_kernels.  Unlike every other entry point
  * they create and destroy HIP events and synchronise; they are meant for
  * benchmarks and profiles, not for production loops.  Kernel order:
- *   pba_backward_timed:                preprocess (dA, dG, D), dK/dV + dBias
- *                                      partials, dQ, dBias reduction
+ *   pba_backward_timed:                preprocess (dA, dG, row seeds), dK/dV +
+ *                                      dBias partials together with dQ (one
+ *                                      launch; two launches for PBA_F32),
+ *                                      dBias reduction
  *   pair_weighted_avg_timed:           weight softmax, weighted sum + gate
  *   pair_weighted_avg_backward_timed:  weight softmax (w and w^T), preprocess
  *                                      (dA, dG), dV product together with the

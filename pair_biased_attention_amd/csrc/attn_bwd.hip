@@ -171,19 +171,29 @@ struct DkdvStage {
   float2 seed;                    // (-log2(e) LSE, -D) of query `lane` of the block (wave 0)
 };
 
-template <int DP, bool ALIGNED, bool SLAB>
-__global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
-  constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
-  constexpr int NCH = DP / 32;
-  constexpr int kTile = 64 * RS;
-  constexpr int kCombF4 = 2 * 2 * CT * 64;
-  __shared__ __attribute__((aligned(16))) u16 sQA[2][2 * kTile];  // [buffer][Q tile | dA tile]
-  __shared__ __attribute__((aligned(16))) float sLD[2][2][64];    // [buffer][-log2(e) LSE | -D]
+template <int DP>
+struct DkdvSmem {
+  static constexpr int kTile = 64 * (DP + 8);
+  u16 sQA[2][2 * kTile];  // [buffer][Q tile | dA tile]
+  float sLD[2][2][64];    // [buffer][-log2(e) LSE | -D]
   // query-half combine area of dK, dV at the end of a row; written again
   // only nqb >= 1 iterations (and barriers) later, so one barrier suffices
-  __shared__ f32x4 comb[kCombF4];
-  extern __shared__ f32x4 slab_lds[];
-  f32x4* const slab = slab_lds;  // [nqb][4 query tiles][2 key tiles][64 lanes] when SLAB
+  f32x4 comb[2 * 2 * (DP / 16) * 64];
+};
+
+// One workgroup's tile: wg is its index among the nwg dK/dV workgroups, which
+// take the first slots of the backward grid (the dispatcher sends slot w to
+// XCD w mod 8); slab is the dynamic LDS [nqb][4 query tiles][2 key tiles]
+// [64 lanes] when SLAB.
+template <int DP, bool ALIGNED, bool SLAB>
+__device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm, f32x4* const slab,
+                                               const BwdArgs& a) {
+  constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
+  constexpr int NCH = DP / 32;
+  constexpr int kTile = DkdvSmem<DP>::kTile;
+  auto& sQA = sm.sQA;
+  auto& sLD = sm.sLD;
+  auto& comb = sm.comb;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, n = lane & 15;
@@ -191,7 +201,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
   const int N = a.N, d = a.d, H = a.H;
   const int nkb = (N + 31) / 32;
   const int nqb = (N + 63) / 64;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int L = xcd_remap(wg, nwg);
   const int kblk = L % nkb;
   const int hp = L / nkb;
   const int p = hp % a.P, h = hp / a.P;
@@ -498,21 +508,45 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_bf16_kernel(BwdArgs a) {
 // so P = exp2(S') and dS = P * (dP - D) cost one exponential and one multiply.
 // The bias of the next key block is fetched one block ahead; masked keys get
 // the most negative bias (exp2 of it is 0) without a branch.
-template <int DP, int QT, bool ALIGNED>
-__global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nqblocks) {
+//
+// This launch also carries the dK/dV workgroups (SLAB: their dBias slab
+// variant): they need the same preprocessed inputs and not dQ, so the first
+// ndk_slots workgroups (ndk rounded up to a multiple of 8, so both parts keep
+// their XCD mapping) run the long dK/dV tiles and the dQ tiles fill the
+// slots they leave free, then the chip.  The two roles share the static LDS;
+// the dynamic LDS is the dK/dV slab or the dQ keep bytes.
+template <int DP, int QT, bool ALIGNED, bool SLAB>
+__global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nqblocks, int ndk, int ndk_slots) {
   constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
   constexpr int QW = 16 * QT, QBLK = 4 * QW;
   constexpr int NCH = DP / 32;
-  __shared__ __attribute__((aligned(16))) u16 sK[2][64 * RS];
-  __shared__ __attribute__((aligned(16))) u16 sV[2][64 * RS];
-  // keep bytes of every key (dynamic, 64 per key block): filled once, so the
-  // key loop issues no mask loads
-  extern __shared__ uint32_t keep_lds[];
+  struct DqSmem {
+    u16 sK[2][64 * RS];
+    u16 sV[2][64 * RS];
+  };
+  union Smem {
+    DqSmem dq;
+    DkdvSmem<DP> dk;
+  };
+  __shared__ Smem sm;
+  extern __shared__ f32x4 bwd_dyn_lds[];
+  int wg = blockIdx.x, nwg = gridDim.x;
+  if (wg < ndk_slots) {
+    if (wg < ndk) attn_dkdv_tile<DP, ALIGNED, SLAB>(wg, ndk, sm.dk, bwd_dyn_lds, a);
+    return;
+  }
+  wg -= ndk_slots;
+  nwg -= ndk_slots;
+  auto& sK = sm.dq.sK;
+  auto& sV = sm.dq.sV;
+  // keep bytes of every key (64 per key block): filled once, so the key
+  // loop issues no mask loads
+  uint32_t* const keep_lds = reinterpret_cast<uint32_t*>(bwd_dyn_lds);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int N = a.N, d = a.d;
-  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int L = xcd_remap(wg, nwg);
   const int qb = L % nqblocks;
   const int bh_lin = L / nqblocks;
   const int h = bh_lin / a.B, b = bh_lin % a.B;
@@ -992,13 +1026,14 @@ static size_t slab_bytes(int N, bool bf16) {
 }
 constexpr size_t kMaxSlabBytes = 112 * 1024;
 
-// Resident dK/dV workgroups per CU (160 KiB of LDS; at most 3 by registers).
+// Resident dK/dV workgroups per CU (160 KiB of LDS; at most 2 by registers in
+// the bf16 launch that also carries dQ, 3 for fp32).
 static int dkdv_wgs_per_cu(int N, int d, bool bf16, bool slab) {
   const size_t dp = d <= 32 ? 32 : 64;
   size_t lds = bf16 ? 2 * 2 * 64 * (dp + 8) * 2 + 1024 + 2 * 2 * (dp / 16) * 64 * 16
                     : 2 * 64 * (dp + 1) * 4 + 512 + 2 * 2 * (dp / 16) * 64 * 16;
   if (slab) lds += slab_bytes(N, bf16);
-  return (int)std::max<size_t>(1, std::min<size_t>(3, 160 * 1024 / lds));
+  return (int)std::max<size_t>(1, std::min<size_t>(bf16 ? 2 : 3, 160 * 1024 / lds));
 }
 
 // Batch rows per chunk.  Cost model in microseconds: the dK/dV launch runs in
@@ -1068,59 +1103,59 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
-  // 2. dK, dV, dBias partials
-  {
-    const int nkb = (a.N + 31) / 32;
-    const dim3 grid((unsigned)((long long)a.H * a.P * nkb));
-    const size_t shmem = a.slab ? slab_bytes(a.N, bf16) : 0;
+  // 2-3. dK, dV, dBias partials and dQ
+  const int nkb = (a.N + 31) / 32;
+  const int ndk = a.H * a.P * nkb;
+  const size_t slab_shmem = a.slab ? slab_bytes(a.N, bf16) : 0;
+  if (bf16) {
+    // one launch: the dK/dV tiles first, then the dQ tiles
+    const int ndk_slots = (ndk + 7) & ~7;
+    const bool qt2 = dp == 32 && bhs * ((a.N + 127) / 128) >= 1024;
     const bool al = (a.N % 8) == 0;
+    const int nqb = qt2 ? (a.N + 127) / 128 : (a.N + 63) / 64;
+    const dim3 grid((unsigned)(ndk_slots + bhs * nqb));
+    const size_t keep_bytes = (size_t)((a.N + 63) / 64) * 64;
+    const size_t shmem = std::max(slab_shmem, keep_bytes);
     const void* fn;
-    if (bf16) {
-#define PBA_DKDV_FN(DPV, ALV, SLV) reinterpret_cast<const void*>(&attn_bwd_dkdv_bf16_kernel<DPV, ALV, SLV>)
-      if (a.slab) {
-        if (dp == 32) fn = al ? PBA_DKDV_FN(32, true, true) : PBA_DKDV_FN(32, false, true);
-        else fn = al ? PBA_DKDV_FN(64, true, true) : PBA_DKDV_FN(64, false, true);
-      } else {
-        if (dp == 32) fn = al ? PBA_DKDV_FN(32, true, false) : PBA_DKDV_FN(32, false, false);
-        else fn = al ? PBA_DKDV_FN(64, true, false) : PBA_DKDV_FN(64, false, false);
-      }
-#undef PBA_DKDV_FN
+#define PBA_BWD_FN(DPV, QTV, ALV, SLV) reinterpret_cast<const void*>(&attn_bwd_dq_bf16_kernel<DPV, QTV, ALV, SLV>)
+#define PBA_BWD_PICK(SLV)                                                                    \
+  if (dp == 32) {                                                                            \
+    if (qt2) fn = al ? PBA_BWD_FN(32, 2, true, SLV) : PBA_BWD_FN(32, 2, false, SLV);         \
+    else fn = al ? PBA_BWD_FN(32, 1, true, SLV) : PBA_BWD_FN(32, 1, false, SLV);             \
+  } else {                                                                                   \
+    if (qt2) fn = al ? PBA_BWD_FN(64, 2, true, SLV) : PBA_BWD_FN(64, 2, false, SLV);         \
+    else fn = al ? PBA_BWD_FN(64, 1, true, SLV) : PBA_BWD_FN(64, 1, false, SLV);             \
+  }
+    if (a.slab) {
+      PBA_BWD_PICK(true)
     } else {
-      fn = dp == 32 ? reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<32>)
-                    : reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<64>);
+      PBA_BWD_PICK(false)
     }
+#undef PBA_BWD_PICK
+#undef PBA_BWD_FN
     // the slab can exceed the default 64 KiB dynamic LDS limit
     if (shmem > 64 * 1024 &&
         (e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem)) != hipSuccess)
       return e;
-    void* kargs[] = {&a};
+    int nqb_arg = nqb, ndk_arg = ndk, slots_arg = ndk_slots;
+    void* kargs[] = {&a, &nqb_arg, &ndk_arg, &slots_arg};
     if ((e = hipLaunchKernel(fn, grid, dim3(256), kargs, shmem, stream)) != hipSuccess) return e;
     timer_mark(timer, stream);
-  }
-  // 3. dQ
-  {
-    if (bf16) {
-      const bool qt2 = dp == 32 && bhs * ((a.N + 127) / 128) >= 1024;
-      const bool al = (a.N % 8) == 0;
-      const int nqb = qt2 ? (a.N + 127) / 128 : (a.N + 63) / 64;
-      const dim3 grid((unsigned)(bhs * nqb));
-      const size_t keep_bytes = (size_t)((a.N + 63) / 64) * 64;
-#define PBA_DQ_LAUNCH(DPV, QTV, ALV) \
-  hipLaunchKernelGGL((attn_bwd_dq_bf16_kernel<DPV, QTV, ALV>), grid, dim3(256), keep_bytes, stream, a, nqb)
-      if (dp == 32) {
-        if (qt2) { if (al) PBA_DQ_LAUNCH(32, 2, true); else PBA_DQ_LAUNCH(32, 2, false); }
-        else { if (al) PBA_DQ_LAUNCH(32, 1, true); else PBA_DQ_LAUNCH(32, 1, false); }
-      } else {
-        if (qt2) { if (al) PBA_DQ_LAUNCH(64, 2, true); else PBA_DQ_LAUNCH(64, 2, false); }
-        else { if (al) PBA_DQ_LAUNCH(64, 1, true); else PBA_DQ_LAUNCH(64, 1, false); }
-      }
-#undef PBA_DQ_LAUNCH
-    } else {
-      const int nqb = (a.N + 63) / 64;
-      const dim3 grid((unsigned)(bhs * nqb));
-      if (dp == 32) hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<32>, grid, dim3(256), 0, stream, a, nqb);
-      else hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<64>, grid, dim3(256), 0, stream, a, nqb);
+  } else {
+    {
+      const void* fn = dp == 32 ? reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<32>)
+                                : reinterpret_cast<const void*>(&attn_bwd_dkdv_f32_kernel<64>);
+      if (slab_shmem > 64 * 1024 &&
+          (e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)slab_shmem)) != hipSuccess)
+        return e;
+      void* kargs[] = {&a};
+      if ((e = hipLaunchKernel(fn, dim3((unsigned)ndk), dim3(256), kargs, slab_shmem, stream)) != hipSuccess) return e;
+      timer_mark(timer, stream);
     }
+    const int nqb = (a.N + 63) / 64;
+    const dim3 grid((unsigned)(bhs * nqb));
+    if (dp == 32) hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<32>, grid, dim3(256), 0, stream, a, nqb);
+    else hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<64>, grid, dim3(256), 0, stream, a, nqb);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
