@@ -65,6 +65,103 @@ __global__ void __launch_bounds__(256) pwa_softmax_kernel(PwaArgs a, u16* wt) {
   if (lane == 0 && a.lse_w) a.lse_w[row] = l > 0.f ? msafe + logf(l) : kNegInf;
 }
 
+// Vectorised variants for N % 8 == 0 and N <= 512 CPL (key mask, if any,
+// 8-byte aligned): one wave per (h, i) row as above, but lane chunk
+// c = lane + 64 m covers 8 consecutive keys with 16-byte accesses and the
+// row stays in registers, so b (and, in the db kernel, the partials) are
+// read once.
+__device__ __forceinline__ uint32_t keep_bits8(const uint8_t* mask, int c) {
+  if (mask == nullptr) return 0xFFu;
+  const uint2 m = *reinterpret_cast<const uint2*>(mask + 8 * c);
+  uint32_t bits = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    bits |= (((m.x >> (8 * e)) & 0xFFu) != 0u ? 1u : 0u) << e;
+    bits |= (((m.y >> (8 * e)) & 0xFFu) != 0u ? 1u : 0u) << (4 + e);
+  }
+  return bits;
+}
+
+template <int CPL>
+__global__ void __launch_bounds__(256) pwa_softmax_vec_kernel(PwaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int N = a.N, nch = N / 8;
+  if (row >= (long long)a.H * N) return;
+  const u16* brow = static_cast<const u16*>(a.b) + row * N;
+  float x[CPL][8];
+  float mx = kNegInf;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int c = lane + 64 * m;
+    const bool ok = c < nch;
+    const u32x4 raw = ok ? ld16(brow + 8 * c) : u32x4{0, 0, 0, 0};
+    const uint32_t keep = ok ? keep_bits8(a.mask, c) : 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t hw = (e & 1) ? (raw[e >> 1] >> 16) : (raw[e >> 1] & 0xFFFFu);
+      x[m][e] = ((keep >> e) & 1u) ? bf2f((u16)hw) : kNegInf;
+      mx = fmaxf(mx, x[m][e]);
+    }
+  }
+  for (int o = 32; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  const float msafe = (mx == kNegInf) ? 0.f : mx;
+  float l = 0.f;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[m][e] = expf(x[m][e] - msafe);  // masked and absent keys: exp(-inf) = 0
+      l += x[m][e];
+    }
+  for (int o = 32; o >= 1; o >>= 1) l += __shfl_xor(l, o);
+  const float inv = l > 0.f ? 1.0f / l : 0.f;
+  u16* wrow = static_cast<u16*>(a.w) + row * N;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int c = lane + 64 * m;
+    if (c < nch)
+      *reinterpret_cast<u32x4*>(wrow + 8 * c) =
+          u32x4{pack2(x[m][0] * inv, x[m][1] * inv), pack2(x[m][2] * inv, x[m][3] * inv),
+                pack2(x[m][4] * inv, x[m][5] * inv), pack2(x[m][6] * inv, x[m][7] * inv)};
+  }
+  if (lane == 0 && a.lse_w) a.lse_w[row] = l > 0.f ? msafe + logf(l) : kNegInf;
+}
+
+// w^T of every head through 64 x 64 LDS tiles (N % 8 == 0): coalesced
+// 16-byte reads of w rows and 16-byte writes of w^T rows.
+__global__ void __launch_bounds__(256) pwa_transpose_kernel(const u16* __restrict__ w, u16* __restrict__ wt, int N) {
+  __shared__ u16 tile[64][72];
+  const int nt = (N + 63) / 64;
+  const int t = blockIdx.x;
+  const int h = t / (nt * nt), ti = (t / nt) % nt, tj = t % nt;
+  const u16* src = w + (size_t)h * N * N;
+  u16* dst = wt + (size_t)h * N * N;
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = tid + 256 * it;
+    const int r = q >> 3, c8 = q & 7;  // row r of the tile, 8 columns from 8 c8
+    const int i = ti * 64 + r, j = tj * 64 + 8 * c8;
+    const u32x4 v = (i < N && j < N) ? ld16(src + (size_t)i * N + j) : u32x4{0, 0, 0, 0};
+    *reinterpret_cast<u32x4*>(&tile[r][8 * c8]) = v;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = tid + 256 * it;
+    const int r = q >> 3, c8 = q & 7;  // row r of w^T's tile (column r of w's), 8 entries from 8 c8
+    const int j = tj * 64 + r, i = ti * 64 + 8 * c8;
+    if (j < N && i < N) {
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        o[e] = (uint32_t)tile[8 * c8 + 2 * e][r] | ((uint32_t)tile[8 * c8 + 2 * e + 1][r] << 16);
+      *reinterpret_cast<u32x4*>(dst + (size_t)j * N + i) = u32x4{o[0], o[1], o[2], o[3]};
+    }
+  }
+}
+
 // ------------------------------------------------------------------ dw split-K GEMM
 // dw_p[h][i][j] = sum_{s in chunk p} sum_c dA[s,i,h,c] V[s,j,h,c].  Both operands
 // keep their natural layout (channels contiguous = the MFMA k axis).
@@ -484,6 +581,57 @@ __global__ void __launch_bounds__(256) pwa_db_kernel(PwaArgs a) {
   }
 }
 
+template <int CPL>
+__global__ void __launch_bounds__(256) pwa_db_vec_kernel(PwaArgs a) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int N = a.N, nch = N / 8;
+  if (row >= (long long)a.H * N) return;
+  const u16* brow = static_cast<const u16*>(a.b) + row * N;
+  const float lse = a.lse_w_in[row];
+  const size_t plane = (size_t)a.H * N * N;
+  float w[CPL][8], dw[CPL][8];
+  float t = 0.f;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int c = lane + 64 * m;
+    const bool ok = c < nch;
+    const u32x4 raw = ok ? ld16(brow + 8 * c) : u32x4{0, 0, 0, 0};
+    const uint32_t keep = (ok && lse != kNegInf) ? keep_bits8(a.mask, c) : 0u;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t hw = (e & 1) ? (raw[e >> 1] >> 16) : (raw[e >> 1] & 0xFFFFu);
+      w[m][e] = ((keep >> e) & 1u) ? expf(bf2f((u16)hw) - lse) : 0.f;
+      dw[m][e] = 0.f;
+    }
+    if (ok) {
+      for (int p = 0; p < a.P; ++p) {
+        const float* src = a.partial + p * plane + row * N + 8 * c;
+        const f32x4 lo = *reinterpret_cast<const f32x4*>(src), hi = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          dw[m][e] += lo[e];
+          dw[m][4 + e] += hi[e];
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t = fmaf(w[m][e], dw[m][e], t);
+  }
+  for (int o = 32; o >= 1; o >>= 1) t += __shfl_xor(t, o);
+  u16* db = static_cast<u16*>(a.db) + row * N;
+#pragma unroll
+  for (int m = 0; m < CPL; ++m) {
+    const int c = lane + 64 * m;
+    if (c >= nch) continue;
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = w[m][e] * (dw[m][e] - t);
+    *reinterpret_cast<u32x4*>(db + 8 * c) =
+        u32x4{pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+  }
+}
+
 // ------------------------------------------------------------------ plan + launch
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -505,9 +653,26 @@ PwaPlan plan_pwa_bwd(int S, int N, int H, int d, bool /*bf16*/) {
   return pl;
 }
 
+// The vectorised row kernels need N % 8 == 0, N <= 1024 and an 8-byte
+// aligned key mask; other shapes take the element-wise kernels.
+static bool pwa_rows_vec(const PwaArgs& a) {
+  return a.N % 8 == 0 && a.N <= 1024 && (reinterpret_cast<uintptr_t>(a.mask) & 7) == 0;
+}
+
 static hipError_t launch_softmax(const PwaArgs& a, u16* wt, hipStream_t stream) {
   const long long rows = (long long)a.H * a.N;
-  hipLaunchKernelGGL(pwa_softmax_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a, wt);
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  if (!pwa_rows_vec(a)) {
+    hipLaunchKernelGGL(pwa_softmax_kernel, grid, dim3(256), 0, stream, a, wt);
+    return hipGetLastError();
+  }
+  if (a.N <= 512) hipLaunchKernelGGL(pwa_softmax_vec_kernel<1>, grid, dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(pwa_softmax_vec_kernel<2>, grid, dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || wt == nullptr) return e;
+  const int nt = (a.N + 63) / 64;
+  hipLaunchKernelGGL(pwa_transpose_kernel, dim3((unsigned)(a.H * nt * nt)), dim3(256), 0, stream,
+                     static_cast<const u16*>(a.w), wt, a.N);
   return hipGetLastError();
 }
 
@@ -597,7 +762,10 @@ hipError_t launch_pwa_bwd(const PwaArgs& args, bool /*bf16*/, hipStream_t stream
   }
   {
     const long long rows = (long long)a.H * a.N;
-    hipLaunchKernelGGL(pwa_db_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
+    const dim3 grid((unsigned)((rows + 3) / 4));
+    if (!pwa_rows_vec(a)) hipLaunchKernelGGL(pwa_db_kernel, grid, dim3(256), 0, stream, a);
+    else if (a.N <= 512) hipLaunchKernelGGL(pwa_db_vec_kernel<1>, grid, dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL(pwa_db_vec_kernel<2>, grid, dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }

@@ -272,6 +272,10 @@ SMALL_PWA = [
     (9, 300, 2, 24, "tail:11"),
     (3, 257, 1, 48, "none"),
     (1, 64, 2, 8, "none"),
+    # N % 8 == 0 with a key mask (16-byte row kernels, masked keys), and
+    # N > 512 with a partial last 64-chunk round
+    (4, 136, 2, 32, "random:9"),
+    (2, 520, 1, 16, "tail:5"),
 ]
 
 
