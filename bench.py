@@ -247,6 +247,8 @@ def main():
     ap.add_argument("--pwa-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-pwa", action="store_true")
+    ap.add_argument("--next-steps", type=int, default=5,
+                    help="timed steps of the MSA row attention workload (0 skips it)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn a FETCH_SIZE and a WRITE_SIZE pass of --counters into profiles/traffic.json")
     ap.add_argument("--counters", action="store_true",
@@ -387,6 +389,41 @@ def main():
                          "traffic": traffic_for("pwa_weighted_sum")},
             "kernels_ms": {n: round(v, 4) for n, v in pkms.items()},
         }
+        del pt, pst, pws_f, pws_b, pgr, pout, plse
+        torch.cuda.empty_cache()
+
+    if args.next_steps > 0:
+        # MSA row attention with pair bias: the same kernels on the row attention
+        # the pair-weighted average replaces (1024 MSA rows, N = 768)
+        mc = workloads.CONFIGS["msa_row_attn"]
+        minp = workloads.attention_inputs(mc, with_f64=False)
+        mt = {n: to_dev(minp[n], torch) for n in ("q", "k", "v", "g", "bias", "dout")}
+        mkm = to_dev(minp["key_mask"], torch)
+        del minp
+        mws = torch.empty(pba.pba_backward_workspace_bytes(mc.B, mc.H, mc.N, mc.d, torch.bfloat16),
+                          dtype=torch.uint8, device="cuda")
+        mst = {}
+
+        def mfwd():
+            mst["out"], mst["lse"] = pba.pba_forward(mt["q"], mt["k"], mt["v"], mt["g"], mt["bias"], mkm)
+
+        def mstep():
+            mfwd()
+            pba.pba_backward(mt["q"], mt["k"], mt["v"], mt["g"], mt["bias"], mkm, mst["out"], mst["lse"],
+                             mt["dout"], workspace=mws)
+
+        ms_m, _ = time_loop(mstep, args.next_steps, 2, torch)
+        ms_mf, _ = time_loop(mfwd, args.next_steps, 2, torch)
+        mval = attn_flops(mc.B, mc.H, mc.N, mc.d) / (ms_m * 1e-3) / 1e12
+        mval_f = 4.0 * mc.B * mc.H * mc.N * mc.N * mc.d / (ms_mf * 1e-3) / 1e12
+        result["msa_row_attn"] = {
+            "workload": "msa_row_attn: MSA row attention with pair bias, B=1024 MSA rows, N=768, H=8, d=32, "
+                        "bf16, last 38 keys masked, bias [8,768,768] broadcast over rows, fwd+bwd",
+            "value": round(mval, 2), "unit": "TFLOP/s", "mfma_frac": round(mval / PEAK_BF16_TFLOPS, 4),
+            "ms_per_step": round(ms_m, 4), "steps": args.next_steps,
+            "fwd": {"ms": round(ms_mf, 4), "value": round(mval_f, 2), "unit": "TFLOP/s"},
+        }
+        del mt, mws, mst
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)

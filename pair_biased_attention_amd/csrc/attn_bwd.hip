@@ -1108,14 +1108,16 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
   const int ndk = a.H * a.P * nkb;
   const size_t slab_shmem = a.slab ? slab_bytes(a.N, bf16) : 0;
   if (bf16) {
-    // one launch: the dK/dV tiles first, then the dQ tiles
+    // One launch, the dK/dV tiles first and then the dQ tiles, while the slab
+    // still leaves room for two workgroups per CU (the dynamic LDS of a
+    // launch is sized for its largest role); beyond that, two launches of the
+    // same kernel (dK/dV tiles only, then dQ tiles only with a small LDS).
     const int ndk_slots = (ndk + 7) & ~7;
     const bool qt2 = dp == 32 && bhs * ((a.N + 127) / 128) >= 1024;
     const bool al = (a.N % 8) == 0;
     const int nqb = qt2 ? (a.N + 127) / 128 : (a.N + 63) / 64;
-    const dim3 grid((unsigned)(ndk_slots + bhs * nqb));
     const size_t keep_bytes = (size_t)((a.N + 63) / 64) * 64;
-    const size_t shmem = std::max(slab_shmem, keep_bytes);
+    const bool fuse = dkdv_wgs_per_cu(a.N, a.d, true, a.slab != 0) >= 2;
     const void* fn;
 #define PBA_BWD_FN(DPV, QTV, ALV, SLV) reinterpret_cast<const void*>(&attn_bwd_dq_bf16_kernel<DPV, QTV, ALV, SLV>)
 #define PBA_BWD_PICK(SLV)                                                                    \
@@ -1133,13 +1135,23 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
     }
 #undef PBA_BWD_PICK
 #undef PBA_BWD_FN
+    const size_t shmem_max = std::max(slab_shmem, keep_bytes);
     // the slab can exceed the default 64 KiB dynamic LDS limit
-    if (shmem > 64 * 1024 &&
-        (e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem)) != hipSuccess)
+    if (shmem_max > 64 * 1024 &&
+        (e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem_max)) != hipSuccess)
       return e;
-    int nqb_arg = nqb, ndk_arg = ndk, slots_arg = ndk_slots;
-    void* kargs[] = {&a, &nqb_arg, &ndk_arg, &slots_arg};
-    if ((e = hipLaunchKernel(fn, grid, dim3(256), kargs, shmem, stream)) != hipSuccess) return e;
+    auto launch = [&](unsigned grid, int ndk_arg, int slots_arg, size_t shmem) -> hipError_t {
+      int nqb_arg = nqb;
+      void* kargs[] = {&a, &nqb_arg, &ndk_arg, &slots_arg};
+      return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, shmem, stream);
+    };
+    if (fuse) {
+      if ((e = launch((unsigned)(ndk_slots + bhs * nqb), ndk, ndk_slots, shmem_max)) != hipSuccess) return e;
+    } else {
+      if ((e = launch((unsigned)ndk_slots, ndk, ndk_slots, std::max(slab_shmem, (size_t)16))) != hipSuccess) return e;
+      timer_mark(timer, stream);
+      if ((e = launch((unsigned)(bhs * nqb), 0, 0, keep_bytes)) != hipSuccess) return e;
+    }
     timer_mark(timer, stream);
   } else {
     {

@@ -108,7 +108,7 @@ def _sample_rows(N):
     return np.array(sorted({0, 1, N // 3, N // 2 + 1, N - 20 if N > 20 else 0, N - 1}))
 
 
-@pytest.mark.parametrize("name", ["tiny_fp32", "tri_attn_n384", "pairformer_apb", "dit_apb_x48"])
+@pytest.mark.parametrize("name", ["tiny_fp32", "tri_attn_n384", "pairformer_apb", "dit_apb_x48", "msa_row_attn"])
 def test_attention_workload(name):
     cfg = workloads.CONFIGS[name]
     dtype = cfg.dtype

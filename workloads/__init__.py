@@ -15,12 +15,18 @@ Workloads (all values standard normal, as the task's configurations state):
                        N=384, H=16, d=48, bf16, one bias shared by the copies.
 * ``msa_pwa``         MSA pair-weighted averaging: S=1024 MSA rows, N=768,
                        H=8, d=32, bf16, no QK term.
+* ``msa_row_attn``    MSA row attention with pair bias, the operation the
+                       pair-weighted average replaces: B=1024 MSA rows,
+                       N=768, H=8, d=32, bf16, one bias shared by the rows,
+                       last 5 % of keys masked (keys 730..767).
 
 Where the workloads come from: the AlphaFold3 open-source implementation page
 (molayo1419.me, "Show HN: AlphaFold3 open-source implementation"), sections
 "Model Efficiency" (triangle attention reused from OpenFold; the 48 diffusion
 copies handled as an extra batch dimension) and "MSA Pair Averaging Efficiency"
-(the pair-weighted average that replaces MSA row attention).
+(the pair-weighted average that replaces MSA row attention, and with it
+the row attention itself, whose pair-biased form the page names as the
+DS4Sci MSARowAttentionWithPairBias kernel).
 
 Draw order per workload (generator ``numpy.random.default_rng(seed)``):
 attention: Q, K, V, G, bias, dO, then the masked key indices (tiny case only);
@@ -81,6 +87,8 @@ CONFIGS = {
                               mask="none", seed=1004),
     "msa_pwa": PwaConfig("msa_pwa", S=1024, N=768, H=8, d=32, dtype="bf16",
                          mask="none", seed=1005),
+    "msa_row_attn": AttnConfig("msa_row_attn", B=1024, H=8, N=768, d=32, dtype="bf16",
+                               mask="tail:38", seed=1006),
 }
 ATTN_CONFIGS = [c for c in CONFIGS.values() if c.kind == "attention"]
 PWA_CONFIGS = [c for c in CONFIGS.values() if c.kind == "pwa"]
