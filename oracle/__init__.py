@@ -1,3 +1,6 @@
 """fp64 CPU oracle (test infrastructure; see pba_oracle's header)."""
 from .pba_oracle import *  # noqa: F401,F403
-from .pba_oracle import __all__  # noqa: F401
+from .bias_proj_oracle import *  # noqa: F401,F403
+from . import pba_oracle as _pba, bias_proj_oracle as _bp
+
+__all__ = list(_pba.__all__) + list(_bp.__all__)
