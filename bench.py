@@ -5,10 +5,14 @@ A step is one forward + backward pass of pair-biased gated attention over one
 batch of the triangle-attention workload (B=384 rows, N=384 tokens, H=4
 heads, d=32, bf16 in / fp32 accumulate, last 19 keys masked): pba_forward then
 pba_backward, i.e. every kernel of the attention path.  The pair-weighted
-average (S=1024 MSA rows, N=768, H=8, d=32) is timed in its own loop and
-reported in the same JSON line under "pair_avg".
+average (S=1024 MSA rows, N=768, H=8, d=32), the MSA row attention with pair
+bias (B=1024 rows, N=768, H=8, d=32) and the pair-bias projection
+Linear(LayerNorm(z)) (z [768, 768, 128], H=16) are timed in loops of their
+own and reported in the same JSON line under "pair_avg", "msa_row_attn" and
+"bias_proj".
 
-Prints one JSON line (see the design doc for the definitions of every figure).
+Prints one JSON line: the step figures, per-kernel times, a roofline object for
+the dominant kernel and the CPU oracle baseline.
 """
 from __future__ import annotations
 
@@ -51,6 +55,30 @@ def attn_kernel_flops(B, H, N, d):
 ATTN_BWD_KERNELS = ["bwd_pre", "bwd_dkdv_dq", "bwd_dbias_reduce"]
 PWA_FWD_KERNELS = ["pwa_softmax", "pwa_weighted_sum"]
 PWA_BWD_KERNELS = ["pwa_bwd_softmax", "pwa_bwd_pre", "pwa_bwd_dv_dw", "pwa_bwd_db"]
+
+
+def proj_fwd_bytes(N, H, c):
+    """Algorithmic HBM bytes of the pair-bias projection forward: read z
+    [N,N,c] bf16, write bias [H,N,N] bf16, read gamma, beta, w (fp32)."""
+    P = N * N
+    return P * (2 * c + 2 * H) + 4 * (2 * c + H * c)
+
+
+def proj_bwd_bytes(N, H, c):
+    """Backward: read z and dbias, write dz (bf16), read and write the fp32
+    parameters and their gradients; the per-workgroup partial sums are the
+    kernels' own traffic, not algorithmic."""
+    P = N * N
+    return P * (4 * c + 2 * H) + 8 * (2 * c + H * c)
+
+
+def proj_main_bwd_bytes(N, H, c):
+    """The backward's main kernel alone: z and dbias in, dz out."""
+    return N * N * (4 * c + 2 * H)
+
+
+PROJ_FWD_KERNELS = ["bias_proj_fwd"]
+PROJ_BWD_KERNELS = ["bias_proj_bwd", "bias_proj_reduce"]
 
 
 def pwa_bytes(S, N, H, d, elt=2):
@@ -138,6 +166,8 @@ KERNEL_SOURCES = {
     "pwa_weighted_sum": ("pwa_gemm_kernel<32, true", "pwa.hip"),
     "pwa_bwd_pre": ("pwa_bwd_pre_kernel", "pwa.hip"),
     "pwa_bwd_dv_dw": ("pwa_gemm_kernel<32, false", "pwa.hip"),
+    "bias_proj_fwd": ("bias_proj_fwd_kernel<4>", "bias_proj.hip"),
+    "bias_proj_bwd": ("bias_proj_bwd_kernel<4>", "bias_proj.hip"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -237,6 +267,74 @@ def counters_pass(args, torch, pba):
         pba.pair_weighted_avg_backward(pt["b"], pt["v"], pt["g"], None, o, l, pt["dout"])
     torch.cuda.synchronize()
     print(f"pair-average steps done: {args.pwa_steps}", flush=True)
+    del pt
+    jc = workloads.CONFIGS["bias_proj_pairformer"]
+    jin = workloads.bias_proj_inputs(jc, with_f64=False)
+    z, dbias = to_dev(jin["z"], torch), to_dev(jin["dbias"], torch)
+    prm = {n: torch.from_numpy(jin[n]).cuda() for n in ("gamma", "beta", "w")}
+    for _ in range(args.pwa_steps):
+        pba.pba_bias_proj_forward(z, prm["gamma"], prm["beta"], prm["w"], 1e-5)
+        pba.pba_bias_proj_backward(z, prm["gamma"], prm["beta"], prm["w"], dbias, 1e-5)
+    torch.cuda.synchronize()
+    print(f"projection steps done: {args.pwa_steps}", flush=True)
+
+
+def bench_proj(args, torch, pba):
+    """Pair-bias projection bias = Linear(LayerNorm(z)) forward + backward on the
+    Pairformer pair bias (z [768, 768, 128] bf16, H = 16)."""
+    jc = workloads.CONFIGS["bias_proj_pairformer"]
+    N, H, c = jc.N, jc.H, jc.c
+    jin = workloads.bias_proj_inputs(jc, with_f64=False)
+    z = to_dev(jin["z"], torch)
+    dbias = to_dev(jin["dbias"], torch)
+    prm = {n: torch.from_numpy(jin[n]).cuda() for n in ("gamma", "beta", "w")}
+    del jin
+    eps = 1e-5
+    jws = torch.empty(pba.pba_bias_proj_backward_workspace_bytes(N, H, c), dtype=torch.uint8, device="cuda")
+    bias = torch.empty((H, N, N), dtype=torch.bfloat16, device="cuda")
+    grads = {"dz": torch.empty_like(z), "dgamma": torch.empty_like(prm["gamma"]),
+             "dbeta": torch.empty_like(prm["beta"]), "dw": torch.empty_like(prm["w"])}
+
+    def jfwd():
+        pba.pba_bias_proj_forward(z, prm["gamma"], prm["beta"], prm["w"], eps)
+
+    def jstep():
+        jfwd()
+        pba.pba_bias_proj_backward(z, prm["gamma"], prm["beta"], prm["w"], dbias, eps, workspace=jws)
+
+    ms_j, _ = time_loop(jstep, args.proj_steps, 3, torch)
+    ms_jf, _ = time_loop(jfwd, args.proj_steps, 3, torch)
+    acc_f, acc_b = [0.0], [0.0] * len(PROJ_BWD_KERNELS)
+    for i in range(args.proj_steps + 1):
+        f = pba.pba_bias_proj_forward_timed(z, prm["gamma"], prm["beta"], prm["w"], eps, bias)
+        b = pba.pba_bias_proj_backward_timed(z, prm["gamma"], prm["beta"], prm["w"], dbias, eps, jws, grads)
+        if i:  # the first pass is a warm-up
+            acc_f = [x + y for x, y in zip(acc_f, f)]
+            acc_b = [x + y for x, y in zip(acc_b, b)]
+    kms = {n: a / args.proj_steps for n, a in zip(PROJ_FWD_KERNELS + PROJ_BWD_KERNELS, acc_f + acc_b)}
+    step_bytes = proj_fwd_bytes(N, H, c) + proj_bwd_bytes(N, H, c)
+    gbs = step_bytes / (ms_j * 1e-3) / 1e9
+    gbs_f = proj_fwd_bytes(N, H, c) / (ms_jf * 1e-3) / 1e9
+    kb = proj_main_bwd_bytes(N, H, c)
+    kgbs = kb / (kms["bias_proj_bwd"] * 1e-3) / 1e9
+    fgbs = proj_fwd_bytes(N, H, c) / (kms["bias_proj_fwd"] * 1e-3) / 1e9
+    out = {
+        "workload": "bias_proj_pairformer: bias = Linear(LayerNorm(z)), z [768,768,128] bf16 -> bias [16,768,768] "
+                    "bf16, fp32 gamma/beta/w, fwd+bwd (dz, dgamma, dbeta, dw)",
+        "value": round(gbs, 1), "unit": "GB/s", "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+        "ms_per_step": round(ms_j, 4), "steps": args.proj_steps,
+        "fwd": {"ms": round(ms_jf, 4), "value": round(gbs_f, 1), "unit": "GB/s",
+                "hbm_frac": round(gbs_f / PEAK_HBM_GBS, 4),
+                "kernel_gbs": round(fgbs, 1), "traffic": traffic_for("bias_proj_fwd")},
+        "roofline": {"kernel": "bias_proj_bwd", "bound": "hbm", "achieved": round(kgbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(kgbs / PEAK_HBM_GBS, 4),
+                     "ms_per_launch": round(kms["bias_proj_bwd"], 4), "bytes_per_launch": kb,
+                     "traffic": traffic_for("bias_proj_bwd")},
+        "kernels_ms": {n: round(v, 4) for n, v in kms.items()},
+    }
+    del z, dbias, prm, jws, bias, grads
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -249,6 +347,8 @@ def main():
     ap.add_argument("--no-pwa", action="store_true")
     ap.add_argument("--next-steps", type=int, default=5,
                     help="timed steps of the MSA row attention workload (0 skips it)")
+    ap.add_argument("--proj-steps", type=int, default=20,
+                    help="timed steps of the pair-bias projection Linear(LayerNorm(z)) (0 skips it)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="turn a FETCH_SIZE and a WRITE_SIZE pass of --counters into profiles/traffic.json")
     ap.add_argument("--counters", action="store_true",
@@ -424,6 +524,9 @@ def main():
             "fwd": {"ms": round(ms_mf, 4), "value": round(mval_f, 2), "unit": "TFLOP/s"},
         }
         del mt, mws, mst
+
+    if args.proj_steps > 0:
+        result["bias_proj"] = bench_proj(args, torch, pba)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)

@@ -24,6 +24,11 @@
  *     out[s,i,h,:] = sigmoid(G[s,i,h,:]) * sum_j w[h,i,j] V[s,j,h,:]
  *   The backward pass returns dV, dG and db (db is reduced over s).
  *
+ *   Pair-bias projection (section "Model Efficiency": the bias each attention
+ *   adds is projected from the pair representation z [N, N, c]):
+ *     bias[h,i,j] = sum_c w[h,c] * (gamma[c] * LayerNorm(z[i,j,:])[c] + beta[c])
+ *   and its backward (dz, dgamma, dbeta, dw given dbias).
+ *
  * Conventions for every entry point:
  *   - All tensor arguments are DEVICE pointers to contiguous row-major
  *     buffers owned by the caller, 16-byte aligned.  Outputs must not alias
@@ -31,7 +36,8 @@
  *     the *_timed measurement entry points at the end of this header).
  *   - Element type: PBA_F32 (float) or PBA_BF16 (bfloat16 bit patterns,
  *     uint16).  Outputs and gradients use the input type; lse, lse_w and all
- *     workspace partials are float32.
+ *     workspace partials are float32, and so are the projection's LayerNorm
+ *     and weight parameters and their gradients.
  *   - key_mask: [N] uint8 device pointer, 0 = masked key, nonzero = keep;
  *     NULL means every key is kept.  A query with every key masked gets
  *     out = 0, lse = -inf and zero gradients.
@@ -62,8 +68,10 @@ typedef enum { PBA_F32 = 0, PBA_BF16 = 1 } pba_dtype;
 typedef enum {
   PBA_OK = 0,
   PBA_ERR_NULL = 1,        /* a required pointer is NULL                      */
-  PBA_ERR_SHAPE = 2,       /* a size is <= 0 or too large for 32-bit indexing */
-  PBA_ERR_UNSUPPORTED = 3, /* unsupported dtype or head width d               */
+  PBA_ERR_SHAPE = 2,       /* a size is <= 0 or too large for 32-bit indexing,
+                              or a LayerNorm eps that is not finite and > 0   */
+  PBA_ERR_UNSUPPORTED = 3, /* unsupported dtype, head width d, head count H
+                              or channel count c                              */
   PBA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
   PBA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
   PBA_ERR_HIP = 6          /* the HIP runtime reported an error at launch     */
@@ -144,6 +152,51 @@ int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype,
                                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Pair-bias projection bias = Linear(LayerNorm(z)) and its backward (the
+ * AlphaFold3 open-source implementation page, section "Model Efficiency":
+ * every attention projects its pair bias from the pair representation and
+ * that projection needs a gradient; the Protenix page lists LayerNorm among
+ * the kernels worth a custom implementation).  Per pair position p = i N + j:
+ *   xhat = (z[p,:] - mean) / sqrt(var + eps)   (biased variance over c)
+ *   bias[h, p] = sum_c w[h, c] (gamma[c] xhat[c] + beta[c])   (no offset term)
+ * Arguments:
+ *   z          : [N, N, c]  bf16 (pair representation)
+ *   gamma, beta: [c]        float32 (LayerNorm scale and shift)
+ *   w          : [H, c]     float32 (projection weight, row h = head h)
+ *   eps        : LayerNorm epsilon, finite and > 0
+ *   bias       : [H, N, N]  bf16 (written), the layout pba_forward takes
+ * Every pointer is 16-byte aligned, as for the other entry points.
+ * dtype must be PBA_BF16 (PBA_ERR_UNSUPPORTED otherwise).  Supported sizes:
+ * c in {32, 64, 128}, 1 <= H <= 16, N >= 1 and N * N * c below 2^31 - 2^14
+ * (PBA_ERR_UNSUPPORTED / PBA_ERR_SHAPE otherwise).  The products run with
+ * bf16 operands (xhat and gamma * w) and float32 accumulation.
+ */
+int pba_bias_proj_forward(int N, int H, int c, int dtype,
+                          const void* z, const float* gamma, const float* beta,
+                          const float* w, float eps, void* bias, void* stream);
+
+/* Bytes of device workspace pba_bias_proj_backward needs (0 if invalid). */
+size_t pba_bias_proj_backward_workspace_bytes(int N, int H, int c, int dtype);
+
+/*
+ * Backward of pba_bias_proj_forward given dbias [H, N, N] (bf16, e.g. the
+ * dbias of pba_backward).  The LayerNorm statistics are recomputed from z.
+ * Writes
+ *   dz     : [N, N, c]  bf16
+ *   dgamma : [c]        float32   (summed over all N * N positions)
+ *   dbeta  : [c]        float32
+ *   dw     : [H, c]     float32
+ * workspace: at least pba_bias_proj_backward_workspace_bytes(...) bytes
+ * (per-workgroup partial sums, no initialisation needed).  The sums over
+ * positions are taken in a fixed order, so results are bitwise reproducible.
+ */
+int pba_bias_proj_backward(int N, int H, int c, int dtype,
+                           const void* z, const float* gamma, const float* beta,
+                           const float* w, float eps, const void* dbias,
+                           void* dz, float* dgamma, float* dbeta, float* dw,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement entry points.  Each takes the arguments of the call it names,
  * enqueues exactly the same kernels on `stream`, records a HIP event before
  * the first kernel and after every kernel, waits for the last event and
@@ -159,6 +212,10 @@ int pair_weighted_avg_backward(int S, int N, int H, int d, int dtype,
  *   pair_weighted_avg_backward_timed:  weight softmax (w and w^T), preprocess
  *                                      (dA, dG), dV product together with the
  *                                      dw partials (one launch), db
+ *   pba_bias_proj_forward_timed:       LayerNorm + projection (one launch)
+ *   pba_bias_proj_backward_timed:      dz with the per-workgroup sums of
+ *                                      dbias (x) xhat and dbias, then their
+ *                                      reduction into dw, dgamma, dbeta
  * kernel_ms or n_kernels NULL returns PBA_ERR_NULL; a runtime failure returns
  * PBA_ERR_HIP.
  */
@@ -182,6 +239,16 @@ int pair_weighted_avg_backward_timed(int S, int N, int H, int d, int dtype,
                                      void* dv, void* dg, void* db,
                                      void* workspace, size_t workspace_bytes, void* stream,
                                      float* kernel_ms, int capacity, int* n_kernels);
+int pba_bias_proj_forward_timed(int N, int H, int c, int dtype,
+                                const void* z, const float* gamma, const float* beta,
+                                const float* w, float eps, void* bias, void* stream,
+                                float* kernel_ms, int capacity, int* n_kernels);
+int pba_bias_proj_backward_timed(int N, int H, int c, int dtype,
+                                 const void* z, const float* gamma, const float* beta,
+                                 const float* w, float eps, const void* dbias,
+                                 void* dz, float* dgamma, float* dbeta, float* dw,
+                                 void* workspace, size_t workspace_bytes, void* stream,
+                                 float* kernel_ms, int capacity, int* n_kernels);
 
 #ifdef __cplusplus
 }

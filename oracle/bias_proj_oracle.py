@@ -16,7 +16,7 @@ names LayerNorm as a kernel worth a custom implementation):
         y     = gamma * xhat + beta                          (affine LayerNorm)
         bias[h, i, j] = sum_k w[h, k] * y[k]                 (linear, no offset)
 
-Readings where the pages are silent (listed in the design doc): the projection is
+Readings where the pages are silent: the projection is
 LayerNorm followed by a linear map without an offset term, the LayerNorm is
 affine with eps = 1e-5 and the biased variance, the output is laid out
 [H, N, N] (head, query, key) as the attention consumes it.

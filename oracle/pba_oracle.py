@@ -27,7 +27,7 @@ on gittoolsai.com):
 * the benchmark spec's formula: softmax(Q K^T / sqrt(d) + B_pair + mask) V,
   multiplied elementwise by sigmoid(G).
 
-Readings where the pages are silent (each is listed in the design doc):
+Readings where the pages are silent:
 * the 1/sqrt(d) scale multiplies Q K^T only, with d the real head dimension;
 * the key mask is a [N] byte vector (0 = masked, nonzero = keep) shared over
   batch, heads and queries; a masked key gets logit -inf, so its weight is 0;

@@ -20,7 +20,7 @@ STATUS = {
 }
 
 # exported symbol -> (restype, argtypes)
-_i, _sz, _p, _f = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p
+_i, _sz, _p, _fl = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 SIGNATURES = {
     "pba_abi_version": (_i, []),
     "pba_status_string": (ctypes.c_char_p, [_i]),
@@ -39,6 +39,13 @@ SIGNATURES = {
                                      _p, _i, _p]),
     "pair_weighted_avg_backward_timed": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p,
                                               _p, _p, _p, _p, _sz, _p, _p, _i, _p]),
+    "pba_bias_proj_forward": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _fl, _p, _p]),
+    "pba_bias_proj_backward_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "pba_bias_proj_backward": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _fl, _p, _p, _p, _p, _p,
+                                    _p, _sz, _p]),
+    "pba_bias_proj_forward_timed": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _fl, _p, _p, _p, _i, _p]),
+    "pba_bias_proj_backward_timed": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _fl, _p, _p, _p, _p, _p,
+                                          _p, _sz, _p, _p, _i, _p]),
 }
 
 _lib = None

@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr long long kMaxElems = (1LL << 31) - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -44,6 +44,19 @@ int check_pwa_sizes(int S, int N, int H, int d, int dtype) {
   if (st != PBA_OK) return st;
   if ((long long)S * N * H * d > kMaxPwaElems) return PBA_ERR_SHAPE;
   if ((long long)H * N * N > kMaxPwaElems) return PBA_ERR_SHAPE;
+  return PBA_OK;
+}
+
+// Pair-bias projection: the kernels address z, dz and the [H,N,N] planes
+// with 32-bit byte offsets, and a ragged last tile reaches up to 16
+// positions past the end.
+constexpr long long kMaxProjElems = (1LL << 31) - (1LL << 14);
+
+int check_proj_sizes(int N, int H, int c, int dtype) {
+  if (dtype != PBA_BF16) return PBA_ERR_UNSUPPORTED;
+  if (N <= 0 || H <= 0 || c <= 0) return PBA_ERR_SHAPE;
+  if (H > 16 || (c != 32 && c != 64 && c != 128)) return PBA_ERR_UNSUPPORTED;
+  if ((long long)N * N * c > kMaxProjElems || (long long)N * N * H > kMaxProjElems) return PBA_ERR_SHAPE;
   return PBA_OK;
 }
 
@@ -87,6 +100,43 @@ int prep_backward(int B, int H, int N, int d, int dtype, const void* q, const vo
   return PBA_OK;
 }
 
+int prep_proj(int N, int H, int c, int dtype, const void* z, const float* gamma, const float* beta,
+              const float* w, float eps, pba::ProjArgs& a) {
+  int st = check_proj_sizes(N, H, c, dtype);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({z, gamma, beta, w})) != PBA_OK) return st;
+  if ((st = all_aligned16({z, gamma, beta, w})) != PBA_OK) return st;
+  if (!(eps > 0.0f) || !isfinite(eps)) return PBA_ERR_SHAPE;
+  a.z = z; a.gamma = gamma; a.beta = beta; a.w = w;
+  a.N = N; a.H = H; a.c = c; a.eps = eps;
+  return PBA_OK;
+}
+
+int prep_proj_fwd(int N, int H, int c, int dtype, const void* z, const float* gamma, const float* beta,
+                  const float* w, float eps, void* bias, pba::ProjArgs& a) {
+  int st = prep_proj(N, H, c, dtype, z, gamma, beta, w, eps, a);
+  if (st != PBA_OK) return st;
+  if (bias == nullptr) return PBA_ERR_NULL;
+  if (!aligned16(bias)) return PBA_ERR_ALIGN;
+  a.bias = bias;
+  return PBA_OK;
+}
+
+int prep_proj_bwd(int N, int H, int c, int dtype, const void* z, const float* gamma, const float* beta,
+                  const float* w, float eps, const void* dbias, void* dz, float* dgamma, float* dbeta, float* dw,
+                  void* workspace, size_t workspace_bytes, pba::ProjArgs& a) {
+  int st = prep_proj(N, H, c, dtype, z, gamma, beta, w, eps, a);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({dbias, dz, dgamma, dbeta, dw})) != PBA_OK) return st;
+  if ((st = all_aligned16({dbias, dz, dgamma, dbeta, dw})) != PBA_OK) return st;
+  if (workspace == nullptr || workspace_bytes < pba::proj_bwd_workspace_bytes(N, c)) return PBA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PBA_ERR_ALIGN;
+  a.dbias = dbias; a.dz = dz; a.dgamma = dgamma; a.dbeta = dbeta; a.dw = dw;
+  a.partial = static_cast<float*>(workspace);
+  a.nwg = pba::proj_bwd_workgroups(N, c);
+  return PBA_OK;
+}
+
 // Measurement helper: runs `launch` with a kernel timer, waits for the last
 // event and reports each kernel's duration in milliseconds.
 template <typename F>
@@ -109,7 +159,7 @@ int run_timed(F launch, hipStream_t stream, float* kernel_ms, int capacity, int*
     for (int i = 0; i < t.n && i < capacity; ++i)
       if (hipEventElapsedTime(&kernel_ms[i], t.ev[i], t.ev[i + 1]) != hipSuccess) st = PBA_ERR_HIP;
   }
-  for (int i = 0; i < made; ++i) hipEventDestroy(t.ev[i]);
+  for (int i = 0; i < made; ++i) (void)hipEventDestroy(t.ev[i]);
   return st;
 }
 
@@ -123,8 +173,8 @@ const char* pba_status_string(int status) {
   switch (status) {
     case PBA_OK: return "PBA_OK";
     case PBA_ERR_NULL: return "PBA_ERR_NULL: a required pointer is NULL";
-    case PBA_ERR_SHAPE: return "PBA_ERR_SHAPE: a size is <= 0 or too large";
-    case PBA_ERR_UNSUPPORTED: return "PBA_ERR_UNSUPPORTED: unsupported dtype or head width";
+    case PBA_ERR_SHAPE: return "PBA_ERR_SHAPE: a size is <= 0 or too large, or eps is not a positive finite value";
+    case PBA_ERR_UNSUPPORTED: return "PBA_ERR_UNSUPPORTED: unsupported dtype, head width, head count or channel count";
     case PBA_ERR_ALIGN: return "PBA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case PBA_ERR_WORKSPACE: return "PBA_ERR_WORKSPACE: workspace missing or too small";
     case PBA_ERR_HIP: return "PBA_ERR_HIP: the HIP runtime reported a launch error";
@@ -271,6 +321,53 @@ int pair_weighted_avg_backward_timed(int S, int N, int H, int d, int dtype, cons
                               workspace_bytes, a);
   if (st != PBA_OK) return st;
   return run_timed([&](pba::KernelTimer* t, hipStream_t s) { return pba::launch_pwa_bwd(a, true, s, t); },
+                   static_cast<hipStream_t>(stream), kernel_ms, capacity, n_kernels);
+}
+
+int pba_bias_proj_forward(int N, int H, int c, int dtype, const void* z, const float* gamma, const float* beta,
+                          const float* w, float eps, void* bias, void* stream) {
+  pba::ProjArgs a{};
+  const int st = prep_proj_fwd(N, H, c, dtype, z, gamma, beta, w, eps, bias, a);
+  if (st != PBA_OK) return st;
+  const hipError_t e = pba::launch_proj_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+int pba_bias_proj_forward_timed(int N, int H, int c, int dtype, const void* z, const float* gamma,
+                                const float* beta, const float* w, float eps, void* bias, void* stream,
+                                float* kernel_ms, int capacity, int* n_kernels) {
+  pba::ProjArgs a{};
+  const int st = prep_proj_fwd(N, H, c, dtype, z, gamma, beta, w, eps, bias, a);
+  if (st != PBA_OK) return st;
+  return run_timed([&](pba::KernelTimer* t, hipStream_t s) { return pba::launch_proj_fwd(a, s, t); },
+                   static_cast<hipStream_t>(stream), kernel_ms, capacity, n_kernels);
+}
+
+size_t pba_bias_proj_backward_workspace_bytes(int N, int H, int c, int dtype) {
+  if (check_proj_sizes(N, H, c, dtype) != PBA_OK) return 0;
+  return pba::proj_bwd_workspace_bytes(N, c);
+}
+
+int pba_bias_proj_backward(int N, int H, int c, int dtype, const void* z, const float* gamma, const float* beta,
+                           const float* w, float eps, const void* dbias, void* dz, float* dgamma, float* dbeta,
+                           float* dw, void* workspace, size_t workspace_bytes, void* stream) {
+  pba::ProjArgs a{};
+  const int st = prep_proj_bwd(N, H, c, dtype, z, gamma, beta, w, eps, dbias, dz, dgamma, dbeta, dw, workspace,
+                               workspace_bytes, a);
+  if (st != PBA_OK) return st;
+  const hipError_t e = pba::launch_proj_bwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+int pba_bias_proj_backward_timed(int N, int H, int c, int dtype, const void* z, const float* gamma,
+                                 const float* beta, const float* w, float eps, const void* dbias, void* dz,
+                                 float* dgamma, float* dbeta, float* dw, void* workspace, size_t workspace_bytes,
+                                 void* stream, float* kernel_ms, int capacity, int* n_kernels) {
+  pba::ProjArgs a{};
+  const int st = prep_proj_bwd(N, H, c, dtype, z, gamma, beta, w, eps, dbias, dz, dgamma, dbeta, dw, workspace,
+                               workspace_bytes, a);
+  if (st != PBA_OK) return st;
+  return run_timed([&](pba::KernelTimer* t, hipStream_t s) { return pba::launch_proj_bwd(a, s, t); },
                    static_cast<hipStream_t>(stream), kernel_ms, capacity, n_kernels);
 }
 

@@ -70,6 +70,31 @@ struct PwaArgs {
   int P;            // S chunks of the dw reduction
 };
 
+// Pair-bias projection bias = Linear(LayerNorm(z)): z, bias, dbias, dz are
+// bf16; the LayerNorm and projection parameters and their gradients fp32.
+struct ProjArgs {
+  const void* z;        // [N, N, c]
+  const float* gamma;   // [c]
+  const float* beta;    // [c]
+  const float* w;       // [H, c]
+  void* bias;           // forward output [H, N, N]
+  const void* dbias;    // backward input [H, N, N]
+  void* dz;             // [N, N, c]
+  float* dgamma;        // [c]
+  float* dbeta;         // [c]
+  float* dw;            // [H, c]
+  float* partial;       // workspace: per-workgroup sums, [nwg][16 c + 16]
+  int N, H, c;
+  float eps;
+  int nwg;              // backward workgroups (proj_bwd_workgroups)
+};
+// Backward: one workgroup per CU at most (its per-workgroup sums are the
+// workspace), as many waves as the kernel's registers leave room for.
+constexpr int kProjBwdMaxWg = 256;
+constexpr int proj_bwd_waves(int c) { return c >= 128 ? 8 : 16; }
+int proj_bwd_workgroups(int N, int c);
+size_t proj_bwd_workspace_bytes(int N, int c);
+
 // Workspace plan of the attention backward (byte offsets into one buffer).
 struct BwdPlan {
   size_t off_da, off_drow, off_partial, total;
@@ -103,5 +128,7 @@ hipError_t launch_attn_fwd(const FwdArgs& a, bool bf16, hipStream_t stream);
 hipError_t launch_attn_bwd(const BwdArgs& a, bool bf16, hipStream_t stream, KernelTimer* timer = nullptr);
 hipError_t launch_pwa_fwd(const PwaArgs& a, bool bf16, hipStream_t stream, KernelTimer* timer = nullptr);
 hipError_t launch_pwa_bwd(const PwaArgs& a, bool bf16, hipStream_t stream, KernelTimer* timer = nullptr);
+hipError_t launch_proj_fwd(const ProjArgs& a, hipStream_t stream, KernelTimer* timer = nullptr);
+hipError_t launch_proj_bwd(const ProjArgs& a, hipStream_t stream, KernelTimer* timer = nullptr);
 
 }  // namespace pba

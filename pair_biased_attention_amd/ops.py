@@ -3,6 +3,7 @@
 PyTorch supplies device memory and the current HIP stream; every step of the
 computation runs in libpba's kernels.  Layouts (contiguous, row-major):
   attention  q, k, v, g, out, dout, dq, dk, dv, dg: [B, H, N, d]; bias, dbias: [H, N, N]
+  pair-bias projection  z, dz: [N, N, c] bf16; gamma, beta: [c], w: [H, c] float32; bias: [H, N, N]
   pair-weighted average  v, g, out, dout, dv, dg: [S, N, H, d]; b, db: [H, N, N]
   key_mask: [N] uint8 (0 = masked) or None.
 """
@@ -129,6 +130,65 @@ def pair_weighted_avg_backward(b, v, g, key_mask, out, lse_w, dout, workspace=No
     return {"dv": dv, "dg": dg, "db": db}
 
 
+def _check_proj(z, params: dict, planes: dict):
+    """z [N, N, c] bf16; float32 parameters; bf16 [H, N, N] planes; all on z's device, contiguous."""
+    if z.dtype != torch.bfloat16:
+        raise TypeError(f"z has dtype {z.dtype}; the projection takes bfloat16 z")
+    if z.device.type != "cuda":
+        raise ValueError("pba kernels run on the GPU; got a tensor on " + str(z.device))
+    if z.dim() != 3 or z.shape[0] != z.shape[1]:
+        raise ValueError(f"z must be [N, N, c], got {tuple(z.shape)}")
+    for group, dtype in ((params, torch.float32), (planes, torch.bfloat16)):
+        for name, (t, shape) in group.items():
+            if t.dtype != dtype:
+                raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+            if t.device != z.device:
+                raise ValueError(f"{name} is on {t.device}, expected {z.device}")
+            if not t.is_contiguous():
+                raise ValueError(f"{name} must be contiguous")
+            if tuple(t.shape) != tuple(shape):
+                raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not z.is_contiguous():
+        raise ValueError("z must be contiguous")
+
+
+def pba_bias_proj_forward(z, gamma, beta, w, eps=1e-5):
+    """Pair-bias projection bias [H, N, N] (bf16) = Linear(LayerNorm(z)) for z [N, N, c] (bf16);
+    gamma, beta [c] and w [H, c] are float32."""
+    lib = _lib.load()
+    N, c = z.shape[0], z.shape[-1]
+    H = w.shape[0]
+    _check_proj(z, {"gamma": (gamma, (c,)), "beta": (beta, (c,)), "w": (w, (H, c))}, {})
+    bias = torch.empty((H, N, N), dtype=torch.bfloat16, device=z.device)
+    st = lib.pba_bias_proj_forward(N, H, c, _lib.PBA_BF16, _ptr(z), _ptr(gamma), _ptr(beta), _ptr(w), float(eps),
+                                   _ptr(bias), _stream(z.device))
+    _lib.check("pba_bias_proj_forward", st)
+    return bias
+
+
+def pba_bias_proj_backward_workspace_bytes(N, H, c, dtype=torch.bfloat16) -> int:
+    return int(_lib.load().pba_bias_proj_backward_workspace_bytes(N, H, c, _DT[dtype]))
+
+
+def pba_bias_proj_backward(z, gamma, beta, w, dbias, eps=1e-5, workspace=None):
+    """Backward of pba_bias_proj_forward; returns dict(dz, dgamma, dbeta, dw)."""
+    lib = _lib.load()
+    N, c = z.shape[0], z.shape[-1]
+    H = w.shape[0]
+    _check_proj(z, {"gamma": (gamma, (c,)), "beta": (beta, (c,)), "w": (w, (H, c))},
+                {"dbias": (dbias, (H, N, N))})
+    nbytes = lib.pba_bias_proj_backward_workspace_bytes(N, H, c, _lib.PBA_BF16)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=z.device)
+    dz = torch.empty_like(z)
+    dgamma, dbeta, dw = torch.empty_like(gamma), torch.empty_like(beta), torch.empty_like(w)
+    st = lib.pba_bias_proj_backward(N, H, c, _lib.PBA_BF16, _ptr(z), _ptr(gamma), _ptr(beta), _ptr(w), float(eps),
+                                    _ptr(dbias), _ptr(dz), _ptr(dgamma), _ptr(dbeta), _ptr(dw), _ptr(workspace),
+                                    workspace.numel(), _stream(z.device))
+    _lib.check("pba_bias_proj_backward", st)
+    return {"dz": dz, "dgamma": dgamma, "dbeta": dbeta, "dw": dw}
+
+
 # ---- measurement entry points (create HIP events and synchronise) ----------
 
 def _timed_call(fn_name, args):
@@ -165,3 +225,22 @@ def pair_weighted_avg_backward_timed(b, v, g, key_mask, out, lse_w, dout, worksp
         S, N, H, d, _DT[v.dtype], _ptr(b), _ptr(key_mask), _ptr(v), _ptr(g), _ptr(out), _ptr(lse_w), _ptr(dout),
         _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["db"]), _ptr(workspace), workspace.numel(),
         _stream(v.device)])
+
+
+def pba_bias_proj_forward_timed(z, gamma, beta, w, eps, bias):
+    """pba_bias_proj_forward into a preallocated bias; returns per-kernel ms."""
+    N, c = z.shape[0], z.shape[-1]
+    H = w.shape[0]
+    return _timed_call("pba_bias_proj_forward_timed", [
+        N, H, c, _lib.PBA_BF16, _ptr(z), _ptr(gamma), _ptr(beta), _ptr(w), float(eps), _ptr(bias),
+        _stream(z.device)])
+
+
+def pba_bias_proj_backward_timed(z, gamma, beta, w, dbias, eps, workspace, grads):
+    """pba_bias_proj_backward into preallocated `grads` (dz, dgamma, dbeta, dw); returns per-kernel ms."""
+    N, c = z.shape[0], z.shape[-1]
+    H = w.shape[0]
+    return _timed_call("pba_bias_proj_backward_timed", [
+        N, H, c, _lib.PBA_BF16, _ptr(z), _ptr(gamma), _ptr(beta), _ptr(w), float(eps), _ptr(dbias),
+        _ptr(grads["dz"]), _ptr(grads["dgamma"]), _ptr(grads["dbeta"]), _ptr(grads["dw"]), _ptr(workspace),
+        workspace.numel(), _stream(z.device)])

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = _declared()
     for fn in ("pba_forward", "pba_backward", "pba_backward_workspace_bytes", "pair_weighted_avg",
                "pair_weighted_avg_backward", "pair_weighted_avg_workspace_bytes",
-               "pair_weighted_avg_backward_workspace_bytes", "pba_status_string", "pba_abi_version"):
+               "pair_weighted_avg_backward_workspace_bytes", "pba_status_string", "pba_abi_version",
+               "pba_bias_proj_forward", "pba_bias_proj_backward", "pba_bias_proj_backward_workspace_bytes"):
         assert fn in names, fn
     assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
 
@@ -44,7 +45,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pba_abi_version() == 1
+    assert lib.pba_abi_version() == 2
     for code in range(7):
         assert lib.pba_status_string(code)
     assert b"unknown" in lib.pba_status_string(99)
@@ -154,6 +155,74 @@ def test_timed_entry_points_validate_like_their_calls(lib):
         S, N2, H2, d2, 1, FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, ws, needb, None, ms, 8, FAKE)
     assert pb(ws=None) == ERR_WS
     assert pb(ms=None) == ERR_NULL
+
+
+def test_bias_proj_workspace_sizes(lib):
+    # one partial record of 16 c + 16 floats per backward workgroup, at most 256 workgroups
+    for N, H, c in [(384, 4, 128), (768, 16, 128), (5, 3, 32), (64, 16, 64)]:
+        ws = lib.pba_bias_proj_backward_workspace_bytes(N, H, c, 1)
+        rec = (16 * c + 16) * 4
+        assert ws > 0 and ws % rec == 0 and ws // rec <= 256
+    # the record count follows N and c only, not H
+    assert (lib.pba_bias_proj_backward_workspace_bytes(768, 16, 128, 1)
+            == lib.pba_bias_proj_backward_workspace_bytes(768, 1, 128, 1))
+    assert lib.pba_bias_proj_backward_workspace_bytes(768, 16, 128, 0) == 0   # bf16 only
+    assert lib.pba_bias_proj_backward_workspace_bytes(768, 17, 128, 1) == 0   # H <= 16
+    assert lib.pba_bias_proj_backward_workspace_bytes(768, 4, 96, 1) == 0     # c in {32, 64, 128}
+    assert lib.pba_bias_proj_backward_workspace_bytes(0, 4, 128, 1) == 0
+    assert lib.pba_bias_proj_backward_workspace_bytes(5000, 4, 128, 1) == 0   # z too large
+
+
+def test_bias_proj_validation(lib):
+    N, H, c = 64, 4, 128
+
+    def f(N_=N, H_=H, c_=c, dt=1, eps=1e-5, p=None):
+        z, gamma, beta, w, bias = p or [FAKE] * 5
+        return lib.pba_bias_proj_forward(N_, H_, c_, dt, z, gamma, beta, w, eps, bias, None)
+
+    assert f(dt=0) == ERR_UNSUP
+    assert f(H_=17) == ERR_UNSUP
+    assert f(c_=48) == ERR_UNSUP
+    assert f(N_=0) == ERR_SHAPE
+    assert f(eps=0.0) == ERR_SHAPE
+    assert f(eps=float("nan")) == ERR_SHAPE
+    assert f(eps=float("inf")) == ERR_SHAPE
+    for i in range(5):
+        p = [FAKE] * 5
+        p[i] = None
+        assert f(p=p) == ERR_NULL, i
+    p = [FAKE] * 5
+    p[0] = FAKE + 8  # z must be 16-byte aligned
+    assert f(p=p) == ERR_ALIGN
+    p = [FAKE] * 5
+    p[1] = FAKE + 4  # gamma must be 16-byte aligned too
+    assert f(p=p) == ERR_ALIGN
+    need = lib.pba_bias_proj_backward_workspace_bytes(N, H, c, 1)
+
+    def b(ws=FAKE, wsb=need, null_at=None, misalign=None, dt=1):
+        p = [FAKE] * 9
+        if null_at is not None:
+            p[null_at] = None
+        if misalign is not None:
+            p[misalign[0]] = FAKE + misalign[1]
+        return lib.pba_bias_proj_backward(N, H, c, dt, p[0], p[1], p[2], p[3], 1e-5, p[4], p[5], p[6], p[7],
+                                          p[8], ws, wsb, None)
+
+    assert b(dt=0) == ERR_UNSUP
+    for i in range(9):
+        assert b(null_at=i) == ERR_NULL, i
+    assert b(misalign=(4, 8)) == ERR_ALIGN   # dbias
+    assert b(misalign=(5, 8)) == ERR_ALIGN   # dz
+    assert b(misalign=(8, 4)) == ERR_ALIGN   # dw
+    assert b(ws=None) == ERR_WS
+    assert b(wsb=need - 4) == ERR_WS
+    assert b(ws=FAKE + 8) == ERR_ALIGN
+    ms = lambda m=FAKE, n=FAKE: lib.pba_bias_proj_forward_timed(N, H, c, 1, FAKE, FAKE, FAKE, FAKE, 1e-5, FAKE,
+                                                                None, m, 1, n)
+    assert ms(m=None) == ERR_NULL and ms(n=None) == ERR_NULL
+    mb = lambda ws=FAKE, m=FAKE: lib.pba_bias_proj_backward_timed(
+        N, H, c, 1, FAKE, FAKE, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE, FAKE, FAKE, ws, need, None, m, 2, FAKE)
+    assert mb(ws=None) == ERR_WS and mb(m=None) == ERR_NULL
 
 
 def test_binding_rejects_cpu_tensors():

@@ -397,6 +397,17 @@ def test_workload_recipe_matches_fixture():
             assert getattr(cfg, key) == val, (name, key)
         assert cfg.dtype == spec["dtype"], name
         assert cfg.mask == spec["mask"], name
+    for name, spec in fixture["proj_configs"].items():
+        cfg = workloads.CONFIGS[name]
+        assert cfg.kind == "bias_proj", name
+        for key, val in spec["shape"].items():
+            assert getattr(cfg, key) == val, (name, key)
+    small = workloads.ProjConfig("small", N=6, H=3, c=32, seed=5)
+    pin = workloads.bias_proj_inputs(small)
+    assert pin["z"].shape == (6, 6, 32) and pin["z"].dtype == np.uint16
+    assert pin["w"].shape == (3, 32) and pin["w"].dtype == np.float32
+    assert pin["dbias"].shape == (3, 6, 6)
+    assert np.array_equal(pin["gamma64"], pin["gamma"].astype(np.float64))
     # small configs: check the drawn arrays
     inp = workloads.attention_inputs(workloads.CONFIGS["tiny_fp32"])
     assert inp["q"].shape == (32, 4, 32, 32) and inp["bias"].shape == (4, 32, 32)

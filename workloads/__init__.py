@@ -20,6 +20,17 @@ Workloads (all values standard normal, as the task's configurations state):
                        N=768, H=8, d=32, bf16, one bias shared by the rows,
                        last 5 % of keys masked (keys 730..767).
 
+* ``bias_proj_tri_n384``   pair-bias projection Linear(LayerNorm(z)) for the
+                       triangle attention above: z [384, 384, c=128] bf16,
+                       H=4 heads.
+* ``bias_proj_pairformer`` the same projection for the Pairformer pair bias:
+                       z [768, 768, c=128] bf16, H=16 heads.
+  Projection inputs: z = standard normal plus a standard-normal shift per
+  pair position (so that the LayerNorm has a mean to remove), rounded to
+  bf16; gamma = 1 + 0.25 N(0,1), beta = 0.25 N(0,1) and w = N(0,1)/sqrt(c)
+  in float32; dbias standard normal in bf16.  Draw order: z, shift, gamma,
+  beta, w, dbias.
+
 Where the workloads come from: the AlphaFold3 open-source implementation page
 (molayo1419.me, "Show HN: AlphaFold3 open-source implementation"), sections
 "Model Efficiency" (triangle attention reused from OpenFold; the 48 diffusion
@@ -38,9 +49,9 @@ import dataclasses
 import numpy as np
 
 __all__ = [
-    "AttnConfig", "PwaConfig", "CONFIGS", "ATTN_CONFIGS", "PWA_CONFIGS",
+    "AttnConfig", "PwaConfig", "ProjConfig", "CONFIGS", "ATTN_CONFIGS", "PWA_CONFIGS", "PROJ_CONFIGS",
     "bf16_round_bits", "bf16_bits_to_f32", "attention_inputs", "pwa_inputs",
-    "scaled_attention_config", "scaled_pwa_config",
+    "scaled_attention_config", "scaled_pwa_config", "bias_proj_inputs",
 ]
 
 
@@ -76,6 +87,19 @@ class PwaConfig:
         return "pwa"
 
 
+@dataclasses.dataclass(frozen=True)
+class ProjConfig:
+    name: str
+    N: int
+    H: int
+    c: int
+    seed: int
+
+    @property
+    def kind(self) -> str:
+        return "bias_proj"
+
+
 CONFIGS = {
     "tiny_fp32": AttnConfig("tiny_fp32", B=32, H=4, N=32, d=32, dtype="f32",
                             mask="random:3", seed=1001),
@@ -89,9 +113,12 @@ CONFIGS = {
                          mask="none", seed=1005),
     "msa_row_attn": AttnConfig("msa_row_attn", B=1024, H=8, N=768, d=32, dtype="bf16",
                                mask="tail:38", seed=1006),
+    "bias_proj_tri_n384": ProjConfig("bias_proj_tri_n384", N=384, H=4, c=128, seed=1007),
+    "bias_proj_pairformer": ProjConfig("bias_proj_pairformer", N=768, H=16, c=128, seed=1008),
 }
 ATTN_CONFIGS = [c for c in CONFIGS.values() if c.kind == "attention"]
 PWA_CONFIGS = [c for c in CONFIGS.values() if c.kind == "pwa"]
+PROJ_CONFIGS = [c for c in CONFIGS.values() if c.kind == "bias_proj"]
 
 
 def scaled_attention_config(cfg: AttnConfig, **overrides) -> AttnConfig:
@@ -187,4 +214,25 @@ def pwa_inputs(cfg: PwaConfig, seed: int | None = None, with_grad: bool = True,
         out[name], out[name + "64"] = _store(x, cfg.dtype, with_f64)
         del x
     out["key_mask"] = _key_mask(cfg.mask, N, rng)
+    return out
+
+
+def bias_proj_inputs(cfg: ProjConfig, seed: int | None = None, with_f64: bool = True):
+    """Draw one pair-bias projection workload.
+
+    Returns ``z`` (uint16 bf16 bits, [N, N, c]), ``gamma``, ``beta`` ([c]) and
+    ``w`` ([H, c]) as float32, ``dbias`` (bf16 bits, [H, N, N]), and float64
+    copies of the exact stored values (``z64`` ...).
+    """
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    N, H, c = cfg.N, cfg.H, cfg.c
+    out = {"cfg": cfg}
+    z = rng.standard_normal((N, N, c), dtype=np.float32)
+    z += rng.standard_normal((N, N, 1), dtype=np.float32)
+    out["z"], out["z64"] = _store(z, "bf16", with_f64)
+    del z
+    out["gamma"], out["gamma64"] = _store(1.0 + 0.25 * rng.standard_normal(c), "f32")
+    out["beta"], out["beta64"] = _store(0.25 * rng.standard_normal(c), "f32")
+    out["w"], out["w64"] = _store(rng.standard_normal((H, c)) / np.sqrt(c), "f32")
+    out["dbias"], out["dbias64"] = _store(rng.standard_normal((H, N, N), dtype=np.float32), "bf16", with_f64)
     return out
