@@ -7,9 +7,10 @@ heads, d=32, bf16 in / fp32 accumulate, last 19 keys masked): pba_forward then
 pba_backward, i.e. every kernel of the attention path.  The pair-weighted
 average (S=1024 MSA rows, N=768, H=8, d=32), the MSA row attention with pair
 bias (B=1024 rows, N=768, H=8, d=32) and the pair-bias projection
-Linear(LayerNorm(z)) (z [768, 768, 128], H=16) are timed in loops of their
-own and reported in the same JSON line under "pair_avg", "msa_row_attn" and
-"bias_proj".
+Linear(LayerNorm(z)) (z [768, 768, 128], H=16) and the windowed atom
+attention (B=48, N=3072 atoms, H=4, d=32) are timed in loops of their own and
+reported in the same JSON line under "pair_avg", "msa_row_attn", "bias_proj"
+and "local_attn".
 
 Prints one JSON line: the step figures, per-kernel times, a roofline object for
 the dominant kernel and the CPU oracle baseline.
@@ -75,6 +76,24 @@ def proj_bwd_bytes(N, H, c):
 def proj_main_bwd_bytes(N, H, c):
     """The backward's main kernel alone: z and dbias in, dz out."""
     return N * N * (4 * c + 2 * H)
+
+
+LOCAL_BWD_KERNELS = ["local_bwd_pre", "local_bwd_dq", "local_bwd_dkdv", "local_bwd_dbias_reduce"]
+
+
+def local_units(B, H, N, d):
+    """Window score elements times d: every query against its 128 window slots."""
+    return float(B) * H * N * 128 * d
+
+
+def local_kernel_flops(B, H, N, d):
+    """Algorithmic flops credited per launch, as for the dense path: forward
+    4 (QK^T, PV); backward 10, of which the key-stationary launch carries 8
+    (S recompute, dP, dV, dK) and the query-stationary one 2 (dQ; its own
+    recompute of S and dP is not credited)."""
+    u = local_units(B, H, N, d)
+    return {"local_fwd": 4 * u, "local_bwd_pre": 0.0, "local_bwd_dq": 2 * u, "local_bwd_dkdv": 8 * u,
+            "local_bwd_dbias_reduce": 0.0}
 
 
 PROJ_FWD_KERNELS = ["bias_proj_fwd"]
@@ -167,6 +186,9 @@ KERNEL_SOURCES = {
     "pwa_bwd_pre": ("pwa_bwd_pre_kernel", "pwa.hip"),
     "pwa_bwd_dv_dw": ("pwa_gemm_kernel<32, false", "pwa.hip"),
     "bias_proj_fwd": ("bias_proj_fwd_kernel<4>", "bias_proj.hip"),
+    "local_fwd": ("local_fwd_kernel", "local_attn.hip"),
+    "local_bwd_dq": ("local_bwd_dq_kernel", "local_attn.hip"),
+    "local_bwd_dkdv": ("local_bwd_dkdv_kernel", "local_attn.hip"),
     "bias_proj_bwd": ("bias_proj_bwd_kernel<4>", "bias_proj.hip"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
@@ -337,6 +359,62 @@ def bench_proj(args, torch, pba):
     return out
 
 
+def bench_local(args, torch, pba):
+    """Windowed atom attention fwd + bwd on B=48 copies, N=3072 atoms, H=4, d=32."""
+    lc = workloads.CONFIGS["local_atom_attn"]
+    B, H, N, d = lc.B, lc.H, lc.N, lc.d
+    lin = workloads.local_inputs(lc, with_f64=False)
+    t = {n: to_dev(lin[n], torch) for n in ("q", "k", "v", "g", "bias", "dout")}
+    km = to_dev(lin["key_mask"], torch)
+    del lin
+    ws = torch.empty(pba.pba_local_backward_workspace_bytes(B, H, N, d), dtype=torch.uint8, device="cuda")
+    st = {}
+
+    def lfwd():
+        st["out"], st["lse"] = pba.pba_local_forward(t["q"], t["k"], t["v"], t["g"], t["bias"], km)
+
+    def lstep():
+        lfwd()
+        pba.pba_local_backward(t["q"], t["k"], t["v"], t["g"], t["bias"], km, st["out"], st["lse"], t["dout"],
+                               workspace=ws)
+
+    ms_l, _ = time_loop(lstep, args.local_steps, 3, torch)
+    ms_lf, _ = time_loop(lfwd, args.local_steps, 3, torch)
+    grads = {n: torch.empty_like(t["q"]) for n in ("dq", "dk", "dv", "dg")}
+    grads["dbias"] = torch.empty_like(t["bias"])
+    out, lse = torch.empty_like(t["q"]), torch.empty((B, H, N), dtype=torch.float32, device="cuda")
+    acc_f, acc_b = [0.0], [0.0] * len(LOCAL_BWD_KERNELS)
+    for i in range(args.local_steps + 1):
+        f = pba.pba_local_forward_timed(t["q"], t["k"], t["v"], t["g"], t["bias"], km, out, lse)
+        b = pba.pba_local_backward_timed(t["q"], t["k"], t["v"], t["g"], t["bias"], km, out, lse, t["dout"], ws,
+                                         grads)
+        if i:  # the first pass is a warm-up
+            acc_f = [x + y for x, y in zip(acc_f, f)]
+            acc_b = [x + y for x, y in zip(acc_b, b)]
+    kms = {n: a / args.local_steps for n, a in zip(["local_fwd"] + LOCAL_BWD_KERNELS, acc_f + acc_b)}
+    kfl = local_kernel_flops(B, H, N, d)
+    dom = max(kms, key=kms.get)
+    dom_tf = kfl[dom] / (kms[dom] * 1e-3) / 1e12
+    u = local_units(B, H, N, d)
+    val = 14 * u / (ms_l * 1e-3) / 1e12
+    out_obj = {
+        "workload": "local_atom_attn: windowed atom attention with pair bias, B=48 copies, N=3072 atoms, H=4, "
+                    "d=32, bf16, 32-query blocks x 128-key windows, local bias [4,96,32,128], last 154 atoms "
+                    "masked, fwd+bwd",
+        "value": round(val, 2), "unit": "TFLOP/s", "mfma_frac": round(val / PEAK_BF16_TFLOPS, 4),
+        "ms_per_step": round(ms_l, 4), "steps": args.local_steps,
+        "fwd": {"ms": round(ms_lf, 4), "value": round(4 * u / (ms_lf * 1e-3) / 1e12, 2), "unit": "TFLOP/s"},
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": round(dom_tf, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(dom_tf / PEAK_BF16_TFLOPS, 4),
+                     "ms_per_launch": round(kms[dom], 4), "flops_per_launch": kfl[dom],
+                     "traffic": traffic_for(dom)},
+        "kernels_ms": {n: round(v, 4) for n, v in kms.items()},
+    }
+    del t, ws, st, grads, out, lse
+    torch.cuda.empty_cache()
+    return out_obj
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -347,6 +425,8 @@ def main():
     ap.add_argument("--no-pwa", action="store_true")
     ap.add_argument("--next-steps", type=int, default=5,
                     help="timed steps of the MSA row attention workload (0 skips it)")
+    ap.add_argument("--local-steps", type=int, default=20,
+                    help="timed steps of the windowed atom attention (0 skips it)")
     ap.add_argument("--proj-steps", type=int, default=20,
                     help="timed steps of the pair-bias projection Linear(LayerNorm(z)) (0 skips it)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -527,6 +607,8 @@ def main():
 
     if args.proj_steps > 0:
         result["bias_proj"] = bench_proj(args, torch, pba)
+    if args.local_steps > 0:
+        result["local_attn"] = bench_local(args, torch, pba)
 
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg)

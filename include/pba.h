@@ -29,6 +29,10 @@
  *     bias[h,i,j] = sum_c w[h,c] * (gamma[c] * LayerNorm(z[i,j,:])[c] + beta[c])
  *   and its backward (dz, dgamma, dbeta, dw given dbias).
  *
+ *   Windowed attention (same section, atom attention with memory linear in
+ *   the number of atoms): each block of 32 queries attends a window of 128
+ *   keys, with a pair bias that exists only inside the windows.
+ *
  * Conventions for every entry point:
  *   - All tensor arguments are DEVICE pointers to contiguous row-major
  *     buffers owned by the caller, 16-byte aligned.  Outputs must not alias
@@ -197,6 +201,45 @@ int pba_bias_proj_backward(int N, int H, int c, int dtype,
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Windowed (sequence-local) pair-biased gated attention, the atom-attention
+ * form whose memory grows linearly with the number of atoms (AlphaFold3
+ * open-source implementation page, section "Model Efficiency", on the atom
+ * attention encoder and decoder).  Query block q = atoms 32q .. 32q+31
+ * attends the 128 keys 32q-48 .. 32q+79 (window slot s = key - 32q + 48):
+ *   L[b,h,i,s] = Q[b,h,i,:] . K[b,h,32q-48+s,:] / sqrt(d) + bias[h,q,i-32q,s]
+ *                (-inf for slots outside [0, N) and for masked keys)
+ *   P = softmax_s(L),  out = sigmoid(G) * (P V),  lse = log sum_s exp(L)
+ * Arguments as for pba_forward except:
+ *   bias   : [H, ceil(N/32), 32, 128] bf16 (head, query block, query in
+ *            block, window slot), shared by every b
+ * bf16 only; d must be a multiple of 8 up to 32 (PBA_ERR_UNSUPPORTED
+ * otherwise).  A query whose window has no usable key gets out = 0,
+ * lse = -inf and zero gradients.
+ */
+int pba_local_forward(int B, int H, int N, int d, int dtype,
+                      const void* q, const void* k, const void* v, const void* g,
+                      const void* bias, const uint8_t* key_mask,
+                      void* out, float* lse, void* stream);
+
+/* Bytes of device workspace pba_local_backward needs (0 if invalid). */
+size_t pba_local_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward of pba_local_forward.  Inputs as there, plus out, lse and dout
+ * [B, H, N, d].  Writes dq, dk, dv, dg [B, H, N, d] and
+ *   dbias : [H, ceil(N/32), 32, 128] bf16, summed over b (zero at slots
+ *           outside [0, N), at masked keys and at rows past N)
+ * workspace: at least pba_local_backward_workspace_bytes(...) bytes (dA, the
+ * per-row softmax seeds and per-chunk dbias partials; no initialisation).
+ */
+int pba_local_backward(int B, int H, int N, int d, int dtype,
+                       const void* q, const void* k, const void* v, const void* g,
+                       const void* bias, const uint8_t* key_mask,
+                       const void* out, const float* lse, const void* dout,
+                       void* dq, void* dk, void* dv, void* dg, void* dbias,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Measurement entry points.  Each takes the arguments of the call it names,
  * enqueues exactly the same kernels on `stream`, records a HIP event before
  * the first kernel and after every kernel, waits for the last event and
@@ -216,6 +259,10 @@ int pba_bias_proj_backward(int N, int H, int c, int dtype,
  *   pba_bias_proj_backward_timed:      dz with the per-workgroup sums of
  *                                      dbias (x) xhat and dbias, then their
  *                                      reduction into dw, dgamma, dbeta
+ *   pba_local_forward_timed:           one launch
+ *   pba_local_backward_timed:          preprocess (dA, dG, row seeds), dQ with
+ *                                      the per-chunk dbias partials, dK/dV,
+ *                                      dbias reduction
  * kernel_ms or n_kernels NULL returns PBA_ERR_NULL; a runtime failure returns
  * PBA_ERR_HIP.
  */
@@ -249,6 +296,18 @@ int pba_bias_proj_backward_timed(int N, int H, int c, int dtype,
                                  void* dz, float* dgamma, float* dbeta, float* dw,
                                  void* workspace, size_t workspace_bytes, void* stream,
                                  float* kernel_ms, int capacity, int* n_kernels);
+int pba_local_forward_timed(int B, int H, int N, int d, int dtype,
+                            const void* q, const void* k, const void* v, const void* g,
+                            const void* bias, const uint8_t* key_mask,
+                            void* out, float* lse, void* stream,
+                            float* kernel_ms, int capacity, int* n_kernels);
+int pba_local_backward_timed(int B, int H, int N, int d, int dtype,
+                             const void* q, const void* k, const void* v, const void* g,
+                             const void* bias, const uint8_t* key_mask,
+                             const void* out, const float* lse, const void* dout,
+                             void* dq, void* dk, void* dv, void* dg, void* dbias,
+                             void* workspace, size_t workspace_bytes, void* stream,
+                             float* kernel_ms, int capacity, int* n_kernels);
 
 #ifdef __cplusplus
 }

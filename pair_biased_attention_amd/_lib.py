@@ -46,6 +46,14 @@ SIGNATURES = {
     "pba_bias_proj_forward_timed": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _fl, _p, _p, _p, _i, _p]),
     "pba_bias_proj_backward_timed": (_i, [_i, _i, _i, _i, _p, _p, _p, _p, _fl, _p, _p, _p, _p, _p,
                                           _p, _sz, _p, _p, _i, _p]),
+    "pba_local_forward": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p]),
+    "pba_local_backward_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
+    "pba_local_backward": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "pba_local_forward_timed": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                     _p, _i, _p]),
+    "pba_local_backward_timed": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                      _p, _p, _p, _p, _p, _p, _sz, _p, _p, _i, _p]),
 }
 
 _lib = None

@@ -1082,6 +1082,19 @@ BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16) {
   return pl;
 }
 
+hipError_t launch_attn_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream) {
+  const long long rows = (long long)a.B * a.H * a.N;
+  const int rpw = 256 / (a.d / 8);
+  hipLaunchKernelGGL(attn_bwd_pre_bf16_kernel, dim3((unsigned)((rows + rpw - 1) / rpw)), dim3(256), 0, stream, a, rpw);
+  return hipGetLastError();
+}
+
+hipError_t launch_partial_sum_bf16(const float* partial, int P, size_t count, void* out, hipStream_t stream) {
+  const dim3 grid((unsigned)((count / 4 + 255) / 256 + 1));
+  hipLaunchKernelGGL(bias_grad_reduce_kernel<true>, grid, dim3(256), 0, stream, partial, P, count, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, KernelTimer* timer) {
   BwdArgs a = args;
   const int dp = a.d <= 32 ? 32 : 64;

@@ -1,0 +1,519 @@
+// local_attn.hip - windowed (sequence-local) pair-biased gated attention on
+// gfx950, forward and backward.
+//
+// AlphaFold3 open-source implementation page (molayo1419.me), section "Model
+// Efficiency": for the atom attention encoder and decoder the authors tried
+// an implementation whose memory grows linearly with the number of atoms,
+// next to the plain reuse of the dense pair-biased attention kernel.  Linear
+// memory means a fixed window of keys per query and a pair bias that exists
+// only inside the windows.  Here query block q (atoms 32q .. 32q+31) attends
+// the 128 keys 32q - 48 .. 32q + 79 (slot s = key - 32q + 48); bias and dbias
+// are [H, nqb, 32, 128]; everything else (scale, key mask, gate, natural-log
+// lse, rows without keys) is as in the dense kernels.
+//
+// Kernels (d <= 32, bf16):
+//  * forward: one wave per (b, h, query block).  S^T = K Q^T for the whole
+//    window (8 key tiles x 2 query tiles), exact softmax in registers (no
+//    online rescale: the window fits), O^T = V^T P^T with V staged in LDS
+//    and read transposed.  The key order inside the score tiles is permuted
+//    so that lane group g owns the 32 contiguous slots 32g .. 32g + 31: its
+//    bias comes as four 16-byte loads per query row.
+//  * backward, query-stationary: one wave per (h, query block, 16-query tile,
+//    batch chunk) walks the chunk's batch rows in order, recomputes P,
+//    forms dS and dQ = dS K and accumulates dS in registers: one dbias
+//    partial per chunk, summed over chunks in a fixed order afterwards.
+//  * backward, key-stationary: one wave per (b, h, 16-key tile).  Each key
+//    tile lies wholly inside the windows of exactly four query blocks (the
+//    windows are 16-aligned); the workgroup stages the Q, dA rows and seeds of
+//    the six query blocks its four key tiles need, and each wave forms
+//    S = Q K^T (bias added on the matrix core by identity products), P, dP,
+//    dS and accumulates dV = P^T dA and dK = dS^T Q.  No atomics anywhere.
+#include <algorithm>
+
+#include "pba.h"
+#include "pba_device.h"
+#include "pba_kernels.h"
+
+namespace pba {
+namespace {
+
+constexpr uint32_t kOob = 0xFFFFFFF0u;
+constexpr int kRS = 40;  // LDS row stride (elements) of a staged 32-channel row
+
+// Score tile t (0..7), result row r (0..15) -> window slot: lane group g (rows
+// 4g..4g+3) owns slots 32g .. 32g+31, in the order (t, r % 4).
+__device__ __forceinline__ int slot_of(int t, int r) { return 32 * (r >> 2) + 4 * t + (r & 3); }
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Sum over the four lanes of a lane column; every one of them gets the same bits.
+__device__ __forceinline__ float sum_over_groups(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const auto s32 = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  x = __uint_as_float(s32[0]) + __uint_as_float(s32[1]);
+  const uint32_t v = __float_as_uint(x);
+  const auto s16 = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return __uint_as_float(s16[0]) + __uint_as_float(s16[1]);
+}
+
+__device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ forward
+__global__ void __launch_bounds__(256) local_fwd_kernel(LocalArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 sV[4][kLocalWk * kRS];
+  __shared__ __attribute__((aligned(16))) uint8_t sKeep[4][kLocalWk];
+  const int lane = threadIdx.x & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
+  const int N = a.N, d = a.d, nqb = a.nqb;
+  const int nqg = (nqb + 3) / 4;
+  const int bh = blockIdx.x / nqg;
+  const int qb = (blockIdx.x % nqg) * 4 + wave;
+  if (qb >= nqb) return;  // a whole wave; no barrier follows
+  const int h = bh % a.H;
+  const size_t base = (size_t)bh * N * d;
+  const uint32_t tb = (uint32_t)N * d * 2u;
+  const auto rq = make_rsrc(static_cast<const u16*>(a.q) + base, tb);
+  const auto rk = make_rsrc(static_cast<const u16*>(a.k) + base, tb);
+  const auto rv = make_rsrc(static_cast<const u16*>(a.v) + base, tb);
+  const auto rg = make_rsrc(static_cast<const u16*>(a.g) + base, tb);
+  const auto ro = make_rsrc(static_cast<u16*>(a.out) + base, tb);
+  const auto rb = make_rsrc(a.bias, (uint32_t)a.H * nqb * kLocalWq * kLocalWk * 2u);
+  const int key0 = kLocalWq * qb - kLocalOff;
+  auto key_off = [&](int key, int c) -> uint32_t {
+    return (key >= 0 && key < N && c < d) ? (uint32_t)(key * d + c) * 2u : kOob;
+  };
+
+  // V window (row = slot) and the usable flags of the slots
+  u32x4 vv[8];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int c = lane + 64 * it, row = c >> 2, c8 = c & 3;
+    vv[it] = buf_load16(rv, key_off(key0 + row, 8 * c8));
+  }
+  // K operand of tile t: lane (g, r) holds K[slot_of(t, r)][8g .. 8g+7]
+  u32x4 ak[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ak[t] = buf_load16(rk, key_off(key0 + slot_of(t, n), 8 * g));
+  // Q^T operand of query tile qt: lane (g, n) holds Q[32qb + 16qt + n][8g .. 8g+7]
+  u32x4 bq[2];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) bq[qt] = buf_load16(rq, key_off(32 * qb + 16 * qt + n, 8 * g));
+  // bias of query row 16qt + n, slots 32g + 8c .. +7
+  u32x4 bb[2][4];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      bb[qt][c] = buf_load16(rb, (uint32_t)(((h * nqb + qb) * kLocalWq + 16 * qt + n) * kLocalWk + 32 * g + 8 * c) * 2u);
+  {
+    const int s0 = 2 * lane;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int key = key0 + s0 + e;
+      bool ok = key >= 0 && key < N;
+      if (a.mask != nullptr && ok) ok = a.mask[key] != 0;
+      sKeep[wave][s0 + e] = ok ? 1 : 0;
+    }
+  }
+  u16* const mv = sV[wave];
+#pragma unroll
+  for (int it = 0; it < 8; ++it) {
+    const int c = lane + 64 * it, row = c >> 2, c8 = c & 3;
+    *reinterpret_cast<u32x4*>(mv + row * kRS + 8 * c8) = vv[it];
+  }
+  // byte (4t + j) of this lane group's 32 flags: slot 32g + 4t + j
+  const u32x4 kf0 = *reinterpret_cast<const u32x4*>(&sKeep[wave][32 * g]);
+  const u32x4 kf1 = *reinterpret_cast<const u32x4*>(&sKeep[wave][32 * g + 16]);
+
+  const float c1 = a.scale * kLog2e;
+  float m[2], l[2];
+  f32x4 s[2][8];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    float mx = kNegInf;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const f32x4 acc = mfma32(as_bf8(ak[t]), as_bf8(bq[qt]), f32x4{0.f, 0.f, 0.f, 0.f});
+      const uint32_t fl = t < 4 ? kf0[t] : kf1[t - 4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t w = bb[qt][t >> 1][(4 * (t & 1) + j) >> 1];
+        const float bv = (j & 1) ? bf_hi(w) : bf_lo(w);
+        const float x = ((fl >> (8 * j)) & 0xFFu) ? fmaf(acc[j], c1, bv * kLog2e) : kNegInf;
+        s[qt][t][j] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    m[qt] = max_over_groups(mx);
+    const float ms = m[qt] == kNegInf ? 0.f : m[qt];
+    float sum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        s[qt][t][j] = exp2_fast(s[qt][t][j] - ms);
+        sum += s[qt][t][j];
+      }
+    l[qt] = sum_over_groups(sum);
+  }
+  // O^T = V^T P^T: k-step j covers slots 32g + 8j .. +7 (tiles 2j, 2j+1)
+  f32x4 o[2][2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) o[ct][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const bf16x8 av = tr_frag<kRS>(mv, 32 * g + 8 * j, 32 * g + 8 * j + 4, 16 * ct, lane);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) o[ct][qt] = mfma32(av, pack8(s[qt][2 * j], s[qt][2 * j + 1]), o[ct][qt]);
+    }
+  }
+  // epilogue: lane (g, n) holds channels 16ct + 4g .. +3 of query 32qb + 16qt + n
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int query = 32 * qb + 16 * qt + n;
+    const float inv = l[qt] > 0.f ? 1.0f / l[qt] : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const uint32_t off = key_off(query, 16 * ct + 4 * g);
+      const u32x2 gw = buf_load8(rg, off);
+      const float gv[4] = {bf_lo(gw[0]), bf_hi(gw[0]), bf_lo(gw[1]), bf_hi(gw[1])};
+      float y[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] = sigmoidf_fast(gv[r]) * o[ct][qt][r] * inv;
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])}, ro, off, 0, 0);
+    }
+    if (g == 0 && query < N)
+      a.lse[(size_t)bh * N + query] = m[qt] == kNegInf ? kNegInf : (m[qt] + __log2f(l[qt])) * kLn2;
+  }
+}
+
+// ------------------------------------------------------------------ backward, dQ and dbias partials
+__global__ void __launch_bounds__(256) local_bwd_dq_kernel(LocalArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 sK[4][kLocalWk * kRS];
+  __shared__ __attribute__((aligned(16))) uint8_t sKeep[4][kLocalWk];
+  const int lane = threadIdx.x & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
+  const int N = a.N, d = a.d, nqb = a.nqb, H = a.H;
+  // wave task: (chunk, h, qb, qt), qt fastest
+  int w = blockIdx.x * 4 + wave;
+  const int qt = w & 1;
+  w >>= 1;
+  const int qb = w % nqb;
+  w /= nqb;
+  const int h = w % H;
+  const int chunk = w / H;
+  if (chunk >= a.P) return;  // a whole wave; no barrier follows
+  const int b0 = chunk * a.C, b1 = std::min(a.B, b0 + a.C);
+  const int key0 = kLocalWq * qb - kLocalOff;
+  const int query = 32 * qb + 16 * qt + n;
+  const bool qvalid = query < N;
+  const uint32_t tb = (uint32_t)N * d * 2u;
+  auto key_off = [&](int key, int c) -> uint32_t {
+    return (key >= 0 && key < N && c < d) ? (uint32_t)(key * d + c) * 2u : kOob;
+  };
+  const auto rb = make_rsrc(a.bias, (uint32_t)H * nqb * kLocalWq * kLocalWk * 2u);
+  u32x4 bb[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    bb[c] = buf_load16(rb, (uint32_t)(((h * nqb + qb) * kLocalWq + 16 * qt + n) * kLocalWk + 32 * g + 8 * c) * 2u);
+  {
+    const int s0 = 2 * lane;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const int key = key0 + s0 + e;
+      bool ok = key >= 0 && key < N;
+      if (a.mask != nullptr && ok) ok = a.mask[key] != 0;
+      sKeep[wave][s0 + e] = ok ? 1 : 0;
+    }
+  }
+  const u32x4 kf0 = *reinterpret_cast<const u32x4*>(&sKeep[wave][32 * g]);
+  const u32x4 kf1 = *reinterpret_cast<const u32x4*>(&sKeep[wave][32 * g + 16]);
+  // log2(e) * bias, -inf where the slot is unusable or the row does not exist
+  float b2[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) {
+    const uint32_t fl = t < 4 ? kf0[t] : kf1[t - 4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t wv = bb[t >> 1][(4 * (t & 1) + j) >> 1];
+      const float bv = (j & 1) ? bf_hi(wv) : bf_lo(wv);
+      b2[t][j] = (qvalid && ((fl >> (8 * j)) & 0xFFu)) ? bv * kLog2e : kNegInf;
+    }
+  }
+  const float c1 = a.scale * kLog2e;
+  float dacc[8][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dacc[t][j] = 0.f;
+  u16* const mk = sK[wave];
+
+  for (int b = b0; b < b1; ++b) {
+    const size_t bh = (size_t)b * H + h;
+    const size_t base = bh * N * d;
+    const auto rq = make_rsrc(static_cast<const u16*>(a.q) + base, tb);
+    const auto rk = make_rsrc(static_cast<const u16*>(a.k) + base, tb);
+    const auto rv = make_rsrc(static_cast<const u16*>(a.v) + base, tb);
+    const auto rda = make_rsrc(static_cast<const u16*>(a.da) + base, tb);
+    const auto rdq = make_rsrc(static_cast<u16*>(a.dq) + base, tb);
+    u32x4 kv[8], av[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int c = lane + 64 * it, row = c >> 2, c8 = c & 3;
+      kv[it] = buf_load16(rk, key_off(key0 + row, 8 * c8));
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) av[t] = buf_load16(rv, key_off(key0 + slot_of(t, n), 8 * g));
+    const u32x4 bq = buf_load16(rq, key_off(query, 8 * g));
+    const u32x4 bda = buf_load16(rda, key_off(query, 8 * g));
+    const float2 sd = qvalid ? a.seed[bh * N + query] : make_float2(kNegInf, 0.f);
+    // the K window in LDS: operand rows for S^T and transposed reads for dQ
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int c = lane + 64 * it, row = c >> 2, c8 = c & 3;
+      *reinterpret_cast<u32x4*>(mk + row * kRS + 8 * c8) = kv[it];
+    }
+    f32x4 ds[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      const u32x4 akt = *reinterpret_cast<const u32x4*>(mk + slot_of(t, n) * kRS + 8 * g);
+      const f32x4 st = mfma32(as_bf8(akt), as_bf8(bq), f32x4{0.f, 0.f, 0.f, 0.f});
+      const f32x4 dp = mfma32(as_bf8(av[t]), as_bf8(bda), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float p = exp2_fast(fmaf(st[j], c1, b2[t][j]) + sd.x);
+        ds[t][j] = p * (dp[j] + sd.y);
+        dacc[t][j] += ds[t][j];
+      }
+    }
+    // dQ^T = K^T dS^T over the slots, k-step j = slots 32g + 8j .. +7
+    f32x4 dq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bf16x8 bds = pack8(ds[2 * j], ds[2 * j + 1]);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+        dq[ct] = mfma32(tr_frag<kRS>(mk, 32 * g + 8 * j, 32 * g + 8 * j + 4, 16 * ct, lane), bds, dq[ct]);
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      const f32x4 y = dq[ct] * a.scale;
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])}, rdq,
+                                            key_off(query, 16 * ct + 4 * g), 0, 0);
+    }
+  }
+  // partial of this chunk: row 16qt + n, slots 32g + 8c .. +7
+  float* const part = a.partial + (((size_t)chunk * H + h) * nqb + qb) * kLocalWq * kLocalWk +
+                      (size_t)(16 * qt + n) * kLocalWk + 32 * g;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    f32x4 v0, v1;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v0[e] = dacc[2 * c][e];
+      v1[e] = dacc[2 * c + 1][e];
+    }
+    *reinterpret_cast<f32x4*>(part + 8 * c) = v0;
+    *reinterpret_cast<f32x4*>(part + 8 * c + 4) = v1;
+  }
+}
+
+// ------------------------------------------------------------------ backward, dK and dV
+// Key tile m (keys 16m .. 16m+15) lies inside the windows of query blocks
+// ceil((m-4)/2) .. floor((m+3)/2); a workgroup takes key tiles 4w .. 4w+3 and
+// stages the rows of query blocks 2w - 2 .. 2w + 3 (192 queries).
+constexpr int kStageRows = 192;
+
+__global__ void __launch_bounds__(256) local_bwd_dkdv_kernel(LocalArgs a) {
+  __shared__ __attribute__((aligned(16))) u16 sQ[kStageRows * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sA[kStageRows * kRS];
+  __shared__ __attribute__((aligned(16))) float2 sSeed[kStageRows];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
+  const int N = a.N, d = a.d, nqb = a.nqb, H = a.H;
+  const int nkt = (N + 15) / 16;
+  const int nkg = (nkt + 3) / 4;
+  const int bh = blockIdx.x / nkg;
+  const int kg = blockIdx.x % nkg;
+  const int h = bh % H;
+  const size_t base = (size_t)bh * N * d;
+  const uint32_t tb = (uint32_t)N * d * 2u;
+  const auto rq = make_rsrc(static_cast<const u16*>(a.q) + base, tb);
+  const auto rk = make_rsrc(static_cast<const u16*>(a.k) + base, tb);
+  const auto rv = make_rsrc(static_cast<const u16*>(a.v) + base, tb);
+  const auto rda = make_rsrc(static_cast<const u16*>(a.da) + base, tb);
+  const auto rdk = make_rsrc(static_cast<u16*>(a.dk) + base, tb);
+  const auto rdv = make_rsrc(static_cast<u16*>(a.dv) + base, tb);
+  const auto rb = make_rsrc(a.bias, (uint32_t)H * nqb * kLocalWq * kLocalWk * 2u);
+  auto row_off = [&](int row, int c) -> uint32_t {
+    return (row >= 0 && row < N && c < d) ? (uint32_t)(row * d + c) * 2u : kOob;
+  };
+  const int qrow0 = 32 * (2 * kg - 2);  // first staged query row (may be negative)
+
+  // stage Q, dA rows and the seeds of the six query blocks (rows past either end are zero / -inf)
+#pragma unroll
+  for (int it = 0; it < 3; ++it) {
+    const int c = tid + 256 * it, row = c >> 2, c8 = c & 3;
+    const uint32_t off = row_off(qrow0 + row, 8 * c8);
+    *reinterpret_cast<u32x4*>(sQ + row * kRS + 8 * c8) = buf_load16(rq, off);
+    *reinterpret_cast<u32x4*>(sA + row * kRS + 8 * c8) = buf_load16(rda, off);
+  }
+  if (tid < kStageRows) {
+    const int row = qrow0 + tid;
+    sSeed[tid] = (row >= 0 && row < N) ? a.seed[(size_t)bh * N + row] : make_float2(kNegInf, 0.f);
+  }
+  __syncthreads();
+
+  const int m = 4 * kg + wave;  // this wave's key tile
+  if (m >= nkt) return;         // after the only barrier
+  const int key = 16 * m + n;
+  bool kok = key < N;
+  if (a.mask != nullptr && kok) kok = a.mask[key] != 0;
+  // K^T (scaled by log2(e)/sqrt(d)) and V^T operands: lane (g, n) holds row `key`, channels 8g .. 8g+7
+  const float c1 = a.scale * kLog2e;
+  u32x4 bk = buf_load16(rk, row_off(key, 8 * g));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) bk[e] = pack2(bf_lo(bk[e]) * c1, bf_hi(bk[e]) * c1);
+  const u32x4 bv = buf_load16(rv, row_off(key, 8 * g));
+  const bf16x8 id_hi = ident_cols_frag(lane, kLog2eHiBf16, 0);
+  const bf16x8 id_lo = ident_cols_frag(lane, kLog2eLoBf16, 0);
+
+  f32x4 dk[2], dv[2];
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    dk[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    dv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int qlo = std::max(0, (m - 3) / 2), qhi = std::min(nqb - 1, (m + 3) / 2);
+  for (int qb = qlo; qb <= qhi; ++qb) {
+    const int s0 = 16 * m - 32 * qb + kLocalOff;  // first slot of this key tile in qb's window
+    if (s0 < 0 || s0 + 16 > kLocalWk) continue;     // wave-uniform
+    const int lr = 32 * qb - qrow0;                 // staged row of the block's first query
+    f32x4 p[2], ds[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      // bias rows 16qt + i, slots s0 + 8(g & 1) .. +7 (lane groups 2-3 repeat them)
+      const u32x4 ab = buf_load16(
+          rb, (uint32_t)(((h * nqb + qb) * kLocalWq + 16 * qt + n) * kLocalWk + s0 + 8 * (g & 1)) * 2u);
+      const u32x4 aq = *reinterpret_cast<const u32x4*>(sQ + (lr + 16 * qt + n) * kRS + 8 * g);
+      const u32x4 ada = *reinterpret_cast<const u32x4*>(sA + (lr + 16 * qt + n) * kRS + 8 * g);
+      // S[query][key] in log2 units: (Q K^T) log2(e)/sqrt(d) + log2(e) bias
+      f32x4 st = mfma32(as_bf8(aq), as_bf8(bk), f32x4{0.f, 0.f, 0.f, 0.f});
+      st = mfma32(as_bf8(ab), id_hi, st);
+      st = mfma32(as_bf8(ab), id_lo, st);
+      const f32x4 dp = mfma32(as_bf8(ada), as_bf8(bv), f32x4{0.f, 0.f, 0.f, 0.f});
+      // lane (g, n) holds queries 16qt + 4g + r of the block
+      const f32x4 sA4 = *reinterpret_cast<const f32x4*>(&sSeed[lr + 16 * qt + 4 * g]);
+      const f32x4 sB4 = *reinterpret_cast<const f32x4*>(&sSeed[lr + 16 * qt + 4 * g + 2]);
+      const float sx[4] = {sA4[0], sA4[2], sB4[0], sB4[2]};
+      const float sy[4] = {sA4[1], sA4[3], sB4[1], sB4[3]};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float pr = kok ? exp2_fast(st[r] + sx[r]) : 0.f;
+        p[qt][r] = pr;
+        ds[qt][r] = pr * (dp[r] + sy[r]);
+      }
+    }
+    // dV^T += dA^T P, dK^T += Q^T dS over the block's 32 queries:
+    // k slot (g, v) = query 16(v / 4) + 4g + v % 4
+    const bf16x8 bp = pack8(p[0], p[1]);
+    const bf16x8 bs = pack8(ds[0], ds[1]);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      dv[ct] = mfma32(tr_frag<kRS>(sA, lr + 4 * g, lr + 16 + 4 * g, 16 * ct, lane), bp, dv[ct]);
+      dk[ct] = mfma32(tr_frag<kRS>(sQ, lr + 4 * g, lr + 16 + 4 * g, 16 * ct, lane), bs, dk[ct]);
+    }
+  }
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct) {
+    const uint32_t off = row_off(key, 16 * ct + 4 * g);
+    const f32x4 yk = dk[ct] * a.scale;
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(yk[0], yk[1]), pack2(yk[2], yk[3])}, rdk, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(dv[ct][0], dv[ct][1]), pack2(dv[ct][2], dv[ct][3])}, rdv, off,
+                                          0, 0);
+  }
+}
+
+// ------------------------------------------------------------------ plan + launch
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+LocalPlan plan_local_bwd(int B, int H, int N, int d) {
+  LocalPlan pl{};
+  const int nqb = (N + kLocalWq - 1) / kLocalWq;
+  // enough query-stationary waves to fill the chip (about 16 per CU), at
+  // most one chunk per batch row
+  const long long per_chunk = (long long)H * nqb * 2;
+  int P = (int)std::min<long long>(B, std::max<long long>(1, (4096 + per_chunk - 1) / per_chunk));
+  const int C = (B + P - 1) / P;
+  P = (B + C - 1) / C;
+  pl.P = P;
+  pl.C = C;
+  size_t off = 0;
+  pl.off_da = off;
+  off = align256(off + (size_t)B * H * N * d * 2);
+  pl.off_seed = off;
+  off = align256(off + (size_t)B * H * N * sizeof(float2));
+  pl.off_partial = off;
+  off = align256(off + (size_t)P * H * nqb * kLocalWq * kLocalWk * 4);
+  pl.total = off;
+  return pl;
+}
+
+hipError_t launch_local_fwd(const LocalArgs& a, hipStream_t stream, KernelTimer* timer) {
+  timer_start(timer, stream);
+  const unsigned grid = (unsigned)((size_t)a.B * a.H * ((a.nqb + 3) / 4));
+  hipLaunchKernelGGL(local_fwd_kernel, dim3(grid), dim3(256), 0, stream, a);
+  timer_mark(timer, stream);
+  return hipGetLastError();
+}
+
+hipError_t launch_local_bwd(const LocalArgs& a, hipStream_t stream, KernelTimer* timer) {
+  hipError_t e;
+  timer_start(timer, stream);
+  // 1. dA, dG and the row seeds: the dense path's preprocess (same layouts)
+  {
+    BwdArgs pa{};
+    pa.g = a.g;
+    pa.out = a.out;
+    pa.lse = a.lse;
+    pa.dout = a.dout;
+    pa.dg = a.dg;
+    pa.da = a.da;
+    pa.seed = a.seed;
+    pa.B = a.B;
+    pa.H = a.H;
+    pa.N = a.N;
+    pa.d = a.d;
+    if ((e = launch_attn_bwd_pre_bf16(pa, stream)) != hipSuccess) return e;
+    timer_mark(timer, stream);
+  }
+  // 2. dQ and the dbias partials
+  {
+    const size_t waves = (size_t)a.P * a.H * a.nqb * 2;
+    hipLaunchKernelGGL(local_bwd_dq_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark(timer, stream);
+  }
+  // 3. dK and dV
+  {
+    const int nkt = (a.N + 15) / 16;
+    const unsigned grid = (unsigned)((size_t)a.B * a.H * ((nkt + 3) / 4));
+    hipLaunchKernelGGL(local_bwd_dkdv_kernel, dim3(grid), dim3(256), 0, stream, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    timer_mark(timer, stream);
+  }
+  // 4. dbias = sum of the partials in chunk order
+  if ((e = launch_partial_sum_bf16(a.partial, a.P, (size_t)a.H * a.nqb * kLocalWq * kLocalWk, a.dbias, stream)) !=
+      hipSuccess)
+    return e;
+  timer_mark(timer, stream);
+  return hipSuccess;
+}
+
+}  // namespace pba

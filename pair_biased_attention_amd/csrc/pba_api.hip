@@ -10,7 +10,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr long long kMaxElems = (1LL << 31) - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -57,6 +57,17 @@ int check_proj_sizes(int N, int H, int c, int dtype) {
   if (N <= 0 || H <= 0 || c <= 0) return PBA_ERR_SHAPE;
   if (H > 16 || (c != 32 && c != 64 && c != 128)) return PBA_ERR_UNSUPPORTED;
   if ((long long)N * N * c > kMaxProjElems || (long long)N * N * H > kMaxProjElems) return PBA_ERR_SHAPE;
+  return PBA_OK;
+}
+
+// Windowed attention: bf16, d a multiple of 8 up to 32; every (b, h) slice
+// is addressed with 32-bit byte offsets.
+int check_local_sizes(int B, int H, int N, int d, int dtype) {
+  int st = check_dims(B, H, N, d, dtype, true);
+  if (st != PBA_OK) return st;
+  if (d > 32) return PBA_ERR_UNSUPPORTED;
+  const long long nqb = (N + 31) / 32;
+  if ((long long)H * nqb * 32 * 128 > kMaxElems / 2) return PBA_ERR_SHAPE;
   return PBA_OK;
 }
 
@@ -134,6 +145,53 @@ int prep_proj_bwd(int N, int H, int c, int dtype, const void* z, const float* ga
   a.dbias = dbias; a.dz = dz; a.dgamma = dgamma; a.dbeta = dbeta; a.dw = dw;
   a.partial = static_cast<float*>(workspace);
   a.nwg = pba::proj_bwd_workgroups(N, c);
+  return PBA_OK;
+}
+
+int prep_local(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+               const void* g, const void* bias, const uint8_t* key_mask, pba::LocalArgs& a) {
+  int st = check_local_sizes(B, H, N, d, dtype);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({q, k, v, g, bias})) != PBA_OK) return st;
+  if ((st = all_aligned16({q, k, v, g, bias})) != PBA_OK) return st;
+  a.q = q; a.k = k; a.v = v; a.g = g; a.bias = bias; a.mask = key_mask;
+  a.B = B; a.H = H; a.N = N; a.d = d;
+  a.nqb = (N + pba::kLocalWq - 1) / pba::kLocalWq;
+  a.scale = attn_scale(d);
+  return PBA_OK;
+}
+
+int prep_local_fwd(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                   const void* g, const void* bias, const uint8_t* key_mask, void* out, float* lse,
+                   pba::LocalArgs& a) {
+  int st = prep_local(B, H, N, d, dtype, q, k, v, g, bias, key_mask, a);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({out, lse})) != PBA_OK) return st;
+  if (!aligned16(out)) return PBA_ERR_ALIGN;
+  if (!aligned4(lse)) return PBA_ERR_ALIGN;
+  a.out = out; a.lse = lse;
+  return PBA_OK;
+}
+
+int prep_local_bwd(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                   const void* g, const void* bias, const uint8_t* key_mask, const void* out, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, void* dg, void* dbias, void* workspace,
+                   size_t workspace_bytes, pba::LocalArgs& a) {
+  int st = prep_local(B, H, N, d, dtype, q, k, v, g, bias, key_mask, a);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({out, lse, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
+  if ((st = all_aligned16({out, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
+  if (!aligned4(lse)) return PBA_ERR_ALIGN;
+  const pba::LocalPlan pl = pba::plan_local_bwd(B, H, N, d);
+  if (workspace == nullptr || workspace_bytes < pl.total) return PBA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return PBA_ERR_ALIGN;
+  char* ws = static_cast<char*>(workspace);
+  a.out = const_cast<void*>(out); a.lse = const_cast<float*>(lse); a.dout = dout;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbias = dbias;
+  a.da = ws + pl.off_da;
+  a.seed = reinterpret_cast<float2*>(ws + pl.off_seed);
+  a.partial = reinterpret_cast<float*>(ws + pl.off_partial);
+  a.P = pl.P; a.C = pl.C;
   return PBA_OK;
 }
 
@@ -368,6 +426,56 @@ int pba_bias_proj_backward_timed(int N, int H, int c, int dtype, const void* z, 
                                workspace_bytes, a);
   if (st != PBA_OK) return st;
   return run_timed([&](pba::KernelTimer* t, hipStream_t s) { return pba::launch_proj_bwd(a, s, t); },
+                   static_cast<hipStream_t>(stream), kernel_ms, capacity, n_kernels);
+}
+
+int pba_local_forward(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                      const void* g, const void* bias, const uint8_t* key_mask, void* out, float* lse,
+                      void* stream) {
+  pba::LocalArgs a{};
+  const int st = prep_local_fwd(B, H, N, d, dtype, q, k, v, g, bias, key_mask, out, lse, a);
+  if (st != PBA_OK) return st;
+  const hipError_t e = pba::launch_local_fwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+int pba_local_forward_timed(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                            const void* g, const void* bias, const uint8_t* key_mask, void* out, float* lse,
+                            void* stream, float* kernel_ms, int capacity, int* n_kernels) {
+  pba::LocalArgs a{};
+  const int st = prep_local_fwd(B, H, N, d, dtype, q, k, v, g, bias, key_mask, out, lse, a);
+  if (st != PBA_OK) return st;
+  return run_timed([&](pba::KernelTimer* t, hipStream_t s) { return pba::launch_local_fwd(a, s, t); },
+                   static_cast<hipStream_t>(stream), kernel_ms, capacity, n_kernels);
+}
+
+size_t pba_local_backward_workspace_bytes(int B, int H, int N, int d, int dtype) {
+  if (check_local_sizes(B, H, N, d, dtype) != PBA_OK) return 0;
+  return pba::plan_local_bwd(B, H, N, d).total;
+}
+
+int pba_local_backward(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                       const void* g, const void* bias, const uint8_t* key_mask, const void* out, const float* lse,
+                       const void* dout, void* dq, void* dk, void* dv, void* dg, void* dbias, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  pba::LocalArgs a{};
+  const int st = prep_local_bwd(B, H, N, d, dtype, q, k, v, g, bias, key_mask, out, lse, dout, dq, dk, dv, dg,
+                                dbias, workspace, workspace_bytes, a);
+  if (st != PBA_OK) return st;
+  const hipError_t e = pba::launch_local_bwd(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+int pba_local_backward_timed(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                             const void* g, const void* bias, const uint8_t* key_mask, const void* out,
+                             const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dg, void* dbias,
+                             void* workspace, size_t workspace_bytes, void* stream, float* kernel_ms, int capacity,
+                             int* n_kernels) {
+  pba::LocalArgs a{};
+  const int st = prep_local_bwd(B, H, N, d, dtype, q, k, v, g, bias, key_mask, out, lse, dout, dq, dk, dv, dg,
+                                dbias, workspace, workspace_bytes, a);
+  if (st != PBA_OK) return st;
+  return run_timed([&](pba::KernelTimer* t, hipStream_t s) { return pba::launch_local_bwd(a, s, t); },
                    static_cast<hipStream_t>(stream), kernel_ms, capacity, n_kernels);
 }
 

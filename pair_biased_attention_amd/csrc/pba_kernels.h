@@ -95,6 +95,37 @@ constexpr int proj_bwd_waves(int c) { return c >= 128 ? 8 : 16; }
 int proj_bwd_workgroups(int N, int c);
 size_t proj_bwd_workspace_bytes(int N, int c);
 
+// Windowed (sequence-local) attention: query block q (32 queries) attends
+// the 128 keys 32q - 48 .. 32q + 79; bias and dbias are [H, nqb, 32, 128].
+constexpr int kLocalWq = 32, kLocalWk = 128, kLocalOff = 48;
+struct LocalArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* g;
+  const void* bias;
+  const uint8_t* mask;
+  void* out;
+  float* lse;
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  void* dg;
+  void* dbias;
+  void* da;         // workspace: dA [B,H,N,d] bf16
+  float2* seed;     // workspace: (-log2(e) * LSE, -D) per query row [B,H,N]
+  float* partial;   // workspace: dbias partial sums [P, H, nqb, 32, 128] fp32
+  int B, H, N, d, nqb;
+  float scale;
+  int P, C;         // backward: batch chunks and batch rows per chunk
+};
+struct LocalPlan {
+  size_t off_da, off_seed, off_partial, total;
+  int P, C;
+};
+LocalPlan plan_local_bwd(int B, int H, int N, int d);
+
 // Workspace plan of the attention backward (byte offsets into one buffer).
 struct BwdPlan {
   size_t off_da, off_drow, off_partial, total;
@@ -130,5 +161,9 @@ hipError_t launch_pwa_fwd(const PwaArgs& a, bool bf16, hipStream_t stream, Kerne
 hipError_t launch_pwa_bwd(const PwaArgs& a, bool bf16, hipStream_t stream, KernelTimer* timer = nullptr);
 hipError_t launch_proj_fwd(const ProjArgs& a, hipStream_t stream, KernelTimer* timer = nullptr);
 hipError_t launch_proj_bwd(const ProjArgs& a, hipStream_t stream, KernelTimer* timer = nullptr);
+hipError_t launch_local_fwd(const LocalArgs& a, hipStream_t stream, KernelTimer* timer = nullptr);
+hipError_t launch_local_bwd(const LocalArgs& a, hipStream_t stream, KernelTimer* timer = nullptr);
+hipError_t launch_attn_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_partial_sum_bf16(const float* partial, int P, size_t count, void* out, hipStream_t stream);
 
 }  // namespace pba

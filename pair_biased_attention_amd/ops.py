@@ -4,6 +4,7 @@ PyTorch supplies device memory and the current HIP stream; every step of the
 computation runs in libpba's kernels.  Layouts (contiguous, row-major):
   attention  q, k, v, g, out, dout, dq, dk, dv, dg: [B, H, N, d]; bias, dbias: [H, N, N]
   pair-bias projection  z, dz: [N, N, c] bf16; gamma, beta: [c], w: [H, c] float32; bias: [H, N, N]
+  windowed attention  q, k, v, g, out, ...: [B, H, N, d]; bias, dbias: [H, ceil(N/32), 32, 128]
   pair-weighted average  v, g, out, dout, dv, dg: [S, N, H, d]; b, db: [H, N, N]
   key_mask: [N] uint8 (0 = masked) or None.
 """
@@ -189,6 +190,50 @@ def pba_bias_proj_backward(z, gamma, beta, w, dbias, eps=1e-5, workspace=None):
     return {"dz": dz, "dgamma": dgamma, "dbeta": dbeta, "dw": dw}
 
 
+def local_bias_shape(H, N):
+    """Shape of the windowed attention's bias: [H, ceil(N/32), 32, 128]."""
+    return (H, (N + 31) // 32, 32, 128)
+
+
+def pba_local_forward(q, k, v, g, bias, key_mask=None):
+    """Windowed pair-biased gated attention forward (bf16, d <= 32); returns (out, lse)."""
+    lib = _lib.load()
+    B, H, N, d = q.shape
+    shp = {"q": (B, H, N, d), "k": (B, H, N, d), "v": (B, H, N, d), "g": (B, H, N, d),
+           "bias": local_bias_shape(H, N), "key_mask": (N,)}
+    _check_tensors(q, dict(q=q, k=k, v=v, g=g, bias=bias, key_mask=key_mask), shp)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    st = lib.pba_local_forward(B, H, N, d, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bias),
+                               _ptr(key_mask), _ptr(out), _ptr(lse), _stream(q.device))
+    _lib.check("pba_local_forward", st)
+    return out, lse
+
+
+def pba_local_backward_workspace_bytes(B, H, N, d, dtype=torch.bfloat16) -> int:
+    return int(_lib.load().pba_local_backward_workspace_bytes(B, H, N, d, _DT[dtype]))
+
+
+def pba_local_backward(q, k, v, g, bias, key_mask, out, lse, dout, workspace=None):
+    """Backward of pba_local_forward; returns dict(dq, dk, dv, dg, dbias), dbias summed over B."""
+    lib = _lib.load()
+    B, H, N, d = q.shape
+    shp = {n: (B, H, N, d) for n in ("q", "k", "v", "g", "out", "dout")}
+    shp.update(bias=local_bias_shape(H, N), key_mask=(N,), lse=(B, H, N))
+    _check_tensors(q, dict(q=q, k=k, v=v, g=g, bias=bias, key_mask=key_mask, out=out, lse=lse,
+                           dout=dout), shp)
+    nbytes = lib.pba_local_backward_workspace_bytes(B, H, N, d, _DT[q.dtype])
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    dq, dk, dv, dg = (torch.empty_like(q) for _ in range(4))
+    dbias = torch.empty_like(bias)
+    st = lib.pba_local_backward(B, H, N, d, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bias),
+                                _ptr(key_mask), _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv),
+                                _ptr(dg), _ptr(dbias), _ptr(workspace), workspace.numel(), _stream(q.device))
+    _lib.check("pba_local_backward", st)
+    return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dbias": dbias}
+
+
 # ---- measurement entry points (create HIP events and synchronise) ----------
 
 def _timed_call(fn_name, args):
@@ -244,3 +289,20 @@ def pba_bias_proj_backward_timed(z, gamma, beta, w, dbias, eps, workspace, grads
         N, H, c, _lib.PBA_BF16, _ptr(z), _ptr(gamma), _ptr(beta), _ptr(w), float(eps), _ptr(dbias),
         _ptr(grads["dz"]), _ptr(grads["dgamma"]), _ptr(grads["dbeta"]), _ptr(grads["dw"]), _ptr(workspace),
         workspace.numel(), _stream(z.device)])
+
+
+def pba_local_forward_timed(q, k, v, g, bias, key_mask, out, lse):
+    """pba_local_forward into preallocated out / lse; returns per-kernel ms."""
+    B, H, N, d = q.shape
+    return _timed_call("pba_local_forward_timed", [
+        B, H, N, d, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bias), _ptr(key_mask), _ptr(out),
+        _ptr(lse), _stream(q.device)])
+
+
+def pba_local_backward_timed(q, k, v, g, bias, key_mask, out, lse, dout, workspace, grads):
+    """pba_local_backward into preallocated `grads` (dq, dk, dv, dg, dbias); returns per-kernel ms."""
+    B, H, N, d = q.shape
+    return _timed_call("pba_local_backward_timed", [
+        B, H, N, d, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bias), _ptr(key_mask), _ptr(out),
+        _ptr(lse), _ptr(dout), _ptr(grads["dq"]), _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]),
+        _ptr(grads["dbias"]), _ptr(workspace), workspace.numel(), _stream(q.device)])

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     for fn in ("pba_forward", "pba_backward", "pba_backward_workspace_bytes", "pair_weighted_avg",
                "pair_weighted_avg_backward", "pair_weighted_avg_workspace_bytes",
                "pair_weighted_avg_backward_workspace_bytes", "pba_status_string", "pba_abi_version",
-               "pba_bias_proj_forward", "pba_bias_proj_backward", "pba_bias_proj_backward_workspace_bytes"):
+               "pba_bias_proj_forward", "pba_bias_proj_backward", "pba_bias_proj_backward_workspace_bytes",
+               "pba_local_forward", "pba_local_backward", "pba_local_backward_workspace_bytes"):
         assert fn in names, fn
     assert set(names) == set(_lib.SIGNATURES), (names, sorted(_lib.SIGNATURES))
 
@@ -45,7 +46,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pba_abi_version() == 2
+    assert lib.pba_abi_version() == 3
     for code in range(7):
         assert lib.pba_status_string(code)
     assert b"unknown" in lib.pba_status_string(99)
@@ -223,6 +224,42 @@ def test_bias_proj_validation(lib):
     mb = lambda ws=FAKE, m=FAKE: lib.pba_bias_proj_backward_timed(
         N, H, c, 1, FAKE, FAKE, FAKE, FAKE, 1e-5, FAKE, FAKE, FAKE, FAKE, FAKE, ws, need, None, m, 2, FAKE)
     assert mb(ws=None) == ERR_WS and mb(m=None) == ERR_NULL
+
+
+def test_local_attention_validation(lib):
+    B, H, N, d = 2, 2, 100, 32
+    need = lib.pba_local_backward_workspace_bytes(B, H, N, d, 1)
+    assert need >= B * H * N * d * 2 + B * H * N * 8 + H * 4 * 32 * 128 * 4
+    assert lib.pba_local_backward_workspace_bytes(B, H, N, 40, 1) == 0   # d <= 32
+    assert lib.pba_local_backward_workspace_bytes(B, H, N, d, 0) == 0    # bf16 only
+    assert lib.pba_local_backward_workspace_bytes(B, H, N, 12, 1) == 0   # multiple of 8
+
+    def f(dt=1, d_=d, p=None):
+        q, k, v, g, bias, out, lse = p or [FAKE] * 7
+        return lib.pba_local_forward(B, H, N, d_, dt, q, k, v, g, bias, None, out, lse, None)
+
+    assert f(dt=0) == ERR_UNSUP and f(d_=64) == ERR_UNSUP
+    for i in range(7):
+        p = [FAKE] * 7
+        p[i] = None
+        assert f(p=p) == ERR_NULL, i
+    p = [FAKE] * 7
+    p[4] = FAKE + 8
+    assert f(p=p) == ERR_ALIGN
+
+    def b(ws=FAKE, wsb=need, null_at=None):
+        p = [FAKE] * 13
+        if null_at is not None:
+            p[null_at] = None
+        return lib.pba_local_backward(B, H, N, d, 1, p[0], p[1], p[2], p[3], p[4], None, p[5], p[6], p[7],
+                                      p[8], p[9], p[10], p[11], p[12], ws, wsb, None)
+
+    for i in range(13):
+        assert b(null_at=i) == ERR_NULL, i
+    assert b(ws=None) == ERR_WS and b(wsb=need - 1) == ERR_WS and b(ws=FAKE + 8) == ERR_ALIGN
+    tb = lambda m=FAKE: lib.pba_local_backward_timed(B, H, N, d, 1, *([FAKE] * 5), None, *([FAKE] * 8), FAKE,
+                                                    need, None, m, 4, FAKE)
+    assert tb(m=None) == ERR_NULL
 
 
 def test_binding_rejects_cpu_tensors():

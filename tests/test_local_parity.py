@@ -1,0 +1,171 @@
+"""GPU parity of the windowed (sequence-local) attention against the fp64
+oracle in ``oracle/local_attn_oracle.py``, through the C ABI.
+
+Bar: per output tensor, max |gpu - oracle| <= 2e-2 * max |oracle| (bf16
+inputs, fp32 accumulation); as in the dense tests, dq, dk and dbias are taken
+relative to max |dv| because D = rowsum(dO * O) is formed from the bf16 O.
+Masked keys get exactly zero dk/dv rows and rows without usable keys exactly
+zero output.  Every element is compared, the full workload included: the
+oracle handles B=48, N=3072 in seconds because every window is small.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import TOL, check_all, log, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import pair_biased_attention_amd._lib as L
+    L.load()  # fails loudly if the library is missing
+
+
+import pair_biased_attention_amd as pba  # noqa: E402
+
+
+def _run(inp):
+    t = {n: to_dev(inp[n], "bf16") for n in ("q", "k", "v", "g", "bias", "dout")}
+    km = None if inp["key_mask"] is None else to_dev(inp["key_mask"], "bf16")
+    out, lse = pba.pba_local_forward(t["q"], t["k"], t["v"], t["g"], t["bias"], km)
+    gr = pba.pba_local_backward(t["q"], t["k"], t["v"], t["g"], t["bias"], km, out, lse, t["dout"])
+    torch.cuda.synchronize()
+    res = {"out": to_f64(out), "lse": lse.cpu().numpy().astype(np.float64)}
+    res.update({k: to_f64(v) for k, v in gr.items()})
+    return res
+
+
+def _check(inp, res, tag):
+    args = (inp["q64"], inp["k64"], inp["v64"], inp["g64"], inp["bias64"])
+    O, L = oracle.local_attention_forward(*args, inp["key_mask"])
+    gr = oracle.local_attention_backward(*args, inp["key_mask"], inp["dout64"])
+    floor = float(np.max(np.abs(gr["dv"])))
+    pairs = {"out": (res["out"], O), "lse": (res["lse"], L)}
+    pairs.update({n: (res[n], gr[n]) for n in ("dq", "dk", "dv", "dg", "dbias")})
+    check_all(tag, pairs, TOL["bf16"], {"dq": floor, "dk": floor, "dbias": floor})
+    if inp["key_mask"] is not None:
+        dead = inp["key_mask"] == 0
+        assert np.all(res["dk"][:, :, dead] == 0) and np.all(res["dv"][:, :, dead] == 0)
+    return gr
+
+
+SMALL = [
+    # B, H, N, d, mask
+    (2, 2, 100, 32, "tail:7"),      # ragged last block, masked tail
+    (3, 1, 64, 16, "random:5"),     # two blocks: every window covers every key
+    (1, 2, 33, 8, "none"),          # a one-query last block
+    (2, 2, 257, 24, "random:20"),   # d padded 24 -> 32, key tiles in several workgroups
+    (20, 4, 1100, 32, "none"),      # two batch rows per dbias chunk (10 chunks)
+    (1, 1, 20, 32, "none"),         # fewer keys than one key tile group
+    (2, 2, 300, 32, "tail:40"),     # the last windows mostly masked
+]
+
+
+@pytest.mark.parametrize("B,H,N,d,mask", SMALL)
+def test_local_small(B, H, N, d, mask):
+    log(f"windowed attention small B={B} H={H} N={N} d={d} mask={mask}")
+    cfg = workloads.LocalConfig("case", B=B, H=H, N=N, d=d, mask=mask, seed=500 + N + d)
+    inp = workloads.local_inputs(cfg)
+    _check(inp, _run(inp), f"local[{B},{H},{N},{d}]")
+
+
+def test_local_workload():
+    cfg = workloads.CONFIGS["local_atom_attn"]
+    log(f"windowed attention workload: B={cfg.B} H={cfg.H} N={cfg.N} d={cfg.d} mask={cfg.mask}")
+    inp = workloads.local_inputs(cfg)
+    _check(inp, _run(inp), "local_atom_attn")
+
+
+def test_local_rows_without_keys():
+    """Block 0's window (atoms -48..79) holds no usable key: its rows give
+    out = 0, lse = -inf and zero gradients; the other blocks are unaffected."""
+    log("windowed attention rows without keys")
+    cfg = workloads.LocalConfig("nokeys", B=2, H=2, N=160, d=32, mask="none", seed=77)
+    inp = workloads.local_inputs(cfg)
+    keep = np.ones(160, dtype=np.uint8)
+    keep[:80] = 0
+    inp["key_mask"] = keep
+    res = _run(inp)
+    _check(inp, res, "local[nokeys]")
+    assert np.all(res["out"][:, :, :32] == 0) and np.all(np.isneginf(res["lse"][:, :, :32]))
+    assert np.all(res["dq"][:, :, :32] == 0) and np.all(res["dbias"][:, 0] == 0)
+
+
+def test_local_matches_dense_kernel_when_windows_cover_everything():
+    """N <= 64: every window covers every key, so the windowed kernels and the
+    dense kernels (given the same bias laid out densely) agree."""
+    log("windowed vs dense kernels")
+    cfg = workloads.LocalConfig("cover", B=3, H=2, N=60, d=32, mask="random:4", seed=31)
+    inp = workloads.local_inputs(cfg)
+    res = _run(inp)
+    N = cfg.N
+    dense = np.zeros((cfg.H, N, N), dtype=np.uint16)
+    for i in range(N):
+        qb = i // 32
+        dense[:, i, :] = inp["bias"][:, qb, i - 32 * qb, 48 - 32 * qb:48 - 32 * qb + N]
+    t = {n: to_dev(inp[n], "bf16") for n in ("q", "k", "v", "g", "dout")}
+    db = to_dev(dense, "bf16")
+    km = to_dev(inp["key_mask"], "bf16")
+    out, lse = pba.pba_forward(t["q"], t["k"], t["v"], t["g"], db, km)
+    gr = pba.pba_backward(t["q"], t["k"], t["v"], t["g"], db, km, out, lse, t["dout"])
+    torch.cuda.synchronize()
+    floor = float(np.max(np.abs(res["dv"])))
+    pairs = {"out": (res["out"], to_f64(out)), "dv": (res["dv"], to_f64(gr["dv"])),
+             "dq": (res["dq"], to_f64(gr["dq"])), "dk": (res["dk"], to_f64(gr["dk"]))}
+    check_all("local vs dense", pairs, TOL["bf16"], {"dq": floor, "dk": floor})
+
+
+def test_local_backward_is_bitwise_deterministic():
+    log("windowed attention determinism")
+    cfg = workloads.LocalConfig("det", B=6, H=2, N=300, d=32, mask="tail:9", seed=41)
+    inp = workloads.local_inputs(cfg)
+    a, b = _run(inp), _run(inp)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_local_outputs_stay_inside_their_buffers():
+    """Every output inside a larger buffer filled with a sentinel, at a ragged size."""
+    log("windowed attention output bounds")
+    lib = pba._lib.load()
+    B, H, N, d = 2, 2, 77, 24
+    cfg = workloads.LocalConfig("bounds", B=B, H=H, N=N, d=d, mask="tail:3", seed=12)
+    inp = workloads.local_inputs(cfg)
+    t = {n: to_dev(inp[n], "bf16") for n in ("q", "k", "v", "g", "bias", "dout")}
+    km = to_dev(inp["key_mask"], "bf16")
+    pad = 4096
+    sent = -12345
+    T = B * H * N * d
+    nb = t["bias"].numel()
+    bufs = {n: torch.full((pad + T + pad,), sent, dtype=torch.int16, device="cuda")
+            for n in ("out", "dq", "dk", "dv", "dg")}
+    bufs["dbias"] = torch.full((pad + nb + pad,), sent, dtype=torch.int16, device="cuda")
+    lse = torch.full((pad + B * H * N + pad,), -7.0, dtype=torch.float32, device="cuda")
+    P = {n: b.data_ptr() + 2 * pad for n, b in bufs.items()}
+    plse = lse.data_ptr() + 4 * pad
+    assert lib.pba_local_forward(B, H, N, d, 1, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                 t["g"].data_ptr(), t["bias"].data_ptr(), km.data_ptr(), P["out"], plse, None) == 0
+    ws = torch.empty(lib.pba_local_backward_workspace_bytes(B, H, N, d, 1), dtype=torch.uint8, device="cuda")
+    assert lib.pba_local_backward(B, H, N, d, 1, t["q"].data_ptr(), t["k"].data_ptr(), t["v"].data_ptr(),
+                                  t["g"].data_ptr(), t["bias"].data_ptr(), km.data_ptr(), P["out"], plse,
+                                  t["dout"].data_ptr(), P["dq"], P["dk"], P["dv"], P["dg"], P["dbias"],
+                                  ws.data_ptr(), ws.numel(), None) == 0
+    torch.cuda.synchronize()
+    for n, b in bufs.items():
+        m = nb if n == "dbias" else T
+        assert bool((b[:pad] == sent).all()) and bool((b[pad + m:] == sent).all()), n
+    assert bool((lse[:pad] == -7.0).all()) and bool((lse[pad + B * H * N:] == -7.0).all())
+    res = {n: to_f64(bufs[n][pad:pad + T].view(torch.bfloat16).view(B, H, N, d))
+           for n in ("out", "dq", "dk", "dv", "dg")}
+    res["dbias"] = to_f64(bufs["dbias"][pad:pad + nb].view(torch.bfloat16).view(*t["bias"].shape))
+    res["lse"] = lse[pad:pad + B * H * N].view(B, H, N).cpu().numpy().astype(np.float64)
+    _check(inp, res, "local[bounds]")

@@ -402,6 +402,14 @@ def test_workload_recipe_matches_fixture():
         assert cfg.kind == "bias_proj", name
         for key, val in spec["shape"].items():
             assert getattr(cfg, key) == val, (name, key)
+    for name, spec in fixture["local_configs"].items():
+        cfg = workloads.CONFIGS[name]
+        assert cfg.kind == "local_attention" and cfg.mask == spec["mask"], name
+        for key, val in spec["shape"].items():
+            assert getattr(cfg, key) == val, (name, key)
+    lin = workloads.local_inputs(workloads.LocalConfig("small", B=2, H=3, N=70, d=8, mask="tail:5", seed=6))
+    assert lin["bias"].shape == (3, 3, 32, 128) and lin["q"].shape == (2, 3, 70, 8)
+    assert np.all(lin["key_mask"][65:] == 0) and np.all(lin["key_mask"][:65] == 1)
     small = workloads.ProjConfig("small", N=6, H=3, c=32, seed=5)
     pin = workloads.bias_proj_inputs(small)
     assert pin["z"].shape == (6, 6, 32) and pin["z"].dtype == np.uint16

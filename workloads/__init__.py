@@ -25,6 +25,12 @@ Workloads (all values standard normal, as the task's configurations state):
                        H=4 heads.
 * ``bias_proj_pairformer`` the same projection for the Pairformer pair bias:
                        z [768, 768, c=128] bf16, H=16 heads.
+* ``local_atom_attn``  windowed (sequence-local) atom attention with pair
+                       bias: B=48 diffusion copies, N=3072 atoms (384 tokens at
+                       8 atoms each), H=4, d=32, bf16, blocks of 32 queries
+                       each attending 128 keys, local bias [4, 96, 32, 128],
+                       last 5 % of atoms masked (154 of 3072).
+  Windowed-attention draw order: Q, K, V, G, bias, dO, then the mask.
   Projection inputs: z = standard normal plus a standard-normal shift per
   pair position (so that the LayerNorm has a mean to remove), rounded to
   bf16; gamma = 1 + 0.25 N(0,1), beta = 0.25 N(0,1) and w = N(0,1)/sqrt(c)
@@ -49,9 +55,9 @@ import dataclasses
 import numpy as np
 
 __all__ = [
-    "AttnConfig", "PwaConfig", "ProjConfig", "CONFIGS", "ATTN_CONFIGS", "PWA_CONFIGS", "PROJ_CONFIGS",
+    "AttnConfig", "PwaConfig", "ProjConfig", "LocalConfig", "CONFIGS", "ATTN_CONFIGS", "PWA_CONFIGS", "PROJ_CONFIGS", "LOCAL_CONFIGS",
     "bf16_round_bits", "bf16_bits_to_f32", "attention_inputs", "pwa_inputs",
-    "scaled_attention_config", "scaled_pwa_config", "bias_proj_inputs",
+    "scaled_attention_config", "scaled_pwa_config", "bias_proj_inputs", "local_inputs",
 ]
 
 
@@ -100,6 +106,22 @@ class ProjConfig:
         return "bias_proj"
 
 
+@dataclasses.dataclass(frozen=True)
+class LocalConfig:
+    name: str
+    B: int
+    H: int
+    N: int
+    d: int
+    mask: str
+    seed: int
+    dtype: str = "bf16"
+
+    @property
+    def kind(self) -> str:
+        return "local_attention"
+
+
 CONFIGS = {
     "tiny_fp32": AttnConfig("tiny_fp32", B=32, H=4, N=32, d=32, dtype="f32",
                             mask="random:3", seed=1001),
@@ -115,10 +137,12 @@ CONFIGS = {
                                mask="tail:38", seed=1006),
     "bias_proj_tri_n384": ProjConfig("bias_proj_tri_n384", N=384, H=4, c=128, seed=1007),
     "bias_proj_pairformer": ProjConfig("bias_proj_pairformer", N=768, H=16, c=128, seed=1008),
+    "local_atom_attn": LocalConfig("local_atom_attn", B=48, H=4, N=3072, d=32, mask="tail:154", seed=1009),
 }
 ATTN_CONFIGS = [c for c in CONFIGS.values() if c.kind == "attention"]
 PWA_CONFIGS = [c for c in CONFIGS.values() if c.kind == "pwa"]
 PROJ_CONFIGS = [c for c in CONFIGS.values() if c.kind == "bias_proj"]
+LOCAL_CONFIGS = [c for c in CONFIGS.values() if c.kind == "local_attention"]
 
 
 def scaled_attention_config(cfg: AttnConfig, **overrides) -> AttnConfig:
@@ -235,4 +259,23 @@ def bias_proj_inputs(cfg: ProjConfig, seed: int | None = None, with_f64: bool = 
     out["beta"], out["beta64"] = _store(0.25 * rng.standard_normal(c), "f32")
     out["w"], out["w64"] = _store(rng.standard_normal((H, c)) / np.sqrt(c), "f32")
     out["dbias"], out["dbias64"] = _store(rng.standard_normal((H, N, N), dtype=np.float32), "bf16", with_f64)
+    return out
+
+
+def local_inputs(cfg: LocalConfig, seed: int | None = None, with_grad: bool = True, with_f64: bool = True):
+    """Draw one windowed-attention workload.
+
+    Layouts: q, k, v, g, dout [B, H, N, d]; bias [H, ceil(N/32), 32, 128]
+    (head, query block, query in block, window slot); key_mask [N] or None.
+    """
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    B, H, N, d = cfg.B, cfg.H, cfg.N, cfg.d
+    out = {"cfg": cfg}
+    names = ["q", "k", "v", "g", "bias"] + (["dout"] if with_grad else [])
+    for name in names:
+        shape = (H, -(-N // 32), 32, 128) if name == "bias" else (B, H, N, d)
+        x = rng.standard_normal(shape, dtype=np.float32)
+        out[name], out[name + "64"] = _store(x, cfg.dtype, with_f64)
+        del x
+    out["key_mask"] = _key_mask(cfg.mask, N, rng)
     return out
