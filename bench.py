@@ -189,7 +189,7 @@ KERNEL_SOURCES = {
     "local_fwd": ("local_fwd_kernel", "local_attn.hip"),
     "local_bwd_dq": ("local_bwd_dq_kernel", "local_attn.hip"),
     "local_bwd_dkdv": ("local_bwd_dkdv_kernel", "local_attn.hip"),
-    "bias_proj_bwd": ("bias_proj_bwd_kernel<4>", "bias_proj.hip"),
+    "bias_proj_bwd": ("bias_proj_bwd_kernel<4, true>", "bias_proj.hip"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
@@ -299,6 +299,17 @@ def counters_pass(args, torch, pba):
         pba.pba_bias_proj_backward(z, prm["gamma"], prm["beta"], prm["w"], dbias, 1e-5)
     torch.cuda.synchronize()
     print(f"projection steps done: {args.pwa_steps}", flush=True)
+    del z, dbias, prm
+    lc = workloads.CONFIGS["local_atom_attn"]
+    lin = workloads.local_inputs(lc, with_f64=False)
+    lt = {n: to_dev(lin[n], torch) for n in ("q", "k", "v", "g", "bias", "dout")}
+    lkm = to_dev(lin["key_mask"], torch)
+    del lin
+    for _ in range(args.pwa_steps):
+        o, l = pba.pba_local_forward(lt["q"], lt["k"], lt["v"], lt["g"], lt["bias"], lkm)
+        pba.pba_local_backward(lt["q"], lt["k"], lt["v"], lt["g"], lt["bias"], lkm, o, l, lt["dout"])
+    torch.cuda.synchronize()
+    print(f"windowed attention steps done: {args.pwa_steps}", flush=True)
 
 
 def bench_proj(args, torch, pba):
@@ -433,7 +444,8 @@ def main():
                     help="turn a FETCH_SIZE and a WRITE_SIZE pass of --counters into profiles/traffic.json")
     ap.add_argument("--counters", action="store_true",
                     help="hardware-counter pass: a 256 MiB device copy (calibration kernel of known size), then "
-                         "--steps attention steps and --pwa-steps pair-average steps; no timing, no JSON line")
+                         "--steps attention steps and --pwa-steps steps of the pair average, the projection and "
+                         "the windowed attention; no timing, no JSON line")
     args = ap.parse_args()
     if args.traffic_from:
         return traffic_from(*args.traffic_from)
