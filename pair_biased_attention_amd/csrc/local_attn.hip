@@ -22,12 +22,12 @@
 //    batch chunk) walks the chunk's batch rows in order, recomputes P,
 //    forms dS and dQ = dS K and accumulates dS in registers: one dbias
 //    partial per chunk, summed over chunks in a fixed order afterwards.
-//  * backward, key-stationary: one wave per (b, h, 16-key tile).  Each key
-//    tile lies wholly inside the windows of exactly four query blocks (the
-//    windows are 16-aligned); the workgroup stages the Q, dA rows and seeds of
-//    the six query blocks its four key tiles need, and each wave forms
-//    S = Q K^T (bias added on the matrix core by identity products), P, dP,
-//    dS and accumulates dV = P^T dA and dK = dS^T Q.  No atomics anywhere.
+//  * backward, key-stationary: one wave per 16-key tile.  Each key tile lies
+//    wholly inside the windows of exactly four query blocks (the windows are
+//    16-aligned).  A workgroup walks consecutive groups of four key tiles
+//    with a ring of query blocks in LDS; each wave forms S = Q K^T (bias
+//    added on the matrix core by identity products), P, dP, dS and
+//    accumulates dV = P^T dA and dK = dS^T Q.  No atomics anywhere.
 #include <algorithm>
 
 #include "pba.h"
@@ -326,21 +326,28 @@ __global__ void __launch_bounds__(256) local_bwd_dq_kernel(LocalArgs a) {
 }
 
 // ------------------------------------------------------------------ backward, dK and dV
-// Key tile m (keys 16m .. 16m+15) lies inside the windows of query blocks
-// ceil((m-4)/2) .. floor((m+3)/2); a workgroup takes key tiles 4w .. 4w+3 and
-// stages the rows of query blocks 2w - 2 .. 2w + 3 (192 queries).
-constexpr int kStageRows = 192;
+// Key group kg = key tiles 4kg .. 4kg+3 (64 keys).  Key tile m lies inside the
+// windows of query blocks ceil((m-4)/2) .. floor((m+3)/2), so group kg needs
+// query blocks 2kg-2 .. 2kg+3.  A workgroup walks a run of consecutive groups
+// of one (b, h).  Its LDS holds a ring of 8 query blocks (Q rows, dA rows and
+// row seeds; block qb in slot qb mod 8): each step computes one group from the
+// six blocks it needs while the two blocks the next group adds, and the next
+// group's own K, V and bias operands, are in flight.  The two new blocks then
+// go into the two slots that no later group reads.
+constexpr int kRing = 8;
 
-__global__ void __launch_bounds__(256) local_bwd_dkdv_kernel(LocalArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 sQ[kStageRows * kRS];
-  __shared__ __attribute__((aligned(16))) u16 sA[kStageRows * kRS];
-  __shared__ __attribute__((aligned(16))) float2 sSeed[kStageRows];
+__global__ void __launch_bounds__(256) local_bwd_dkdv_kernel(LocalArgs a, int seg) {
+  __shared__ __attribute__((aligned(16))) u16 sQ[kRing * 32 * kRS];
+  __shared__ __attribute__((aligned(16))) u16 sA[kRing * 32 * kRS];
+  __shared__ __attribute__((aligned(16))) float2 sSeed[kRing * 32];
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int N = a.N, d = a.d, nqb = a.nqb, H = a.H;
   const int nkt = (N + 15) / 16;
   const int nkg = (nkt + 3) / 4;
-  const int bh = blockIdx.x / nkg;
-  const int kg = blockIdx.x % nkg;
+  const int nseg = (nkg + seg - 1) / seg;
+  const int bh = blockIdx.x / nseg;
+  const int kg0 = (blockIdx.x % nseg) * seg;
+  const int kg1 = std::min(nkg, kg0 + seg);
   const int h = bh % H;
   const size_t base = (size_t)bh * N * d;
   const uint32_t tb = (uint32_t)N * d * 2u;
@@ -354,89 +361,142 @@ __global__ void __launch_bounds__(256) local_bwd_dkdv_kernel(LocalArgs a) {
   auto row_off = [&](int row, int c) -> uint32_t {
     return (row >= 0 && row < N && c < d) ? (uint32_t)(row * d + c) * 2u : kOob;
   };
-  const int qrow0 = 32 * (2 * kg - 2);  // first staged query row (may be negative)
-
-  // stage Q, dA rows and the seeds of the six query blocks (rows past either end are zero / -inf)
-#pragma unroll
-  for (int it = 0; it < 3; ++it) {
-    const int c = tid + 256 * it, row = c >> 2, c8 = c & 3;
-    const uint32_t off = row_off(qrow0 + row, 8 * c8);
-    *reinterpret_cast<u32x4*>(sQ + row * kRS + 8 * c8) = buf_load16(rq, off);
-    *reinterpret_cast<u32x4*>(sA + row * kRS + 8 * c8) = buf_load16(rda, off);
-  }
-  if (tid < kStageRows) {
-    const int row = qrow0 + tid;
-    sSeed[tid] = (row >= 0 && row < N) ? a.seed[(size_t)bh * N + row] : make_float2(kNegInf, 0.f);
-  }
-  __syncthreads();
-
-  const int m = 4 * kg + wave;  // this wave's key tile
-  if (m >= nkt) return;         // after the only barrier
-  const int key = 16 * m + n;
-  bool kok = key < N;
-  if (a.mask != nullptr && kok) kok = a.mask[key] != 0;
-  // K^T (scaled by log2(e)/sqrt(d)) and V^T operands: lane (g, n) holds row `key`, channels 8g .. 8g+7
   const float c1 = a.scale * kLog2e;
-  u32x4 bk = buf_load16(rk, row_off(key, 8 * g));
-#pragma unroll
-  for (int e = 0; e < 4; ++e) bk[e] = pack2(bf_lo(bk[e]) * c1, bf_hi(bk[e]) * c1);
-  const u32x4 bv = buf_load16(rv, row_off(key, 8 * g));
   const bf16x8 id_hi = ident_cols_frag(lane, kLog2eHiBf16, 0);
   const bf16x8 id_lo = ident_cols_frag(lane, kLog2eLoBf16, 0);
 
-  f32x4 dk[2], dv[2];
+  // one query block = 32 rows x 4 chunks of Q (waves 0-1) and of dA (waves 2-3):
+  // one 16-byte chunk per thread, and the block's 32 seeds
+  const int srow = (tid & 127) >> 2, sc8 = tid & 3;
+  auto stage_load = [&](int qb, u32x4& r, float2& sd) {
+    const int row = 32 * qb + srow;
+    r = buf_load16((wave >> 1) ? rda : rq, row_off(row, 8 * sc8));
+    const int srow2 = 32 * qb + tid;
+    sd = (tid < 32 && srow2 >= 0 && srow2 < N) ? a.seed[(size_t)bh * N + srow2] : make_float2(kNegInf, 0.f);
+  };
+  auto stage_store = [&](int qb, const u32x4& r, const float2& sd) {
+    const int slot = qb & (kRing - 1);
+    u16* const dst = (wave >> 1) ? sA : sQ;
+    *reinterpret_cast<u32x4*>(dst + (slot * 32 + srow) * kRS + 8 * sc8) = r;
+    if (tid < 32) sSeed[slot * 32 + tid] = sd;
+  };
+  // this wave's operands for key tile m: K^T and V^T rows (lane (g, n) holds key
+  // 16m + n, channels 8g .. 8g+7) and the bias tiles of its four query blocks
+  // (rows 16qt + i, slots s0 + 8(g & 1) .. +7; lane groups 2-3 repeat them)
+  struct Ops {
+    u32x4 k, v, b[4][2];
+  };
+  auto ops_load = [&](int m, Ops& o) {
+    const int key = 16 * m + n;
+    o.k = buf_load16(rk, row_off(key, 8 * g));
+    o.v = buf_load16(rv, row_off(key, 8 * g));
+    const int qlo = std::max(0, (m - 3) / 2);
 #pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    dk[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
-    dv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < 4; ++u) {
+      const int qb = qlo + u;
+      const int s0 = 16 * m - 32 * qb + kLocalOff;
+      const bool ok = qb < nqb && s0 >= 0 && s0 + 16 <= kLocalWk;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        o.b[u][qt] = buf_load16(
+            rb, ok ? (uint32_t)(((h * nqb + qb) * kLocalWq + 16 * qt + n) * kLocalWk + s0 + 8 * (g & 1)) * 2u : kOob);
+    }
+  };
+
+  // prologue: the six blocks of the first group, and its operands
+  Ops cur;
+  ops_load(4 * kg0 + wave, cur);
+  {
+    u32x4 r[6];
+    float2 sd[6];
+#pragma unroll
+    for (int u = 0; u < 6; ++u) stage_load(2 * kg0 - 2 + u, r[u], sd[u]);
+#pragma unroll
+    for (int u = 0; u < 6; ++u) stage_store(2 * kg0 - 2 + u, r[u], sd[u]);
   }
-  const int qlo = std::max(0, (m - 3) / 2), qhi = std::min(nqb - 1, (m + 3) / 2);
-  for (int qb = qlo; qb <= qhi; ++qb) {
-    const int s0 = 16 * m - 32 * qb + kLocalOff;  // first slot of this key tile in qb's window
-    if (s0 < 0 || s0 + 16 > kLocalWk) continue;     // wave-uniform
-    const int lr = 32 * qb - qrow0;                 // staged row of the block's first query
-    f32x4 p[2], ds[2];
+  __syncthreads();
+
+  for (int kg = kg0; kg < kg1; ++kg) {
+    const bool more = kg + 1 < kg1;
+    // next group's two new blocks and operands (past the run: nothing is used)
+    u32x4 nr0, nr1;
+    float2 nsd0, nsd1;
+    Ops nxt;
+    stage_load(more ? 2 * kg + 4 : -4, nr0, nsd0);
+    stage_load(more ? 2 * kg + 5 : -4, nr1, nsd1);
+    ops_load(4 * (kg + 1) + wave, nxt);
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int m = 4 * kg + wave;  // this wave's key tile
+    if (m < nkt) {                // wave-uniform; the barrier below is reached by every wave
+      const int key = 16 * m + n;
+      bool kok = key < N;
+      if (a.mask != nullptr && kok) kok = a.mask[key] != 0;
+      u32x4 bk = cur.k;
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
-      // bias rows 16qt + i, slots s0 + 8(g & 1) .. +7 (lane groups 2-3 repeat them)
-      const u32x4 ab = buf_load16(
-          rb, (uint32_t)(((h * nqb + qb) * kLocalWq + 16 * qt + n) * kLocalWk + s0 + 8 * (g & 1)) * 2u);
-      const u32x4 aq = *reinterpret_cast<const u32x4*>(sQ + (lr + 16 * qt + n) * kRS + 8 * g);
-      const u32x4 ada = *reinterpret_cast<const u32x4*>(sA + (lr + 16 * qt + n) * kRS + 8 * g);
-      // S[query][key] in log2 units: (Q K^T) log2(e)/sqrt(d) + log2(e) bias
-      f32x4 st = mfma32(as_bf8(aq), as_bf8(bk), f32x4{0.f, 0.f, 0.f, 0.f});
-      st = mfma32(as_bf8(ab), id_hi, st);
-      st = mfma32(as_bf8(ab), id_lo, st);
-      const f32x4 dp = mfma32(as_bf8(ada), as_bf8(bv), f32x4{0.f, 0.f, 0.f, 0.f});
-      // lane (g, n) holds queries 16qt + 4g + r of the block
-      const f32x4 sA4 = *reinterpret_cast<const f32x4*>(&sSeed[lr + 16 * qt + 4 * g]);
-      const f32x4 sB4 = *reinterpret_cast<const f32x4*>(&sSeed[lr + 16 * qt + 4 * g + 2]);
-      const float sx[4] = {sA4[0], sA4[2], sB4[0], sB4[2]};
-      const float sy[4] = {sA4[1], sA4[3], sB4[1], sB4[3]};
+      for (int e = 0; e < 4; ++e) bk[e] = pack2(bf_lo(bk[e]) * c1, bf_hi(bk[e]) * c1);  // K^T * log2(e)/sqrt(d)
+      f32x4 dk[2], dv[2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float pr = kok ? exp2_fast(st[r] + sx[r]) : 0.f;
-        p[qt][r] = pr;
-        ds[qt][r] = pr * (dp[r] + sy[r]);
+      for (int ct = 0; ct < 2; ++ct) {
+        dk[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dv[ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      const int qlo = std::max(0, (m - 3) / 2);
+      const int qhi = std::min(nqb - 1, (m + 3) / 2);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int qb = qlo + u;
+        const int s0 = 16 * m - 32 * qb + kLocalOff;  // first slot of this key tile in qb's window
+        if (qb > qhi || s0 < 0 || s0 + 16 > kLocalWk) continue;  // wave-uniform
+        const int lr = (qb & (kRing - 1)) * 32;                  // ring row of the block's first query
+        f32x4 p[2], ds[2];
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          const u32x4 aq = *reinterpret_cast<const u32x4*>(sQ + (lr + 16 * qt + n) * kRS + 8 * g);
+          const u32x4 ada = *reinterpret_cast<const u32x4*>(sA + (lr + 16 * qt + n) * kRS + 8 * g);
+          // S[query][key] in log2 units: (Q K^T) log2(e)/sqrt(d) + log2(e) bias
+          f32x4 st = mfma32(as_bf8(aq), as_bf8(bk), f32x4{0.f, 0.f, 0.f, 0.f});
+          st = mfma32(as_bf8(cur.b[u][qt]), id_hi, st);
+          st = mfma32(as_bf8(cur.b[u][qt]), id_lo, st);
+          const f32x4 dp = mfma32(as_bf8(ada), as_bf8(cur.v), f32x4{0.f, 0.f, 0.f, 0.f});
+          // lane (g, n) holds queries 16qt + 4g + r of the block
+          const f32x4 sA4 = *reinterpret_cast<const f32x4*>(&sSeed[lr + 16 * qt + 4 * g]);
+          const f32x4 sB4 = *reinterpret_cast<const f32x4*>(&sSeed[lr + 16 * qt + 4 * g + 2]);
+          const float sx[4] = {sA4[0], sA4[2], sB4[0], sB4[2]};
+          const float sy[4] = {sA4[1], sA4[3], sB4[1], sB4[3]};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pr = kok ? exp2_fast(st[r] + sx[r]) : 0.f;
+            p[qt][r] = pr;
+            ds[qt][r] = pr * (dp[r] + sy[r]);
+          }
+        }
+        // dV^T += dA^T P, dK^T += Q^T dS over the block's 32 queries:
+        // k slot (g, v) = query 16(v / 4) + 4g + v % 4
+        const bf16x8 bp = pack8(p[0], p[1]);
+        const bf16x8 bs = pack8(ds[0], ds[1]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          dv[ct] = mfma32(tr_frag<kRS>(sA, lr + 4 * g, lr + 16 + 4 * g, 16 * ct, lane), bp, dv[ct]);
+          dk[ct] = mfma32(tr_frag<kRS>(sQ, lr + 4 * g, lr + 16 + 4 * g, 16 * ct, lane), bs, dk[ct]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const uint32_t off = row_off(key, 16 * ct + 4 * g);
+        const f32x4 yk = dk[ct] * a.scale;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(yk[0], yk[1]), pack2(yk[2], yk[3])}, rdk, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(dv[ct][0], dv[ct][1]), pack2(dv[ct][2], dv[ct][3])}, rdv,
+                                              off, 0, 0);
       }
     }
-    // dV^T += dA^T P, dK^T += Q^T dS over the block's 32 queries:
-    // k slot (g, v) = query 16(v / 4) + 4g + v % 4
-    const bf16x8 bp = pack8(p[0], p[1]);
-    const bf16x8 bs = pack8(ds[0], ds[1]);
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      dv[ct] = mfma32(tr_frag<kRS>(sA, lr + 4 * g, lr + 16 + 4 * g, 16 * ct, lane), bp, dv[ct]);
-      dk[ct] = mfma32(tr_frag<kRS>(sQ, lr + 4 * g, lr + 16 + 4 * g, 16 * ct, lane), bs, dk[ct]);
+    // blocks 2kg+4, 2kg+5 go over those of 2kg-4, 2kg-3, which no group from kg on reads
+    if (more) {
+      stage_store(2 * kg + 4, nr0, nsd0);
+      stage_store(2 * kg + 5, nr1, nsd1);
     }
-  }
-#pragma unroll
-  for (int ct = 0; ct < 2; ++ct) {
-    const uint32_t off = row_off(key, 16 * ct + 4 * g);
-    const f32x4 yk = dk[ct] * a.scale;
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(yk[0], yk[1]), pack2(yk[2], yk[3])}, rdk, off, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(dv[ct][0], dv[ct][1]), pack2(dv[ct][2], dv[ct][3])}, rdv, off,
-                                          0, 0);
+    cur = nxt;
+    __syncthreads();
   }
 }
 
@@ -500,11 +560,14 @@ hipError_t launch_local_bwd(const LocalArgs& a, hipStream_t stream, KernelTimer*
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
-  // 3. dK and dV
+  // 3. dK and dV: runs of `seg` key groups per workgroup, about 768 workgroups
+  // (three per CU by LDS)
   {
-    const int nkt = (a.N + 15) / 16;
-    const unsigned grid = (unsigned)((size_t)a.B * a.H * ((nkt + 3) / 4));
-    hipLaunchKernelGGL(local_bwd_dkdv_kernel, dim3(grid), dim3(256), 0, stream, a);
+    const int nkg = ((a.N + 15) / 16 + 3) / 4;
+    const long long bhs = (long long)a.B * a.H;
+    const int seg = (int)std::max<long long>(1, (bhs * nkg + 767) / 768);
+    const unsigned grid = (unsigned)(bhs * ((nkg + seg - 1) / seg));
+    hipLaunchKernelGGL(local_bwd_dkdv_kernel, dim3(grid), dim3(256), 0, stream, a, seg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
