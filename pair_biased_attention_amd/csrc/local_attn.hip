@@ -12,16 +12,18 @@
 // lse, rows without keys) is as in the dense kernels.
 //
 // Kernels (d <= 32, bf16):
-//  * forward: one wave per (b, h, query block).  S^T = K Q^T for the whole
+//  * forward: one wave per (b, h, query block), four consecutive blocks per
+//    workgroup sharing one staged V window.  S^T = K Q^T for the whole
 //    window (8 key tiles x 2 query tiles), exact softmax in registers (no
-//    online rescale: the window fits), O^T = V^T P^T with V staged in LDS
-//    and read transposed.  The key order inside the score tiles is permuted
+//    online rescale: the window fits), O^T = V^T P^T with V read transposed
+//    from LDS.  The key order inside the score tiles is permuted
 //    so that lane group g owns the 32 contiguous slots 32g .. 32g + 31: its
 //    bias comes as four 16-byte loads per query row.
 //  * backward, query-stationary: one wave per (h, query block, 16-query tile,
-//    batch chunk) walks the chunk's batch rows in order, recomputes P,
-//    forms dS and dQ = dS K and accumulates dS in registers: one dbias
-//    partial per chunk, summed over chunks in a fixed order afterwards.
+//    batch chunk), two blocks per workgroup sharing a staged K window, walks
+//    the chunk's batch rows in order, recomputes P, forms dS and dQ = dS K
+//    and accumulates dS in registers: one dbias partial per chunk, summed
+//    over chunks in a fixed order afterwards.
 //  * backward, key-stationary: one wave per 16-key tile.  Each key tile lies
 //    wholly inside the windows of exactly four query blocks (the windows are
 //    16-aligned).  A workgroup walks consecutive groups of four key tiles
@@ -64,15 +66,20 @@ __device__ __forceinline__ u32x2 buf_load8(__amdgpu_buffer_rsrc_t r, uint32_t of
 }  // namespace
 
 // ------------------------------------------------------------------ forward
+// The four waves of a workgroup take four consecutive query blocks of one
+// (b, h) and share one staged V window: keys 128qg - 48 .. 128qg + 175 (224
+// rows), wave w's window starting at row 32w.
+constexpr int kFwdRows = 224;
+
 __global__ void __launch_bounds__(256) local_fwd_kernel(LocalArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 sV[4][kLocalWk * kRS];
-  __shared__ __attribute__((aligned(16))) uint8_t sKeep[4][kLocalWk];
-  const int lane = threadIdx.x & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
+  __shared__ __attribute__((aligned(16))) u16 sV[kFwdRows * kRS];
+  __shared__ __attribute__((aligned(16))) uint8_t sKeep[kFwdRows + 32];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int N = a.N, d = a.d, nqb = a.nqb;
   const int nqg = (nqb + 3) / 4;
   const int bh = blockIdx.x / nqg;
-  const int qb = (blockIdx.x % nqg) * 4 + wave;
-  if (qb >= nqb) return;  // a whole wave; no barrier follows
+  const int qg = blockIdx.x % nqg;
+  const int qb = qg * 4 + wave;
   const int h = bh % a.H;
   const size_t base = (size_t)bh * N * d;
   const uint32_t tb = (uint32_t)N * d * 2u;
@@ -83,51 +90,51 @@ __global__ void __launch_bounds__(256) local_fwd_kernel(LocalArgs a) {
   const auto ro = make_rsrc(static_cast<u16*>(a.out) + base, tb);
   const auto rb = make_rsrc(a.bias, (uint32_t)a.H * nqb * kLocalWq * kLocalWk * 2u);
   const int key0 = kLocalWq * qb - kLocalOff;
+  const int row0 = 128 * qg - kLocalOff;  // key of staged row 0
   auto key_off = [&](int key, int c) -> uint32_t {
     return (key >= 0 && key < N && c < d) ? (uint32_t)(key * d + c) * 2u : kOob;
   };
+  const bool qok = qb < nqb;  // a wave past the last block only helps staging
 
-  // V window (row = slot) and the usable flags of the slots
-  u32x4 vv[8];
-#pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int c = lane + 64 * it, row = c >> 2, c8 = c & 3;
-    vv[it] = buf_load16(rv, key_off(key0 + row, 8 * c8));
-  }
-  // K operand of tile t: lane (g, r) holds K[slot_of(t, r)][8g .. 8g+7]
-  u32x4 ak[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) ak[t] = buf_load16(rk, key_off(key0 + slot_of(t, n), 8 * g));
-  // Q^T operand of query tile qt: lane (g, n) holds Q[32qb + 16qt + n][8g .. 8g+7]
-  u32x4 bq[2];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt) bq[qt] = buf_load16(rq, key_off(32 * qb + 16 * qt + n, 8 * g));
+  // this wave's operands: K of tile t (lane (g, r) holds K[slot_of(t, r)][8g .. 8g+7]),
+  // Q^T of query tile qt (lane (g, n) holds Q[32qb + 16qt + n][8g .. 8g+7]),
   // bias of query row 16qt + n, slots 32g + 8c .. +7
-  u32x4 bb[2][4];
+  u32x4 ak[8], bq[2], bb[2][4];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) ak[t] = buf_load16(rk, qok ? key_off(key0 + slot_of(t, n), 8 * g) : kOob);
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) bq[qt] = buf_load16(rq, qok ? key_off(32 * qb + 16 * qt + n, 8 * g) : kOob);
 #pragma unroll
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int c = 0; c < 4; ++c)
-      bb[qt][c] = buf_load16(rb, (uint32_t)(((h * nqb + qb) * kLocalWq + 16 * qt + n) * kLocalWk + 32 * g + 8 * c) * 2u);
-  {
-    const int s0 = 2 * lane;
+      bb[qt][c] = buf_load16(
+          rb, qok ? (uint32_t)(((h * nqb + qb) * kLocalWq + 16 * qt + n) * kLocalWk + 32 * g + 8 * c) * 2u : kOob);
+  // the shared V window and the usable flags of its keys
+  u32x4 vv[4];
 #pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int key = key0 + s0 + e;
-      bool ok = key >= 0 && key < N;
-      if (a.mask != nullptr && ok) ok = a.mask[key] != 0;
-      sKeep[wave][s0 + e] = ok ? 1 : 0;
-    }
+  for (int it = 0; it < 4; ++it) {
+    const int c = tid + 256 * it, row = c >> 2, c8 = c & 3;
+    vv[it] = buf_load16(rv, row < kFwdRows ? key_off(row0 + row, 8 * c8) : kOob);
   }
-  u16* const mv = sV[wave];
+  if (tid < kFwdRows) {
+    const int key = row0 + tid;
+    bool ok = key >= 0 && key < N;
+    if (a.mask != nullptr && ok) ok = a.mask[key] != 0;
+    sKeep[tid] = ok ? 1 : 0;
+  }
 #pragma unroll
-  for (int it = 0; it < 8; ++it) {
-    const int c = lane + 64 * it, row = c >> 2, c8 = c & 3;
-    *reinterpret_cast<u32x4*>(mv + row * kRS + 8 * c8) = vv[it];
+  for (int it = 0; it < 4; ++it) {
+    const int c = tid + 256 * it, row = c >> 2, c8 = c & 3;
+    if (row < kFwdRows) *reinterpret_cast<u32x4*>(sV + row * kRS + 8 * c8) = vv[it];
   }
+  __syncthreads();
+  if (!qok) return;  // after the only barrier
+  const u16* const mv = sV + 32 * wave * kRS;
+  const uint8_t* const mkeep = sKeep + 32 * wave;
   // byte (4t + j) of this lane group's 32 flags: slot 32g + 4t + j
-  const u32x4 kf0 = *reinterpret_cast<const u32x4*>(&sKeep[wave][32 * g]);
-  const u32x4 kf1 = *reinterpret_cast<const u32x4*>(&sKeep[wave][32 * g + 16]);
+  const u32x4 kf0 = *reinterpret_cast<const u32x4*>(mkeep + 32 * g);
+  const u32x4 kf1 = *reinterpret_cast<const u32x4*>(mkeep + 32 * g + 16);
 
   const float c1 = a.scale * kLog2e;
   float m[2], l[2];
@@ -196,24 +203,29 @@ __global__ void __launch_bounds__(256) local_fwd_kernel(LocalArgs a) {
 }
 
 // ------------------------------------------------------------------ backward, dQ and dbias partials
+// A workgroup takes query blocks 2p, 2p+1 of one (head, batch chunk); wave w
+// owns block 2p + w/2, query tile w%2.  Per batch row the four waves stage
+// one shared K window: keys 64p - 48 .. 64p + 111 (160 rows), block 2p + u
+// starting at row 32u.
+constexpr int kDqRows = 160;
+
 __global__ void __launch_bounds__(256) local_bwd_dq_kernel(LocalArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 sK[4][kLocalWk * kRS];
-  __shared__ __attribute__((aligned(16))) uint8_t sKeep[4][kLocalWk];
-  const int lane = threadIdx.x & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
+  __shared__ __attribute__((aligned(16))) u16 sK[kDqRows * kRS];
+  __shared__ __attribute__((aligned(16))) uint8_t sKeep[kDqRows];
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int N = a.N, d = a.d, nqb = a.nqb, H = a.H;
-  // wave task: (chunk, h, qb, qt), qt fastest
-  int w = blockIdx.x * 4 + wave;
-  const int qt = w & 1;
-  w >>= 1;
-  const int qb = w % nqb;
-  w /= nqb;
-  const int h = w % H;
-  const int chunk = w / H;
-  if (chunk >= a.P) return;  // a whole wave; no barrier follows
+  const int npair = (nqb + 1) / 2;
+  const int p = blockIdx.x % npair;
+  const int h = (blockIdx.x / npair) % H;
+  const int chunk = blockIdx.x / (npair * H);
+  const int qt = wave & 1;
+  const int qb = 2 * p + (wave >> 1);
+  const bool qok = qb < nqb;  // a wave past the last block only helps staging
   const int b0 = chunk * a.C, b1 = std::min(a.B, b0 + a.C);
+  const int row0 = 64 * p - kLocalOff;  // key of staged row 0
   const int key0 = kLocalWq * qb - kLocalOff;
   const int query = 32 * qb + 16 * qt + n;
-  const bool qvalid = query < N;
+  const bool qvalid = qok && query < N;
   const uint32_t tb = (uint32_t)N * d * 2u;
   auto key_off = [&](int key, int c) -> uint32_t {
     return (key >= 0 && key < N && c < d) ? (uint32_t)(key * d + c) * 2u : kOob;
@@ -222,19 +234,18 @@ __global__ void __launch_bounds__(256) local_bwd_dq_kernel(LocalArgs a) {
   u32x4 bb[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c)
-    bb[c] = buf_load16(rb, (uint32_t)(((h * nqb + qb) * kLocalWq + 16 * qt + n) * kLocalWk + 32 * g + 8 * c) * 2u);
-  {
-    const int s0 = 2 * lane;
-#pragma unroll
-    for (int e = 0; e < 2; ++e) {
-      const int key = key0 + s0 + e;
-      bool ok = key >= 0 && key < N;
-      if (a.mask != nullptr && ok) ok = a.mask[key] != 0;
-      sKeep[wave][s0 + e] = ok ? 1 : 0;
-    }
+    bb[c] = buf_load16(
+        rb, qok ? (uint32_t)(((h * nqb + qb) * kLocalWq + 16 * qt + n) * kLocalWk + 32 * g + 8 * c) * 2u : kOob);
+  if (tid < kDqRows) {
+    const int key = row0 + tid;
+    bool ok = key >= 0 && key < N;
+    if (a.mask != nullptr && ok) ok = a.mask[key] != 0;
+    sKeep[tid] = ok ? 1 : 0;
   }
-  const u32x4 kf0 = *reinterpret_cast<const u32x4*>(&sKeep[wave][32 * g]);
-  const u32x4 kf1 = *reinterpret_cast<const u32x4*>(&sKeep[wave][32 * g + 16]);
+  __syncthreads();
+  const int wr = 32 * (wave >> 1);  // this wave's first window row
+  const u32x4 kf0 = *reinterpret_cast<const u32x4*>(&sKeep[wr + 32 * g]);
+  const u32x4 kf1 = *reinterpret_cast<const u32x4*>(&sKeep[wr + 32 * g + 16]);
   // log2(e) * bias, -inf where the slot is unusable or the row does not exist
   float b2[8][4];
 #pragma unroll
@@ -253,7 +264,7 @@ __global__ void __launch_bounds__(256) local_bwd_dq_kernel(LocalArgs a) {
   for (int t = 0; t < 8; ++t)
 #pragma unroll
     for (int j = 0; j < 4; ++j) dacc[t][j] = 0.f;
-  u16* const mk = sK[wave];
+  const u16* const mk = sK + wr * kRS;
 
   for (int b = b0; b < b1; ++b) {
     const size_t bh = (size_t)b * H + h;
@@ -263,52 +274,57 @@ __global__ void __launch_bounds__(256) local_bwd_dq_kernel(LocalArgs a) {
     const auto rv = make_rsrc(static_cast<const u16*>(a.v) + base, tb);
     const auto rda = make_rsrc(static_cast<const u16*>(a.da) + base, tb);
     const auto rdq = make_rsrc(static_cast<u16*>(a.dq) + base, tb);
-    u32x4 kv[8], av[8];
+    u32x4 kv[3], av[8];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int c = lane + 64 * it, row = c >> 2, c8 = c & 3;
-      kv[it] = buf_load16(rk, key_off(key0 + row, 8 * c8));
+    for (int it = 0; it < 3; ++it) {
+      const int c = tid + 256 * it, row = c >> 2, c8 = c & 3;
+      kv[it] = buf_load16(rk, row < kDqRows ? key_off(row0 + row, 8 * c8) : kOob);
     }
 #pragma unroll
-    for (int t = 0; t < 8; ++t) av[t] = buf_load16(rv, key_off(key0 + slot_of(t, n), 8 * g));
-    const u32x4 bq = buf_load16(rq, key_off(query, 8 * g));
-    const u32x4 bda = buf_load16(rda, key_off(query, 8 * g));
+    for (int t = 0; t < 8; ++t) av[t] = buf_load16(rv, qok ? key_off(key0 + slot_of(t, n), 8 * g) : kOob);
+    const u32x4 bq = buf_load16(rq, qok ? key_off(query, 8 * g) : kOob);
+    const u32x4 bda = buf_load16(rda, qok ? key_off(query, 8 * g) : kOob);
     const float2 sd = qvalid ? a.seed[bh * N + query] : make_float2(kNegInf, 0.f);
-    // the K window in LDS: operand rows for S^T and transposed reads for dQ
+    // the shared K window: operand rows for S^T and transposed reads for dQ
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int c = lane + 64 * it, row = c >> 2, c8 = c & 3;
-      *reinterpret_cast<u32x4*>(mk + row * kRS + 8 * c8) = kv[it];
+    for (int it = 0; it < 3; ++it) {
+      const int c = tid + 256 * it, row = c >> 2, c8 = c & 3;
+      if (row < kDqRows) *reinterpret_cast<u32x4*>(sK + row * kRS + 8 * c8) = kv[it];
     }
-    f32x4 ds[8];
+    __syncthreads();
+    if (qok) {  // wave-uniform
+      f32x4 ds[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const u32x4 akt = *reinterpret_cast<const u32x4*>(mk + slot_of(t, n) * kRS + 8 * g);
-      const f32x4 st = mfma32(as_bf8(akt), as_bf8(bq), f32x4{0.f, 0.f, 0.f, 0.f});
-      const f32x4 dp = mfma32(as_bf8(av[t]), as_bf8(bda), f32x4{0.f, 0.f, 0.f, 0.f});
+      for (int t = 0; t < 8; ++t) {
+        const u32x4 akt = *reinterpret_cast<const u32x4*>(mk + slot_of(t, n) * kRS + 8 * g);
+        const f32x4 st = mfma32(as_bf8(akt), as_bf8(bq), f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 dp = mfma32(as_bf8(av[t]), as_bf8(bda), f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float pr = exp2_fast(fmaf(st[j], c1, b2[t][j]) + sd.x);
+          ds[t][j] = pr * (dp[j] + sd.y);
+          dacc[t][j] += ds[t][j];
+        }
+      }
+      // dQ^T = K^T dS^T over the slots, k-step j = slots 32g + 8j .. +7
+      f32x4 dq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float p = exp2_fast(fmaf(st[j], c1, b2[t][j]) + sd.x);
-        ds[t][j] = p * (dp[j] + sd.y);
-        dacc[t][j] += ds[t][j];
+        const bf16x8 bds = pack8(ds[2 * j], ds[2 * j + 1]);
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+          dq[ct] = mfma32(tr_frag<kRS>(mk, 32 * g + 8 * j, 32 * g + 8 * j + 4, 16 * ct, lane), bds, dq[ct]);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const f32x4 y = dq[ct] * a.scale;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])}, rdq,
+                                              key_off(query, 16 * ct + 4 * g), 0, 0);
       }
     }
-    // dQ^T = K^T dS^T over the slots, k-step j = slots 32g + 8j .. +7
-    f32x4 dq[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const bf16x8 bds = pack8(ds[2 * j], ds[2 * j + 1]);
-#pragma unroll
-      for (int ct = 0; ct < 2; ++ct)
-        dq[ct] = mfma32(tr_frag<kRS>(mk, 32 * g + 8 * j, 32 * g + 8 * j + 4, 16 * ct, lane), bds, dq[ct]);
-    }
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct) {
-      const f32x4 y = dq[ct] * a.scale;
-      __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(y[0], y[1]), pack2(y[2], y[3])}, rdq,
-                                            key_off(query, 16 * ct + 4 * g), 0, 0);
-    }
+    __syncthreads();  // the window is restaged for the next batch row
   }
+  if (!qok) return;
   // partial of this chunk: row 16qt + n, slots 32g + 8c .. +7
   float* const part = a.partial + (((size_t)chunk * H + h) * nqb + qb) * kLocalWq * kLocalWk +
                       (size_t)(16 * qt + n) * kLocalWk + 32 * g;
@@ -553,10 +569,10 @@ hipError_t launch_local_bwd(const LocalArgs& a, hipStream_t stream, KernelTimer*
     if ((e = launch_attn_bwd_pre_bf16(pa, stream)) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
-  // 2. dQ and the dbias partials
+  // 2. dQ and the dbias partials: one workgroup per (batch chunk, head, pair of query blocks)
   {
-    const size_t waves = (size_t)a.P * a.H * a.nqb * 2;
-    hipLaunchKernelGGL(local_bwd_dq_kernel, dim3((unsigned)((waves + 3) / 4)), dim3(256), 0, stream, a);
+    const size_t grid = (size_t)a.P * a.H * ((a.nqb + 1) / 2);
+    hipLaunchKernelGGL(local_bwd_dq_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
