@@ -78,7 +78,7 @@ def proj_main_bwd_bytes(N, H, c):
     return N * N * (4 * c + 2 * H)
 
 
-LOCAL_BWD_KERNELS = ["local_bwd_pre", "local_bwd_dq", "local_bwd_dkdv", "local_bwd_dbias_reduce"]
+LOCAL_BWD_KERNELS = ["local_bwd_pre", "local_bwd_dkdv_dq", "local_bwd_dbias_reduce"]
 
 
 def local_units(B, H, N, d):
@@ -88,12 +88,11 @@ def local_units(B, H, N, d):
 
 def local_kernel_flops(B, H, N, d):
     """Algorithmic flops credited per launch, as for the dense path: forward
-    4 (QK^T, PV); backward 10, of which the key-stationary launch carries 8
-    (S recompute, dP, dV, dK) and the query-stationary one 2 (dQ; its own
-    recompute of S and dP is not credited)."""
+    4 (QK^T, PV); backward 10 in the one launch that carries the
+    key-stationary role (S recompute, dP, dV, dK: 8) and the query-stationary
+    role (dQ: 2; its own recompute of S and dP is not credited)."""
     u = local_units(B, H, N, d)
-    return {"local_fwd": 4 * u, "local_bwd_pre": 0.0, "local_bwd_dq": 2 * u, "local_bwd_dkdv": 8 * u,
-            "local_bwd_dbias_reduce": 0.0}
+    return {"local_fwd": 4 * u, "local_bwd_pre": 0.0, "local_bwd_dkdv_dq": 10 * u, "local_bwd_dbias_reduce": 0.0}
 
 
 PROJ_FWD_KERNELS = ["bias_proj_fwd"]
@@ -187,8 +186,7 @@ KERNEL_SOURCES = {
     "pwa_bwd_dv_dw": ("pwa_gemm_kernel<32, false", "pwa.hip"),
     "bias_proj_fwd": ("bias_proj_fwd_kernel<4>", "bias_proj.hip"),
     "local_fwd": ("local_fwd_kernel", "local_attn.hip"),
-    "local_bwd_dq": ("local_bwd_dq_kernel", "local_attn.hip"),
-    "local_bwd_dkdv": ("local_bwd_dkdv_kernel", "local_attn.hip"),
+    "local_bwd_dkdv_dq": ("local_bwd_kernel", "local_attn.hip"),
     "bias_proj_bwd": ("bias_proj_bwd_kernel<4, true>", "bias_proj.hip"),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")

@@ -260,9 +260,10 @@ int pba_local_backward(int B, int H, int N, int d, int dtype,
  *                                      dbias (x) xhat and dbias, then their
  *                                      reduction into dw, dgamma, dbeta
  *   pba_local_forward_timed:           one launch
- *   pba_local_backward_timed:          preprocess (dA, dG, row seeds), dQ with
- *                                      the per-chunk dbias partials, dK/dV,
- *                                      dbias reduction
+ *   pba_local_backward_timed:          preprocess (dA, dG, row seeds), dK/dV
+ *                                      together with dQ and the per-chunk
+ *                                      dbias partials (one launch), dbias
+ *                                      reduction
  * kernel_ms or n_kernels NULL returns PBA_ERR_NULL; a runtime failure returns
  * PBA_ERR_HIP.
  */

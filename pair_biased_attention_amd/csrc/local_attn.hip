@@ -24,7 +24,8 @@
 //    the chunk's batch rows in order, recomputes P, forms dS and dQ = dS K
 //    and accumulates dS in registers: one dbias partial per chunk, summed
 //    over chunks in a fixed order afterwards.
-//  * backward, key-stationary: one wave per 16-key tile.  Each key tile lies
+//  * backward, key-stationary (in the same launch as the query-stationary
+//    role, whose workgroups fill the slots after it): one wave per 16-key tile.  Each key tile lies
 //    wholly inside the windows of exactly four query blocks (the windows are
 //    16-aligned).  A workgroup walks consecutive groups of four key tiles
 //    with a ring of query blocks in LDS; each wave forms S = Q K^T (bias
@@ -209,15 +210,17 @@ __global__ void __launch_bounds__(256) local_fwd_kernel(LocalArgs a) {
 // starting at row 32u.
 constexpr int kDqRows = 160;
 
-__global__ void __launch_bounds__(256) local_bwd_dq_kernel(LocalArgs a) {
-  __shared__ __attribute__((aligned(16))) u16 sK[kDqRows * kRS];
-  __shared__ __attribute__((aligned(16))) uint8_t sKeep[kDqRows];
+constexpr size_t kDqLds = kDqRows * kRS * 2 + kDqRows;
+
+__device__ __forceinline__ void local_dq_role(const LocalArgs& a, const int blk, char* const lds) {
+  u16* const sK = reinterpret_cast<u16*>(lds);
+  uint8_t* const sKeep = reinterpret_cast<uint8_t*>(lds + kDqRows * kRS * 2);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int N = a.N, d = a.d, nqb = a.nqb, H = a.H;
   const int npair = (nqb + 1) / 2;
-  const int p = blockIdx.x % npair;
-  const int h = (blockIdx.x / npair) % H;
-  const int chunk = blockIdx.x / (npair * H);
+  const int p = blk % npair;
+  const int h = (blk / npair) % H;
+  const int chunk = blk / (npair * H);
   const int qt = wave & 1;
   const int qb = 2 * p + (wave >> 1);
   const bool qok = qb < nqb;  // a wave past the last block only helps staging
@@ -352,17 +355,19 @@ __global__ void __launch_bounds__(256) local_bwd_dq_kernel(LocalArgs a) {
 // go into the two slots that no later group reads.
 constexpr int kRing = 8;
 
-__global__ void __launch_bounds__(256) local_bwd_dkdv_kernel(LocalArgs a, int seg) {
-  __shared__ __attribute__((aligned(16))) u16 sQ[kRing * 32 * kRS];
-  __shared__ __attribute__((aligned(16))) u16 sA[kRing * 32 * kRS];
-  __shared__ __attribute__((aligned(16))) float2 sSeed[kRing * 32];
+constexpr size_t kDkdvLds = 2 * kRing * 32 * kRS * 2 + kRing * 32 * sizeof(float2);
+
+__device__ __forceinline__ void local_dkdv_role(const LocalArgs& a, const int seg, const int blk, char* const lds) {
+  u16* const sQ = reinterpret_cast<u16*>(lds);
+  u16* const sA = sQ + kRing * 32 * kRS;
+  float2* const sSeed = reinterpret_cast<float2*>(sA + kRing * 32 * kRS);
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index(), g = lane >> 4, n = lane & 15;
   const int N = a.N, d = a.d, nqb = a.nqb, H = a.H;
   const int nkt = (N + 15) / 16;
   const int nkg = (nkt + 3) / 4;
   const int nseg = (nkg + seg - 1) / seg;
-  const int bh = blockIdx.x / nseg;
-  const int kg0 = (blockIdx.x % nseg) * seg;
+  const int bh = blk / nseg;
+  const int kg0 = (blk % nseg) * seg;
   const int kg1 = std::min(nkg, kg0 + seg);
   const int h = bh % H;
   const size_t base = (size_t)bh * N * d;
@@ -516,6 +521,17 @@ __global__ void __launch_bounds__(256) local_bwd_dkdv_kernel(LocalArgs a, int se
   }
 }
 
+// One launch carries both backward roles: the key-stationary runs take the
+// first `ndkdv` workgroup slots (they are the longer ones), the
+// query-stationary workgroups the rest; the roles share the LDS buffer.
+__global__ void __launch_bounds__(256) local_bwd_kernel(LocalArgs a, int seg, int ndkdv) {
+  __shared__ __attribute__((aligned(16))) char lds[kDkdvLds > kDqLds ? kDkdvLds : kDqLds];
+  if ((int)blockIdx.x < ndkdv)
+    local_dkdv_role(a, seg, blockIdx.x, lds);
+  else
+    local_dq_role(a, blockIdx.x - ndkdv, lds);
+}
+
 // ------------------------------------------------------------------ plan + launch
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
@@ -569,21 +585,16 @@ hipError_t launch_local_bwd(const LocalArgs& a, hipStream_t stream, KernelTimer*
     if ((e = launch_attn_bwd_pre_bf16(pa, stream)) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
-  // 2. dQ and the dbias partials: one workgroup per (batch chunk, head, pair of query blocks)
-  {
-    const size_t grid = (size_t)a.P * a.H * ((a.nqb + 1) / 2);
-    hipLaunchKernelGGL(local_bwd_dq_kernel, dim3((unsigned)grid), dim3(256), 0, stream, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    timer_mark(timer, stream);
-  }
-  // 3. dK and dV: runs of `seg` key groups per workgroup, about 768 workgroups
-  // (three per CU by LDS)
+  // 2-3. dK/dV (runs of `seg` key groups per workgroup, about 768 of them:
+  // three per CU) and dQ with the dbias partials (one workgroup per batch
+  // chunk, head and pair of query blocks), in one launch
   {
     const int nkg = ((a.N + 15) / 16 + 3) / 4;
     const long long bhs = (long long)a.B * a.H;
     const int seg = (int)std::max<long long>(1, (bhs * nkg + 767) / 768);
-    const unsigned grid = (unsigned)(bhs * ((nkg + seg - 1) / seg));
-    hipLaunchKernelGGL(local_bwd_dkdv_kernel, dim3(grid), dim3(256), 0, stream, a, seg);
+    const long long ndkdv = bhs * ((nkg + seg - 1) / seg);
+    const long long ndq = (long long)a.P * a.H * ((a.nqb + 1) / 2);
+    hipLaunchKernelGGL(local_bwd_kernel, dim3((unsigned)(ndkdv + ndq)), dim3(256), 0, stream, a, seg, (int)ndkdv);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
