@@ -67,6 +67,9 @@ SMALL = [
     (20, 4, 1100, 32, "none"),      # two batch rows per dbias chunk (10 chunks)
     (1, 1, 20, 32, "none"),         # fewer keys than one key tile group
     (2, 2, 300, 32, "tail:40"),     # the last windows mostly masked
+    (3, 2, 1, 32, "none"),          # a single atom: one query, one key
+    (2, 1, 17, 32, "random:3"),     # one ragged query block and key tile
+    (1, 3, 2, 8, "none"),           # the narrowest head
 ]
 
 
@@ -122,6 +125,18 @@ def test_local_matches_dense_kernel_when_windows_cover_everything():
     pairs = {"out": (res["out"], to_f64(out)), "dv": (res["dv"], to_f64(gr["dv"])),
              "dq": (res["dq"], to_f64(gr["dq"])), "dk": (res["dk"], to_f64(gr["dk"]))}
     check_all("local vs dense", pairs, TOL["bf16"], {"dq": floor, "dk": floor})
+
+
+def test_local_null_mask_equals_all_keep():
+    """key_mask NULL and a mask of ones give the same bits."""
+    log("windowed attention NULL mask")
+    cfg = workloads.LocalConfig("nullmask", B=2, H=2, N=130, d=32, mask="none", seed=51)
+    inp = workloads.local_inputs(cfg)
+    a = _run(inp)
+    inp["key_mask"] = np.ones(130, dtype=np.uint8)
+    b = _run(inp)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
 
 
 def test_local_backward_is_bitwise_deterministic():
