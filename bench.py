@@ -181,7 +181,7 @@ KERNEL_SOURCES = {
     "bwd_pre": ("attn_bwd_pre_bf16_kernel", "attn_bwd.hip"),
     "bwd_dkdv_dq": ("attn_bwd_dq_bf16_kernel", "attn_bwd.hip"),
     "bwd_dbias_reduce": ("bias_grad_reduce_kernel", "attn_bwd.hip"),
-    "pwa_weighted_sum": ("pwa_gemm_kernel<32, true", "pwa.hip"),
+    "pwa_weighted_sum": ("pwa_gemm_dl_kernel<32, true>", "pwa.hip"),
     "pwa_bwd_pre": ("pwa_bwd_pre_kernel", "pwa.hip"),
     "pwa_bwd_dv_dw": ("pwa_gemm_kernel<32, false", "pwa.hip"),
     "bias_proj_fwd": ("bias_proj_fwd_kernel<4>", "bias_proj.hip"),

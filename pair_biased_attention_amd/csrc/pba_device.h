@@ -131,6 +131,41 @@ __device__ __forceinline__ bf16x8 tr_frag(const u16* tile, int rb0, int rb1, int
   return as_bf8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
+// ---- vector-memory waits for loads the compiler does not track as producers
+// (buffer loads with an LDS destination): s_waitcnt with only the vector
+// counter set, at most N of this wave's vector-memory operations outstanding.
+typedef __attribute__((address_space(3))) void lds_void;
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Buffer resource words (base, stride 0, num_records bytes, the same flags as
+// make_rsrc) for the inline-asm loads below; every word is wave-uniform.
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t num_bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+               __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu)),
+               __builtin_amdgcn_readfirstlane((int)num_bytes), 0x00020000};
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane l writes LDS bytes
+// lds_base + 16 l .. + 15 (zeros where byte_off fails the range check).  It
+// has no register results.  Written as asm so that the compiler, which cannot
+// tell which LDS bytes such a load writes, does not drain every one of them
+// before each later LDS read; callers order them with vm_wait and barriers.
+__device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds_base, uint32_t byte_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(byte_off), "s"(rsrc)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_void*)(p);
+}
+template <int N>
+__device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt has six bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
 // ---- bounds-checked global loads through a buffer resource: any byte past
 // num_bytes reads as zero, so ragged tiles need no per-element guards.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {

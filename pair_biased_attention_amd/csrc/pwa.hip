@@ -12,7 +12,10 @@
 //
 // Kernels (all on the caller's stream):
 //   pwa_softmax   w and w^T (bf16 workspace) and lse_w
-//   pwa_gemm<FWD> out = sigmoid(G) * (w V)   or  dV = w^T dA   (same kernel)
+//   pwa_gemm_dl   out = sigmoid(G) * (w V): persistent, operands staged
+//                 by direct-to-LDS loads (N % 8 == 0)
+//   pwa_gemm<FWD> the same product with register-staged operands (any N),
+//                 and dV = w^T dA together with the dw tiles
 //   pwa_bwd_pre   dA = dO*sigmoid(G), dG = dO*O*(1-sigmoid(G))
 //   pwa_dw        split-K GEMM dw_p[h,i,j] = sum_{s in chunk p, c} dA[s,i,h,c] V[s,j,h,c]
 //   pwa_db        dw = sum_p dw_p (index order), db = w*(dw - sum_j w*dw)
@@ -529,6 +532,302 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
   }
 }
 
+// ------------------------------------------------------------------ GEMM, direct-to-LDS pipeline
+// The forward product of pwa_gemm_kernel (same tile and tile order, N % 8 ==
+// 0) with the load path rebuilt around the LDS, run as a persistent kernel:
+//  - operands go from memory straight into LDS (buffer loads with an LDS
+//    destination): no registers hold staged data and no LDS stores are issued;
+//  - a workgroup takes tiles L0, L0 + G, L0 + 2G, ... (G = grid size), and its
+//    chunks (64 tokens) form one stream across its tiles.  X chunks rotate
+//    through three LDS buffers and W chunks through two: after the barrier
+//    that retires chunk q, chunk q + 3 of X (from HBM) and q + 2 of W (from
+//    L2) go into the buffers chunk q held, one load after each group of
+//    products (a burst of them right after the barrier would fill the
+//    address queue and stall every wave's issue);
+//  - that barrier sits between the two 32-token halves of chunk q's
+//    products: the second half's fragments are read before it and the next
+//    chunk's first half during the second half's products, two reads per
+//    four products;
+//  - a tile's epilogue runs while the next tile's first chunks load, so
+//    there is no per-tile prologue;
+//  - token row r of an X chunk stores its 16-byte unit u (8 columns) at slot
+//    u ^ f(r), f(r) = 4 (r mod 4) + (r / 8 mod 2).  A transposing read gives
+//    lane group g token rows 8g .. 8g + 7 (so the k axis of each lane is W's
+//    natural 16-byte chunk), and the four address lanes a of a row take
+//    units U0 + a with alternating 8-byte halves.  With the permutation each
+//    32-lane half of a read covers the 64 banks once.
+// Result lane (g, n) of tile 2p + t holds half t ^ (g mod 2) of unit U0 + g;
+// the epilogue swaps the two tiles of a pair on odd lane groups, so every
+// lane moves the 8 channels of one unit in one 16-byte access.
+__device__ __forceinline__ int xunit_swz(int r) { return 4 * (r & 3) + ((r >> 3) & 1); }
+
+// Position of a workgroup in its tile list: tile index ti, chunk k, and the
+// tile's coordinates as mixed-radix digits of L (n tile, head in the pair,
+// column tile, head pair), stepped by adding the grid size digit by digit.
+struct PwaCursor {
+  int ti, k, ntb, hp, colt, hpr;
+};
+
+template <int DP, bool FWD>
+__global__ void __launch_bounds__(512) pwa_gemm_dl_kernel(const u16* __restrict__ X, const u16* __restrict__ W,
+                                                          const u16* __restrict__ G, u16* __restrict__ out,
+                                                          int S, int N, int H, int d, int ncolt, int nnt) {
+  constexpr int SPT = 256 / DP;    // MSA rows per column tile
+  constexpr int C8 = DP / 8;       // 16-byte units per (s, token) row
+  constexpr int XB = 64 * 32;      // 16-byte units per X buffer (64 tokens x 256 columns)
+  constexpr int WB = 16 * 2 * 64;  // per W buffer (256 rows x 64 tokens, operand order)
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+  __shared__ u32x4 lds[3 * XB + 2 * WB];
+  const int wg = blockIdx.x, nwg = gridDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int g = lane >> 4, ln = lane & 15;
+  const int wc = wave & 3, wn = wave >> 2;
+  const int pairs = (H + 1) / 2;
+  const int ntiles = nnt * 2 * ncolt * pairs;
+  const int L0 = xcd_remap(wg, nwg);
+  if (L0 >= ntiles) return;  // whole workgroup, before any barrier
+  const int ntw = (ntiles - L0 + nwg - 1) / nwg;  // tiles of this workgroup
+  const int nkc = (N + 63) / 64;
+  const int nq = ntw * nkc;                      // chunks in its stream
+  const size_t srow = (size_t)N * H * d;
+  const size_t krow = (size_t)H * d;
+  const i32x4 xrs = rsrc_words(X, (uint32_t)((size_t)S * srow * 2));
+  const i32x4 wrs = rsrc_words(W, (uint32_t)((size_t)H * N * N * 2));
+
+  // grid size as digits of the tile numbering (n tile, head in pair, column tile, pair)
+  const int g0 = nwg % nnt, g1 = (nwg / nnt) & 1, g2 = (nwg / (2 * nnt)) % ncolt, g3 = nwg / (2 * nnt * ncolt);
+  auto start = [&](PwaCursor& c) {
+    c.ti = 0;
+    c.k = 0;
+    c.ntb = L0 % nnt;
+    c.hp = (L0 / nnt) & 1;
+    c.colt = (L0 / (2 * nnt)) % ncolt;
+    c.hpr = L0 / (2 * nnt * ncolt);
+  };
+  auto advance = [&](PwaCursor& c) {
+    if (++c.k < nkc) return;
+    c.k = 0;
+    ++c.ti;
+    c.ntb += g0;
+    int cy = c.ntb >= nnt;
+    c.ntb -= cy ? nnt : 0;
+    c.hp += g1 + cy;
+    cy = c.hp >= 2;
+    c.hp -= cy ? 2 : 0;
+    c.colt += g2 + cy;
+    cy = c.colt >= ncolt;
+    c.colt -= cy ? ncolt : 0;
+    c.hpr += g3 + cy;
+  };
+
+  // Staging: this wave fills four 1 KB blocks of each chunk.  X block b =
+  // 4 wave + i holds token rows 2b, 2b + 1 (lane l: row 2b + l / 32, slot
+  // l mod 32); W block b holds n tile b / 2, token half b mod 2 in operand
+  // order (lane 16 g + n: row n, tokens 8g .. 8g + 7 of the half).  Offsets
+  // are recomputed per load rather than kept in registers.
+  auto load_x1 = [&](int q, const PwaCursor& c, int i) {  // block i of this wave's share of X chunk q
+    const int h = 2 * c.hpr + c.hp, s0 = c.colt * SPT;
+    const int r = 2 * (4 * wave + i) + (lane >> 5);
+    const int u = (lane & 31) ^ xunit_swz(r);
+    const int sl = u / C8, c8 = u % C8;
+    const int k = 64 * c.k + r;
+    const bool ok = c.ti < ntw && h < H && s0 + sl < S && 8 * c8 < d && k < N;
+    const uint32_t off = ok ? (uint32_t)((((size_t)(s0 + sl) * srow + (size_t)k * krow + (size_t)h * d) + 8 * c8) * 2)
+                            : kOob;
+    lds_dma16(xrs, lds_addr(lds + (q % 3) * XB + (4 * wave + i) * 64), off);
+  };
+  auto load_w1 = [&](int q, const PwaCursor& c, int i) {  // block i of this wave's share of W chunk q
+    const int h = 2 * c.hpr + c.hp, n0 = c.ntb * 256;
+    const int b = 4 * wave + i, nr = 16 * (b >> 1) + ln, kk = 32 * (b & 1) + 8 * g;
+    const bool ok = c.ti < ntw && h < H && n0 + nr < N && 64 * c.k + kk < N;
+    const uint32_t base = (uint32_t)(((size_t)h * N * N + (size_t)n0 * N) * 2);
+    const uint32_t off = ok ? base + (uint32_t)((nr * N + kk + 64 * c.k) * 2) : kOob;
+    lds_dma16(wrs, lds_addr(lds + 3 * XB + (q & 1) * WB + (4 * wave + i) * 64), off);
+  };
+
+  // Fragment reads.  A operand (X^T) of tile 2p + t: lane (g, 4e + a) reads
+  // token rows 8g + e and 8g + 4 + e of the half at unit 8 wc + 4p + a, half
+  // t ^ (a mod 2); f of those rows is the same (it only sees r mod 4 and r / 8
+  // mod 2), so the four reads of a lane share one permuted slot per unit.
+  const int e = (lane >> 2) & 3, a = lane & 3;
+  const int rr = 8 * g + e;
+  const int fsw = xunit_swz(rr);
+  uint32_t xro[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) xro[p][t] = (uint32_t)((rr * 32 + ((8 * wc + 4 * p + a) ^ fsw)) * 16 + 8 * (t ^ (a & 1)));
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[4][8];
+#pragma unroll
+  for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) acc[ct][nt] = zero4;
+
+  // One half-chunk of products (fragments ua, ub) with the 16 reads of the
+  // next fragments (chunk q, half kh into va, vb) spread through it, two reads
+  // per four products.  Issuing all 16 reads first would leave more LDS
+  // operations outstanding than the counter can wait past, so the products
+  // would wait for the newest reads behind every other wave's.  Products go
+  // n tile by n tile (group j uses W fragment j and all four X fragments) and
+  // the X fragments are read first, so each fragment is read several groups
+  // before the next half needs it.  issue(j) runs after group j.
+  auto half_step = [&](auto read, int q, int kh, bf16x8 (&va)[4], bf16x8 (&vb)[8], const bf16x8 (&ua)[4],
+                       const bf16x8 (&ub)[8], auto&& issue) {
+    constexpr bool RD = decltype(read)::value;
+    const char* xb = reinterpret_cast<const char*>(lds + (q % 3) * XB) + kh * 32 * 512;
+    const u32x4* wb = lds + 3 * XB + (q & 1) * WB + kh * 64 + 8 * wn * 128 + lane;
+    u32x2 lo[4], hi[4];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if constexpr (RD) {
+        if (j < 4) {
+          const u16* p0 = reinterpret_cast<const u16*>(xb + xro[j >> 1][j & 1]);
+          lo[j] = lds_tr16(p0);
+          hi[j] = lds_tr16(p0 + 4 * 256);  // token rows + 4
+        } else {
+          vb[2 * (j - 4)] = as_bf8(wb[(2 * (j - 4)) * 128]);
+          vb[2 * (j - 4) + 1] = as_bf8(wb[(2 * (j - 4) + 1) * 128]);
+        }
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) acc[ct][j] = mfma32(ua[ct], ub[j], acc[ct][j]);
+      if constexpr (RD) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                    // four products
+      issue(j);
+    }
+    if constexpr (RD) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) va[ct] = as_bf8(u32x4{lo[ct][0], lo[ct][1], hi[ct][0], hi[ct][1]});
+    }
+  };
+  auto read_frags = [&](int q, int kh, bf16x8 (&af)[4], bf16x8 (&bf)[8]) {
+    const char* xb = reinterpret_cast<const char*>(lds + (q % 3) * XB) + kh * 32 * 512;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      const u16* p0 = reinterpret_cast<const u16*>(xb + xro[ct >> 1][ct & 1]);
+      const u32x2 lo = lds_tr16(p0);
+      const u32x2 hi = lds_tr16(p0 + 4 * 256);
+      af[ct] = as_bf8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+    }
+    const u32x4* wb = lds + 3 * XB + (q & 1) * WB;
+#pragma unroll
+    for (int nt = 0; nt < 8; ++nt) bf[nt] = as_bf8(wb[((8 * wn + nt) * 2 + kh) * 64 + lane]);
+  };
+
+  // Epilogue of the tile at cursor c: lane (g, n) of tiles 2p and 2p + 1
+  // holds the 8 channels of unit U = 8 wc + 4p + g of the column tile in row
+  // n: tile 2p + (g mod 2) has channels 0..3, the other tile 4..7.  Gate
+  // reads and output writes are buffer accesses with the range check, always
+  // 16 of each per lane, so the count of memory operations stays fixed.
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(FWD ? G : out, (uint32_t)((size_t)S * srow * 2));
+  const __amdgpu_buffer_rsrc_t ors = make_rsrc(out, (uint32_t)((size_t)S * srow * 2));
+  auto epilogue = [&](const PwaCursor& c) {
+    // the lane index goes through an empty asm so that the per-lane address
+    // terms below are computed here, not hoisted into registers that stay
+    // live through the whole product loop
+    int el = lane;
+    asm volatile("" : "+v"(el));
+    const int g = el >> 4, ln = el & 15;
+    const bool odd = (g & 1) != 0;
+    const int h = 2 * c.hpr + c.hp, s0 = c.colt * SPT, n0 = c.ntb * 256;
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const int col = 8 * (8 * wc + 4 * p + g);
+      const int s = s0 + col / DP, cc = col % DP;  // d % 8 == 0: all 8 channels are valid or none
+      const bool ok = h < H && s < S && cc < d;
+      const uint32_t base = (uint32_t)((s * srow + (size_t)(n0 + 128 * wn + ln) * krow + (size_t)h * d + cc) * 2);
+      auto off = [&](int nt) -> uint32_t {
+        return (ok && n0 + 128 * wn + 16 * nt + ln < N) ? base + (uint32_t)(32 * nt * krow) : kOob;
+      };
+#pragma unroll
+      for (int nb = 0; nb < 8; nb += 4) {
+      u32x4 gr[4];
+#pragma unroll
+      for (int nt = nb; nt < nb + 4; ++nt) gr[nt - nb] = FWD ? buf_load16(grs, off(nt)) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int nt = nb; nt < nb + 4; ++nt) {
+        const f32x4 lo = odd ? acc[2 * p + 1][nt] : acc[2 * p][nt];
+        const f32x4 hi = odd ? acc[2 * p][nt] : acc[2 * p + 1][nt];
+        float o[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        if constexpr (FWD) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            o[2 * k] *= sigmoidf_fast(bf2f(lo16(gr[nt - nb][k])));
+            o[2 * k + 1] *= sigmoidf_fast(bf2f(hi16(gr[nt - nb][k])));
+          }
+        }
+        const u32x4 v = {pack2(o[0], o[1]), pack2(o[2], o[3]), pack2(o[4], o[5]), pack2(o[6], o[7])};
+        __builtin_amdgcn_raw_buffer_store_b128(v, ors, off(nt), 0, 0);
+      }
+      }
+    }
+  };
+
+  // Every wave issues the same loads for every chunk index, past the end of
+  // its stream too: there all offsets fail the range check and zeros land in
+  // a retired buffer.  So the count of loads after any given one is fixed.
+  // Prologue: X chunks 0..2 and W chunks 0..1 in the order X0 W0 X1 W1 X2.
+  PwaCursor cx, cw, cc;
+  start(cx);
+  start(cw);
+  start(cc);
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load_x1(q, cx, i);
+    advance(cx);
+    if (q < 2) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) load_w1(q, cw, i);
+      advance(cw);
+    }
+  }
+  vm_wait<12>();
+  __syncthreads();
+  bf16x8 a0[4], b0[8], a1[4], b1[8];
+  read_frags(0, 0, a0, b0);
+  // Chunk q: half 0's products with half 1's reads; then, once this wave's
+  // loads of chunk q + 1 have landed, the barrier: every wave has finished
+  // reading chunk q and chunk q + 1 is complete.  After it half 1's products
+  // run with the reads of chunk q + 1's first half (past the end of the
+  // stream they read a retired buffer and are not used) and the loads of W
+  // chunk q + 2 and X chunk q + 3 into chunk q's buffers.  In issue order
+  // the loads after W(q + 1) are X(q + 2) only.  A tile's last chunk reads
+  // nothing during its second half; the wave then waits for chunk q + 2 (only
+  // X(q + 3) is newer), runs the epilogue and reads the next chunk's first
+  // half.  So the fragment registers are free during the epilogue and the
+  // next barrier needs no wait past the epilogue's writes.
+  using rd_t = std::integral_constant<bool, true>;
+  using nord_t = std::integral_constant<bool, false>;
+  int q = 0;
+  auto chunk = [&](auto read, bool wait) {
+    half_step(rd_t{}, q, 1, a1, b1, a0, b0, [](int) {});
+    if (wait) vm_wait<4>();
+    __syncthreads();
+    half_step(read, q + 1, 0, a0, b0, a1, b1, [&](int j) {
+      if (j < 4) load_w1(q + 2, cw, j);
+      else load_x1(q + 3, cx, j - 4);
+    });
+    advance(cw);
+    advance(cx);
+    ++q;
+  };
+  for (int ti = 0; ti < ntw; ++ti) {
+    for (int k = 0; k + 1 < nkc; ++k) chunk(rd_t{}, k > 0 || ti == 0);
+    chunk(nord_t{}, nkc == 1 && ti == 0 && q + 1 < nq);
+    vm_wait<4>();
+    epilogue(cc);
+    for (int k = 0; k < nkc; ++k) advance(cc);
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) acc[ct][nt] = zero4;
+    read_frags(q, 0, a0, b0);
+  }
+  vm_wait<0>();  // the loads past the end of the stream land before the LDS is released
+}
+
 // ------------------------------------------------------------------ backward elementwise
 __global__ void __launch_bounds__(256) pwa_bwd_pre_kernel(PwaArgs a) {
   const size_t n8 = (size_t)a.S * a.N * a.H * a.d / 8;
@@ -653,6 +952,19 @@ PwaPlan plan_pwa_bwd(int S, int N, int H, int d, bool /*bf16*/) {
   return pl;
 }
 
+// One workgroup per CU for the persistent product kernel (the device's CU
+// count, read once per device).
+static long long pwa_persistent_workgroups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
 // The vectorised row kernels need N % 8 == 0, N <= 1024 and an 8-byte
 // aligned key mask; other shapes take the element-wise kernels.
 static bool pwa_rows_vec(const PwaArgs& a) {
@@ -686,15 +998,23 @@ static hipError_t launch_gemm(const u16* X, const u16* W, const u16* G, u16* out
   const int pairs = (a.H + 1) / 2;
   const dim3 grid((unsigned)((long long)ncolt * nnt * 2 * pairs));
   const bool wal = (a.N & 7) == 0;
-#define PBA_GEMM_LAUNCH(DPV, WALV)                                                                              \
-  hipLaunchKernelGGL((pwa_gemm_kernel<DPV, FWD, WALV, false>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, \
-                     a.H, a.d, ncolt, nnt, PwaDwArgs{})
-  if (dp == 32) {
-    if (wal) PBA_GEMM_LAUNCH(32, true); else PBA_GEMM_LAUNCH(32, false);
+  // the pipelined kernel is persistent: one workgroup per CU walks its tiles
+  const dim3 pgrid((unsigned)std::min<long long>((long long)grid.x, pwa_persistent_workgroups()));
+  if (wal) {
+    if (dp == 32)
+      hipLaunchKernelGGL((pwa_gemm_dl_kernel<32, FWD>), pgrid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, a.H, a.d,
+                         ncolt, nnt);
+    else
+      hipLaunchKernelGGL((pwa_gemm_dl_kernel<64, FWD>), pgrid, dim3(512), 0, stream, X, W, G, out, a.S, a.N, a.H, a.d,
+                         ncolt, nnt);
   } else {
-    if (wal) PBA_GEMM_LAUNCH(64, true); else PBA_GEMM_LAUNCH(64, false);
+    if (dp == 32)
+      hipLaunchKernelGGL((pwa_gemm_kernel<32, FWD, false, false>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N,
+                         a.H, a.d, ncolt, nnt, PwaDwArgs{});
+    else
+      hipLaunchKernelGGL((pwa_gemm_kernel<64, FWD, false, false>), grid, dim3(512), 0, stream, X, W, G, out, a.S, a.N,
+                         a.H, a.d, ncolt, nnt, PwaDwArgs{});
   }
-#undef PBA_GEMM_LAUNCH
   return hipGetLastError();
 }
 
@@ -748,6 +1068,8 @@ hipError_t launch_pwa_bwd(const PwaArgs& args, bool /*bf16*/, hipStream_t stream
     const bool wal = (a.N & 7) == 0;
     const u16* dA = static_cast<const u16*>(a.da);
     u16* dV = static_cast<u16*>(a.dv);
+    // (the register-staged kernel: in this launch, next to the dw tiles, it
+    // measured faster than the pipelined one)
 #define PBA_PROD_LAUNCH(DPV, WALV)                                                                           \
   hipLaunchKernelGGL((pwa_gemm_kernel<DPV, false, WALV, true>), grid, dim3(512), 0, stream, dA, wt, nullptr, dV, \
                      a.S, a.N, a.H, a.d, ncolt, nnt, dw)

@@ -276,6 +276,10 @@ SMALL_PWA = [
     # N > 512 with a partial last 64-chunk round
     (4, 136, 2, 32, "random:9"),
     (2, 520, 1, 16, "tail:5"),
+    # N % 8 == 0 with channels padded to 64, an odd head count (a pair with
+    # one head) and ragged column and row tiles
+    (3, 136, 3, 64, "random:5"),
+    (5, 200, 2, 48, "none"),
 ]
 
 
