@@ -143,6 +143,148 @@ def time_loop(fn, steps, warmup, torch):
     return t0.elapsed_time(t1) / steps, wall
 
 
+def call_dist(fn, calls, torch, before=None):
+    """Per-call HIP-event durations on the current stream: median, p10, p90
+    (ms).  `before` runs ahead of each call, outside the timed interval."""
+    stream = torch.cuda.current_stream()
+    ms = []
+    for _ in range(calls):
+        if before is not None:
+            before()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    q = np.percentile(ms, [50, 10, 90])
+    return {"median_ms": round(float(q[0]), 4), "p10_ms": round(float(q[1]), 4), "p90_ms": round(float(q[2]), 4),
+            "calls": calls}
+
+
+COLD_BYTES = 512 << 20
+
+
+def call_protocols(fwd, bwd, step, torch, calls):
+    """Warm (back-to-back calls, caches as the previous call left them) and
+    cold (a 512 MiB buffer is written before each call, evicting L2 and most
+    of the 256 MB MALL) per-call distributions of fwd, bwd and fwd+bwd."""
+    fwd()
+    torch.cuda.synchronize()
+    out = {"warm": {"fwd": call_dist(fwd, calls, torch), "bwd": call_dist(bwd, calls, torch),
+                    "fwd_bwd": call_dist(step, calls, torch)}}
+    scratch = torch.empty(COLD_BYTES // 4, dtype=torch.float32, device="cuda")
+    flush = lambda: scratch.fill_(1.0)  # noqa: E731
+    out["cold"] = {"fwd": call_dist(fwd, calls, torch, flush), "bwd": call_dist(bwd, calls, torch, flush),
+                   "fwd_bwd": call_dist(step, calls, torch, flush)}
+    del scratch
+    return out
+
+
+def sclk_during(fn, torch, seconds=1.0):
+    """Shader clock read from the amdgpu sysfs files (current DPM level of
+    pp_dpm_sclk, or hwmon freq1_input) every few ms while `fn` runs back to
+    back for about `seconds`; None where the files are not readable."""
+    import glob
+    import threading
+    paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+    hw = sorted(glob.glob("/sys/class/drm/card*/device/hwmon/hwmon*/freq1_input"))
+
+    def read_mhz():
+        vals = []
+        for pth in paths:
+            try:
+                with open(pth) as f:
+                    for line in f:
+                        if "*" in line:
+                            vals.append(float(line.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz")))
+            except (OSError, ValueError, IndexError):
+                pass
+        if not vals:
+            for pth in hw:
+                try:
+                    with open(pth) as f:
+                        vals.append(float(f.read().strip()) / 1e6)
+                except (OSError, ValueError):
+                    pass
+        return max(vals) if vals else None
+
+    if read_mhz() is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = read_mhz()
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.005)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    a = np.array(samples)
+    return {"source": "pp_dpm_sclk" if paths else "hwmon freq1_input", "samples": int(a.size),
+            "median_mhz": round(float(np.median(a)), 1), "min_mhz": round(float(a.min()), 1),
+            "max_mhz": round(float(a.max()), 1)}
+
+
+def attn_bytes(B, H, N, d, elt):
+    """Minimum HBM bytes of one forward + backward call pair: 15 T + 3 |bias| +
+    4 |LSE| (forward reads Q, K, V, G, bias and writes O, LSE; backward reads
+    Q, K, V, G, O, dO, LSE, bias, writes dQ, dK, dV, dG, dBias and writes and
+    reads the D workspace)."""
+    T = B * H * N * d * elt
+    return 15 * T + 3 * H * N * N * elt + 4 * B * H * N * 4
+
+
+PEAK_FP32_MFMA_TFLOPS = 157.3
+
+
+def bench_attn_config(name, torch, pba, calls):
+    """fwd+bwd per-call median of one attention config, with %MFMA (against the
+    peak of its dtype), %HBM and the fraction of roofline max(MFMA floor, HBM
+    floor) / measured time."""
+    c = workloads.CONFIGS[name]
+    inp = workloads.attention_inputs(c, with_f64=False)
+    f32 = c.dtype == "f32"
+    dev = (lambda a: torch.from_numpy(a).cuda()) if f32 else (lambda a: to_dev(a, torch))
+    t = {n: dev(inp[n]) for n in ("q", "k", "v", "g", "bias", "dout")}
+    km = None if inp["key_mask"] is None else to_dev(inp["key_mask"], torch)
+    dt = torch.float32 if f32 else torch.bfloat16
+    ws = torch.empty(pba.pba_backward_workspace_bytes(c.B, c.H, c.N, c.d, dt), dtype=torch.uint8, device="cuda")
+    st = {}
+
+    def step():
+        st["out"], st["lse"] = pba.pba_forward(t["q"], t["k"], t["v"], t["g"], t["bias"], km)
+        pba.pba_backward(t["q"], t["k"], t["v"], t["g"], t["bias"], km, st["out"], st["lse"], t["dout"], workspace=ws)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    dist = call_dist(step, calls, torch)
+    ms = dist["median_ms"]
+    flops = attn_flops(c.B, c.H, c.N, c.d)
+    nbytes = attn_bytes(c.B, c.H, c.N, c.d, 4 if f32 else 2)
+    peak = PEAK_FP32_MFMA_TFLOPS if f32 else PEAK_BF16_TFLOPS
+    tf = flops / (ms * 1e-3) / 1e12
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    floor_ms = max(flops / (peak * 1e12), nbytes / (PEAK_HBM_GBS * 1e9)) * 1e3
+    return {"B": c.B, "H": c.H, "N": c.N, "d": c.d, "dtype": c.dtype, "fwd_bwd": dist,
+            "tflops": round(tf, 2), "mfma_frac": round(tf / peak, 4), "mfma_peak": peak,
+            "gbs": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+            "roofline_frac": round(floor_ms / ms, 4)}
+
+
 def cpu_baseline(cfg, target_s=15.0):
     """The fp64 oracle on a bounded sample of the same workload (rows of B)."""
     import oracle  # test infrastructure: used only for this baseline leg
@@ -431,6 +573,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--pwa-steps", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calls", type=int, default=30,
+                    help="per-call timings (warm and cold, median/p10/p90), the sampled shader clock and the "
+                         "all-config table use this many calls each; 0 skips them")
     ap.add_argument("--no-pwa", action="store_true")
     ap.add_argument("--next-steps", type=int, default=5,
                     help="timed steps of the MSA row attention workload (0 skips it)")
@@ -526,6 +671,16 @@ def main():
         "kernels_ms": {n: round(v, 4) for n, v in kernel_ms.items()},
     }
 
+    def bwd():
+        pba.pba_backward(t["q"], t["k"], t["v"], t["g"], t["bias"], km, state["out"], state["lse"], t["dout"],
+                         workspace=ws)
+
+    if args.calls > 0:
+        result["calls"] = call_protocols(fwd, bwd, step, torch, args.calls)
+        result["sclk"] = sclk_during(step, torch)
+        print("call protocols done", file=sys.stderr, flush=True)
+
+    pcalls = None
     if not args.no_pwa:
         del t, state, ws, timed_args, grads
         torch.cuda.empty_cache()
@@ -549,6 +704,13 @@ def main():
 
         ms_p, _ = time_loop(pstep, args.pwa_steps, 2, torch)
         ms_pf, _ = time_loop(pfwd, args.pwa_steps, 2, torch)
+
+        def pbwd():
+            pba.pair_weighted_avg_backward(pt["b"], pt["v"], pt["g"], None, pst["out"], pst["lse"], pt["dout"],
+                                           workspace=pws_b)
+
+        pcalls = call_protocols(pfwd, pbwd, pstep, torch, args.calls) if args.calls > 0 else None
+        psclk = sclk_during(pstep, torch) if args.calls > 0 else None
         gbs = pwa_bytes(pc.S, pc.N, pc.H, pc.d) / (ms_p * 1e-3) / 1e9
         gbs_f = pwa_fwd_bytes(pc.S, pc.N, pc.H, pc.d) / (ms_pf * 1e-3) / 1e9
         pgr = {"dv": torch.empty_like(pt["v"]), "dg": torch.empty_like(pt["g"]), "db": torch.empty_like(pt["b"])}
@@ -579,6 +741,18 @@ def main():
                          "traffic": traffic_for("pwa_weighted_sum")},
             "kernels_ms": {n: round(v, 4) for n, v in pkms.items()},
         }
+        if pcalls is not None:
+            result["pair_avg"]["calls"] = pcalls
+            result["pair_avg"]["sclk"] = psclk
+            med = pcalls["warm"]["fwd_bwd"]["median_ms"]
+            pflops, pb = pwa_flops(pc.S, pc.N, pc.H, pc.d), pwa_bytes(pc.S, pc.N, pc.H, pc.d)
+            floor_ms = max(pflops / (PEAK_BF16_TFLOPS * 1e12), pb / (PEAK_HBM_GBS * 1e9)) * 1e3
+            pair_cfg = {"S": pc.S, "H": pc.H, "N": pc.N, "d": pc.d, "dtype": "bf16",
+                        "fwd_bwd": pcalls["warm"]["fwd_bwd"],
+                        "tflops": round(pflops / (med * 1e-3) / 1e12, 2),
+                        "mfma_frac": round(pflops / (med * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+                        "gbs": round(pb / (med * 1e-3) / 1e9, 1), "hbm_frac": round(pb / (med * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                        "bytes": pb, "roofline_frac": round(floor_ms / med, 4)}
         del pt, pst, pws_f, pws_b, pgr, pout, plse
         torch.cuda.empty_cache()
 
@@ -614,6 +788,18 @@ def main():
             "fwd": {"ms": round(ms_mf, 4), "value": round(mval_f, 2), "unit": "TFLOP/s"},
         }
         del mt, mws, mst
+
+    if args.calls > 0:
+        # every config of the path: fwd+bwd per-call median, %MFMA, %HBM and the
+        # fraction of roofline (the other configs run only here)
+        table = {}
+        for name in ("tiny_fp32", "tri_attn_n384", "pairformer_apb", "dit_apb_x48"):
+            table[name] = bench_attn_config(name, torch, pba, args.calls)
+            torch.cuda.empty_cache()
+        if not args.no_pwa and pcalls is not None:
+            table["msa_pwa"] = pair_cfg
+        result["configs_table"] = table
+        print("config table done", file=sys.stderr, flush=True)
 
     if args.proj_steps > 0:
         result["bias_proj"] = bench_proj(args, torch, pba)

@@ -280,6 +280,10 @@ SMALL_PWA = [
     # one head) and ragged column and row tiles
     (3, 136, 3, 64, "random:5"),
     (5, 200, 2, 48, "none"),
+    # more product tiles (65 column tiles x 2 heads x 2 pairs = 260) than the
+    # persistent forward's workgroups, so some walk two tiles, one of them the
+    # empty fourth head of an odd count; ragged last column and row tiles
+    (517, 136, 3, 32, "random:9"),
 ]
 
 
