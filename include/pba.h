@@ -249,8 +249,12 @@ int pba_local_backward(int B, int H, int N, int d, int dtype,
  * benchmarks and profiles, not for production loops.  Kernel order:
  *   pba_backward_timed:                preprocess (dA, dG, row seeds), dK/dV +
  *                                      dBias partials together with dQ (one
- *                                      launch; two launches for PBA_F32),
- *                                      dBias reduction
+ *                                      launch; two, dK/dV then dQ, for PBA_F32
+ *                                      and where the dBias slab leaves room
+ *                                      for only one workgroup per CU), dBias
+ *                                      reduction (an entry of zero duration
+ *                                      when B == 1 and no slab is used: the
+ *                                      dK/dV tiles then store dBias directly)
  *   pair_weighted_avg_timed:           weight softmax, weighted sum + gate
  *   pair_weighted_avg_backward_timed:  weight softmax (w and w^T), preprocess
  *                                      (dA, dG), dV product together with the

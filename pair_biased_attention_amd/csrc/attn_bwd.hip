@@ -408,14 +408,25 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
       pj[0] = pj[1] = dsj[0] = dsj[1] = zero4;
     }
     if constexpr (!SLAB) {
-      float* part = a.partial + ((size_t)b * H + h) * N * N;
+      if (a.direct) {  // b == 0: dS is dBias
+        u16* db = static_cast<u16*>(a.dbias) + (size_t)h * N * N;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = qblk * 64 + 16 * (2 * qh + j) + 4 * g + r;
-          if (q < N && key < N) part[(size_t)q * N + key] = dsj[j][r];
-        }
+          for (int r = 0; r < 4; ++r) {
+            const int q = qblk * 64 + 16 * (2 * qh + j) + 4 * g + r;
+            if (q < N && key < N) db[(size_t)q * N + key] = f2bf(dsj[j][r]);
+          }
+      } else {
+        float* part = a.partial + ((size_t)b * H + h) * N * N;
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = qblk * 64 + 16 * (2 * qh + j) + 4 * g + r;
+            if (q < N && key < N) part[(size_t)q * N + key] = dsj[j][r];
+          }
+      }
     }
     // P and dS as 16x16x32 operands: k slot (g, v) is query row
     // 32qh + 16(v/4) + 4g + v%4 of the block
@@ -844,7 +855,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkdv_f32_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) slab[(qbase + qt0 + 4 * g + r) * kSlabStride + 16 * kt + n] += ds[r];
         } else {
-          float* part = a.partial + ((size_t)b * H + h) * N * N;
+          // one partial per batch row, or (a.direct, b == 0) dBias itself
+          float* part = a.direct ? static_cast<float*>(a.dbias) + (size_t)h * N * N
+                                 : a.partial + ((size_t)b * H + h) * N * N;
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int q = qbase + qt0 + 4 * g + r;
@@ -1071,13 +1084,16 @@ BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16) {
     pl.C = 1;
     pl.P = B;
   }
+  // a single batch row without a slab: its dS rows are dBias itself, stored
+  // in the output dtype by the main kernel (no partial, no reduction)
+  pl.direct = (!pl.slab && B == 1) ? 1 : 0;
   size_t off = 0;
   pl.off_da = off;
   off = align256(off + rows * d * (bf16 ? 2 : 4));
   pl.off_drow = off;  // fp32: D per row; bf16: (-log2(e) LSE, -D) pairs
   off = align256(off + rows * (bf16 ? 8 : 4));
   pl.off_partial = off;
-  off = align256(off + (size_t)pl.P * H * N * N * 4);
+  if (!pl.direct) off = align256(off + (size_t)pl.P * H * N * N * 4);
   pl.total = off;
   return pl;
 }
@@ -1184,8 +1200,10 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
     if ((e = hipGetLastError()) != hipSuccess) return e;
     timer_mark(timer, stream);
   }
-  // 4. dBias = sum of partials
-  {
+  // 4. dBias = sum of partials (already in place when the kernel stored it directly)
+  if (a.direct) {
+    timer_mark(timer, stream);
+  } else {
     const size_t count = (size_t)a.H * a.N * a.N;
     const dim3 grid((unsigned)((count / 4 + 255) / 256 + 1));
     if (bf16) hipLaunchKernelGGL(bias_grad_reduce_kernel<true>, grid, dim3(256), 0, stream, a.partial, a.P, count, a.dbias);

@@ -107,7 +107,7 @@ int prep_backward(int B, int H, int N, int d, int dtype, const void* q, const vo
   a.partial = reinterpret_cast<float*>(ws + pl.off_partial);
   a.B = B; a.H = H; a.N = N; a.d = d;
   a.scale = attn_scale(d);
-  a.P = pl.P; a.C = pl.C; a.slab = pl.slab;
+  a.P = pl.P; a.C = pl.C; a.slab = pl.slab; a.direct = pl.direct;
   return PBA_OK;
 }
 

@@ -48,6 +48,8 @@ struct BwdArgs {
   int P;            // number of batch chunks (partials)
   int C;            // batch rows per chunk
   int slab;         // 1: dS sums over the chunk in an LDS slab; 0: one partial per batch row
+  int direct;       // 1 (one batch row, no slab): dS is stored into dbias in the output
+                    // dtype and no partial or reduction is used
 };
 
 struct PwaArgs {
@@ -129,7 +131,7 @@ LocalPlan plan_local_bwd(int B, int H, int N, int d);
 // Workspace plan of the attention backward (byte offsets into one buffer).
 struct BwdPlan {
   size_t off_da, off_drow, off_partial, total;
-  int P, C, slab;
+  int P, C, slab, direct;
 };
 BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16);
 

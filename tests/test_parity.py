@@ -78,7 +78,9 @@ SMALL_ATTN = [
     (2, 2, 96, 48, "bf16", "none"),          # d = 48 (three 16-wide column tiles)
     (2, 2, 77, 64, "bf16", "random:5"),
     (2, 2, 70, 8, "bf16", "none"),
-    (1, 2, 150, 16, "bf16", "random:4"),     # B = 1: the bias gradient is dS itself
+    (1, 2, 150, 16, "bf16", "random:4"),     # B = 1: dS is stored straight into the bias gradient
+    (1, 2, 97, 64, "bf16", "tail:5"),        # the same in the 64-wide template, ragged N
+    (1, 3, 90, 32, "f32", "random:6"),       # the same on the fp32 path
     (40, 1, 64, 32, "bf16", "tail:3"),       # several batch chunks and partials
     (4, 2, 100, 32, "f32", "random:9"),
     (2, 2, 65, 48, "f32", "none"),
