@@ -19,6 +19,7 @@
 //   pwa_bwd_pre   dA = dO*sigmoid(G), dG = dO*O*(1-sigmoid(G))
 //   pwa_dw        split-K GEMM dw_p[h,i,j] = sum_{s in chunk p, c} dA[s,i,h,c] V[s,j,h,c]
 //   pwa_db        dw = sum_p dw_p (index order), db = w*(dw - sum_j w*dw)
+#include <atomic>
 #include <type_traits>
 
 #include "pba_device.h"
@@ -955,15 +956,15 @@ PwaPlan plan_pwa_bwd(int S, int N, int H, int d, bool /*bf16*/) {
 // One workgroup per CU for the persistent product kernel (the device's CU
 // count, read once per device).
 static long long pwa_persistent_workgroups() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // zero-initialised (static storage); 0 = not read yet
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);  // every thread stores the same value
   }
-  return cached[dev];
+  return n;
 }
 // The vectorised row kernels need N % 8 == 0, N <= 1024 and an 8-byte
 // aligned key mask; other shapes take the element-wise kernels.
