@@ -450,6 +450,22 @@ def counters_pass(args, torch, pba):
         pba.pba_local_backward(lt["q"], lt["k"], lt["v"], lt["g"], lt["bias"], lkm, o, l, lt["dout"])
     torch.cuda.synchronize()
     print(f"windowed attention steps done: {args.pwa_steps}", flush=True)
+    del lt, lkm
+    # the other attention configs (c1 tiny fp32, c3 Pairformer B = 1 d = 24, c4
+    # DiT 48 copies d = 48): their own kernel instances
+    for name in ("tiny_fp32", "pairformer_apb", "dit_apb_x48"):
+        c = workloads.CONFIGS[name]
+        cin = workloads.attention_inputs(c, with_f64=False)
+        f32 = c.dtype == "f32"
+        dev = (lambda a: torch.from_numpy(a).cuda()) if f32 else (lambda a: to_dev(a, torch))
+        ct = {n: dev(cin[n]) for n in ("q", "k", "v", "g", "bias", "dout")}
+        ckm = None if cin["key_mask"] is None else to_dev(cin["key_mask"], torch)
+        for _ in range(args.pwa_steps):
+            o, l = pba.pba_forward(ct["q"], ct["k"], ct["v"], ct["g"], ct["bias"], ckm)
+            pba.pba_backward(ct["q"], ct["k"], ct["v"], ct["g"], ct["bias"], ckm, o, l, ct["dout"])
+        torch.cuda.synchronize()
+        print(f"{name} steps done: {args.pwa_steps}", flush=True)
+        del ct, ckm
 
 
 def bench_proj(args, torch, pba):
