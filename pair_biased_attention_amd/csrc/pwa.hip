@@ -814,9 +814,12 @@ __global__ void __launch_bounds__(512) pwa_gemm_dl_kernel(const u16* __restrict_
     advance(cx);
     ++q;
   };
+  // Every barrier that publishes a chunk is preceded by this wave's wait for
+  // its loads of that chunk, except the first barrier after an epilogue: the
+  // wait before the epilogue already covered that chunk.
   for (int ti = 0; ti < ntw; ++ti) {
     for (int k = 0; k + 1 < nkc; ++k) chunk(rd_t{}, k > 0 || ti == 0);
-    chunk(nord_t{}, nkc == 1 && ti == 0 && q + 1 < nq);
+    chunk(nord_t{}, (nkc > 1 || ti == 0) && q + 1 < nq);
     vm_wait<4>();
     epilogue(cc);
     for (int k = 0; k < nkc; ++k) advance(cc);
