@@ -162,6 +162,10 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_f32_kernel(BwdArgs a) {
 // conflicts), through an identity product that reads the slab tile as its
 // accumulator: no VALU, no atomics, one owner per cell, fixed order.  The
 // chunk's sums are stored once as this workgroup's slice of partial p.
+// With NQR > 0 the same slab tiles live in registers instead (each wave owns
+// its tiles: NQR query blocks x 2 tiles x 4 floats per lane), which takes the
+// slab's read and write of every iteration off the LDS; the row loop is then
+// unrolled over the query blocks so every tile index is a constant.
 // Without `slab` (one row per chunk) dS goes straight to partial b.
 template <int DP>
 struct DkdvStage {
@@ -184,8 +188,10 @@ struct DkdvSmem {
 // One workgroup's tile: wg is its index among the nwg dK/dV workgroups, which
 // take the first slots of the backward grid (the dispatcher sends slot w to
 // XCD w mod 8); slab is the dynamic LDS [nqb][4 query tiles][2 key tiles]
-// [64 lanes] when SLAB.
-template <int DP, bool ALIGNED, bool SLAB>
+// [64 lanes] when SLAB and NQR == 0.  NQR > 0 (with SLAB): the slab is held
+// in registers; the host only picks it for an even number of 64-query blocks,
+// at most NQR.
+template <int DP, bool ALIGNED, bool SLAB, int NQR>
 __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm, f32x4* const slab,
                                                const BwdArgs& a) {
   constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
@@ -217,7 +223,12 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
   const bool keep_lane = key < N && (a.mask == nullptr || a.mask[key] != 0);
   const bool wave_masked = __any(!keep_lane);
 
-  if constexpr (SLAB) {
+  static_assert(NQR == 0 || (SLAB && NQR % 2 == 0 && NQR <= 6), "register slab: SLAB, even, at most 6 blocks");
+  f32x4 rslab[NQR > 0 ? NQR : 1][2];
+  if constexpr (NQR > 0) {
+#pragma unroll
+    for (int i = 0; i < NQR; ++i) rslab[i][0] = rslab[i][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if constexpr (SLAB) {
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     for (int idx = tid; idx < nqb * 8 * 64; idx += 256) slab[idx] = z;
   }
@@ -353,8 +364,11 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
   }
   __syncthreads();
 
-  auto step = [&](auto S_c) {
-    constexpr int S = decltype(S_c)::value;  // == it & 1: LDS buffer and register set of this iteration
+  // S_c: it & 1, the LDS buffer and register set of this iteration; QB_c:
+  // the query block (== cq) when the slab is in registers, else unused
+  auto step = [&](auto S_c, auto QB_c) {
+    constexpr int S = decltype(S_c)::value;
+    constexpr int QB = decltype(QB_c)::value;
     const int b = cb, qblk = cq;
     const bool last_q = qblk == nqb - 1;
     const u16* tQ = sQA[S];
@@ -376,7 +390,7 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
     }
     f32x4 slab0, slab1;
     f32x4* const st = slab + ((qblk * 4 + 2 * qh) * 2 + kt) * 64 + lane;
-    if constexpr (SLAB) {
+    if constexpr (SLAB && NQR == 0) {
       slab0 = st[0];
       slab1 = st[128];
     }
@@ -432,7 +446,10 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
     // 32qh + 16(v/4) + 4g + v%4 of the block
     const bf16x8 pb = pack8(pj[0], pj[1]);
     const bf16x8 dsb = pack8(dsj[0], dsj[1]);
-    if constexpr (SLAB) {
+    if constexpr (NQR > 0) {
+      rslab[QB][0] = mfma32(id_lo, dsb, rslab[QB][0]);
+      rslab[QB][1] = mfma32(id_hi, dsb, rslab[QB][1]);
+    } else if constexpr (SLAB) {
       // slab tiles (qblk, 2qh+j, kt) += dS rows of query tile 2qh+j
       st[0] = mfma32(id_lo, dsb, slab0);
       st[128] = mfma32(id_hi, dsb, slab1);
@@ -488,9 +505,42 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
       for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
     }
   };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  if constexpr (NQR > 0) {
+    // nqb is even, so iteration parity is the query block's parity
+    auto pair = [&](auto Q0_c) __attribute__((always_inline)) {
+      constexpr int Q0 = decltype(Q0_c)::value;
+      if constexpr (Q0 < NQR) {
+        if (Q0 < nqb) {
+          step(I0{}, Q0_c);
+          step(I1{}, std::integral_constant<int, Q0 + 1>{});
+        }
+      }
+    };
+    for (int b = b0; b < b1; ++b) {
+      pair(std::integral_constant<int, 0>{});
+      pair(std::integral_constant<int, 2>{});
+      pair(std::integral_constant<int, 4>{});
+    }
+    if (key < N) {
+      float* part = a.partial + ((size_t)p * H + h) * N * N;
+#pragma unroll
+      for (int qblk = 0; qblk < NQR; ++qblk)
+        if (qblk < nqb)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int q = qblk * 64 + 16 * (2 * qh + j) + 4 * g + r;
+              if (q < N) part[(size_t)q * N + key] = rslab[qblk][j][r];
+            }
+    }
+    return;
+  }
   for (int it = 0; it < T; it += 2) {
-    step(std::integral_constant<int, 0>{});
-    if (it + 1 < T) step(std::integral_constant<int, 1>{});
+    step(I0{}, I0{});
+    if (it + 1 < T) step(I1{}, I0{});
   }
 
   if (SLAB && key < N) {
@@ -526,7 +576,7 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
 // their XCD mapping) run the long dK/dV tiles and the dQ tiles fill the
 // slots they leave free, then the chip.  The two roles share the static LDS;
 // the dynamic LDS is the dK/dV slab or the dQ keep bytes.
-template <int DP, int QT, bool ALIGNED, bool SLAB>
+template <int DP, int QT, bool ALIGNED, bool SLAB, int NQR>
 __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nqblocks, int ndk, int ndk_slots) {
   constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
   constexpr int QW = 16 * QT, QBLK = 4 * QW;
@@ -543,7 +593,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   extern __shared__ f32x4 bwd_dyn_lds[];
   int wg = blockIdx.x, nwg = gridDim.x;
   if (wg < ndk_slots) {
-    if (wg < ndk) attn_dkdv_tile<DP, ALIGNED, SLAB>(wg, ndk, sm.dk, bwd_dyn_lds, a);
+    if (wg < ndk) attn_dkdv_tile<DP, ALIGNED, SLAB, NQR>(wg, ndk, sm.dk, bwd_dyn_lds, a);
     return;
   }
   wg -= ndk_slots;
@@ -1135,7 +1185,11 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
   // 2-3. dK, dV, dBias partials and dQ
   const int nkb = (a.N + 31) / 32;
   const int ndk = a.H * a.P * nkb;
-  const size_t slab_shmem = a.slab ? slab_bytes(a.N, bf16) : 0;
+  // bf16, d <= 32, an even number of at most 6 query blocks: the dBias slab
+  // sits in registers (no dynamic slab LDS)
+  const int nqb64 = (a.N + 63) / 64;
+  const bool reg_slab = bf16 && a.slab && dp == 32 && nqb64 % 2 == 0 && nqb64 <= 6;
+  const size_t slab_shmem = a.slab && !reg_slab ? slab_bytes(a.N, bf16) : 0;
   if (bf16) {
     // One launch, the dK/dV tiles first and then the dQ tiles, while the slab
     // still leaves room for two workgroups per CU (the dynamic LDS of a
@@ -1146,18 +1200,22 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
     const bool al = (a.N % 8) == 0;
     const int nqb = qt2 ? (a.N + 127) / 128 : (a.N + 63) / 64;
     const size_t keep_bytes = (size_t)((a.N + 63) / 64) * 64;
-    const bool fuse = dkdv_wgs_per_cu(a.N, a.d, true, a.slab != 0) >= 2;
+    const bool fuse = dkdv_wgs_per_cu(a.N, a.d, true, a.slab != 0 && !reg_slab) >= 2;
     const void* fn;
-#define PBA_BWD_FN(DPV, QTV, ALV, SLV) reinterpret_cast<const void*>(&attn_bwd_dq_bf16_kernel<DPV, QTV, ALV, SLV>)
-#define PBA_BWD_PICK(SLV)                                                                    \
-  if (dp == 32) {                                                                            \
-    if (qt2) fn = al ? PBA_BWD_FN(32, 2, true, SLV) : PBA_BWD_FN(32, 2, false, SLV);         \
-    else fn = al ? PBA_BWD_FN(32, 1, true, SLV) : PBA_BWD_FN(32, 1, false, SLV);             \
-  } else {                                                                                   \
-    if (qt2) fn = al ? PBA_BWD_FN(64, 2, true, SLV) : PBA_BWD_FN(64, 2, false, SLV);         \
-    else fn = al ? PBA_BWD_FN(64, 1, true, SLV) : PBA_BWD_FN(64, 1, false, SLV);             \
+#define PBA_BWD_FN(DPV, QTV, ALV, SLV, NQV) \
+  reinterpret_cast<const void*>(&attn_bwd_dq_bf16_kernel<DPV, QTV, ALV, SLV, NQV>)
+#define PBA_BWD_PICK(SLV)                                                                          \
+  if (dp == 32) {                                                                                  \
+    if (qt2) fn = al ? PBA_BWD_FN(32, 2, true, SLV, 0) : PBA_BWD_FN(32, 2, false, SLV, 0);         \
+    else fn = al ? PBA_BWD_FN(32, 1, true, SLV, 0) : PBA_BWD_FN(32, 1, false, SLV, 0);             \
+  } else {                                                                                         \
+    if (qt2) fn = al ? PBA_BWD_FN(64, 2, true, SLV, 0) : PBA_BWD_FN(64, 2, false, SLV, 0);         \
+    else fn = al ? PBA_BWD_FN(64, 1, true, SLV, 0) : PBA_BWD_FN(64, 1, false, SLV, 0);             \
   }
-    if (a.slab) {
+    if (reg_slab) {
+      if (qt2) fn = al ? PBA_BWD_FN(32, 2, true, true, 6) : PBA_BWD_FN(32, 2, false, true, 6);
+      else fn = al ? PBA_BWD_FN(32, 1, true, true, 6) : PBA_BWD_FN(32, 1, false, true, 6);
+    } else if (a.slab) {
       PBA_BWD_PICK(true)
     } else {
       PBA_BWD_PICK(false)
