@@ -74,6 +74,7 @@ def _check_attn_full(inp, res, dtype, tag):
 SMALL_ATTN = [
     # B, H, N, d, dtype, mask
     (3, 2, 200, 32, "bf16", "tail:7"),       # ragged N, tail mask, several key blocks
+    (3, 2, 380, 32, "bf16", "tail:9"),       # six query blocks, N % 8 != 0: dBias slab in registers, all block pairs
     (2, 3, 130, 24, "bf16", "random:10"),    # d padded 24 -> 32
     (2, 2, 96, 48, "bf16", "none"),          # d = 48 (three 16-wide column tiles)
     (2, 2, 77, 64, "bf16", "random:5"),
