@@ -152,10 +152,12 @@ __device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t num_bytes
 // tell which LDS bytes such a load writes, does not drain every one of them
 // before each later LDS read; callers order them with vm_wait and barriers.
 __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds_base, uint32_t byte_off) {
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  // the LDS base goes in through the m0 operand constraint, so the compiler
+  // itself writes m0 and knows the register is taken by this statement
+  asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "s"(lds_base), "v"(byte_off), "s"(rsrc)
-               : "memory", "m0");
+               : "v"(byte_off), "s"(rsrc), "{m0}"(lds_base)
+               : "memory");
 }
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void*)(p);

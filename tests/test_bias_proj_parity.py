@@ -180,13 +180,10 @@ def test_bias_proj_feeds_attention_end_to_end():
     pairs = {"bias": (to_f64(bias), rbias), "out": (to_f64(out), O)}
     pairs.update({n: (to_f64(ag[n]), rg[n]) for n in ("dq", "dv", "dbias")})
     pairs.update({n: (to_f64(pg[n]), rp[n]) for n in ("dz", "dgamma", "dbeta", "dw")})
-    # as in the attention parity tests: dq and dbias carry an absolute error of
-    # order eps |dO| |O| from D = rowsum(dO * O), so their bar is relative to |dV|
-    floor = float(np.max(np.abs(rg["dv"])))
     # every softmax row of dS sums to zero, so the attention's dbias sums to zero
     # over all positions of each head and dbeta = sum_h w[h] sum_p dbias[h, p]
     # vanishes analytically: its bar is relative to dgamma, the same kind of sum
     # over positions that does not vanish
     assert np.abs(rp["dbeta"]).max() < 1e-9 * np.abs(rp["dgamma"]).max()
-    floors = {"dq": floor, "dbias": floor, "dbeta": float(np.max(np.abs(rp["dgamma"])))}
+    floors = {"dbeta": float(np.max(np.abs(rp["dgamma"])))}
     check_all("proj+attention", pairs, TOL["bf16"], floors)
