@@ -78,7 +78,9 @@ typedef enum {
                               or channel count c                              */
   PBA_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned               */
   PBA_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
-  PBA_ERR_HIP = 6          /* the HIP runtime reported an error at launch     */
+  PBA_ERR_HIP = 6,         /* the HIP runtime reported an error at launch     */
+  PBA_ERR_SCRATCH = 7      /* pba_backward_noalloc: the call needs more than
+                              the static scratch area holds                   */
 } pba_status;
 
 /* ABI version; bumped on any change of signature or semantics. */
@@ -313,6 +315,31 @@ int pba_local_backward_timed(int B, int H, int N, int d, int dtype,
                              void* dq, void* dk, void* dv, void* dg, void* dbias,
                              void* workspace, size_t workspace_bytes, void* stream,
                              float* kernel_ms, int capacity, int* n_kernels);
+
+/*
+ * Backward attention that allocates nothing and takes no workspace, for
+ * callers that cannot allocate device memory: code recorded into a HIP graph,
+ * tight serving loops, harnesses that forbid allocation.  Arguments, results
+ * and kernels are those of pba_backward without the workspace pair.
+ *
+ * The workspace pba_backward would take lives in one static device array of
+ * PBA_NOALLOC_SCRATCH_BYTES bytes (128 MiB), which each GPU the library runs
+ * on holds from the library's first use on it until the process ends.  The
+ * first call on a device looks that device's copy up once (no allocation);
+ * later calls reuse it.  A call for which pba_backward_workspace_bytes(...)
+ * exceeds the array returns PBA_ERR_SCRATCH and enqueues nothing (the
+ * triangle workload B = N = 384, H = 4, d = 32 needs 63 MiB).  The kernels
+ * need no part of the array cleared: every value they read was written by
+ * the same call.  All calls on one GPU share the array, so calls that overlap
+ * in time on one GPU (two streams, or two host threads) race and give
+ * undefined results; calls on different GPUs are independent.
+ */
+#define PBA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int pba_backward_noalloc(int B, int H, int N, int d, int dtype,
+                         const void* q, const void* k, const void* v, const void* g,
+                         const void* bias, const uint8_t* key_mask,
+                         const void* out, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv, void* dg, void* dbias, void* stream);
 
 #ifdef __cplusplus
 }

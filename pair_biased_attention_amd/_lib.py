@@ -16,8 +16,9 @@ PBA_BF16 = 1
 
 STATUS = {
     0: "PBA_OK", 1: "PBA_ERR_NULL", 2: "PBA_ERR_SHAPE", 3: "PBA_ERR_UNSUPPORTED",
-    4: "PBA_ERR_ALIGN", 5: "PBA_ERR_WORKSPACE", 6: "PBA_ERR_HIP",
+    4: "PBA_ERR_ALIGN", 5: "PBA_ERR_WORKSPACE", 6: "PBA_ERR_HIP", 7: "PBA_ERR_SCRATCH",
 }
+NOALLOC_SCRATCH_BYTES = 128 << 20
 
 # exported symbol -> (restype, argtypes)
 _i, _sz, _p, _fl = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -54,6 +55,8 @@ SIGNATURES = {
                                      _p, _i, _p]),
     "pba_local_backward_timed": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
                                       _p, _p, _p, _p, _p, _p, _sz, _p, _p, _i, _p]),
+    "pba_backward_noalloc": (_i, [_i, _i, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                  _p, _p, _p, _p, _p, _p]),
 }
 
 _lib = None

@@ -5,12 +5,20 @@
 // allocates, frees, synchronises or prints.
 #include <math.h>
 
+#include <mutex>
+
 #include "pba.h"
 #include "pba_kernels.h"
 
+// The workspace of pba_backward_noalloc: one copy per GPU, created with the
+// code object on that device.  In host code this name is only a stand-in for
+// the symbol; kernels get the device address that hipGetSymbolAddress
+// returns for the current device (scratch_for_current_device below).
+static __device__ __align__(256) char scratch[PBA_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr long long kMaxElems = (1LL << 31) - 1;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -195,6 +203,25 @@ int prep_local_bwd(int B, int H, int N, int d, int dtype, const void* q, const v
   return PBA_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per
+// device (with that device current) and kept; no allocation.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_for_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PBA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return PBA_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PBA_OK;
+}
+
 // Measurement helper: runs `launch` with a kernel timer, waits for the last
 // event and reports each kernel's duration in milliseconds.
 template <typename F>
@@ -236,6 +263,9 @@ const char* pba_status_string(int status) {
     case PBA_ERR_ALIGN: return "PBA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case PBA_ERR_WORKSPACE: return "PBA_ERR_WORKSPACE: workspace missing or too small";
     case PBA_ERR_HIP: return "PBA_ERR_HIP: the HIP runtime reported a launch error";
+    case PBA_ERR_SCRATCH:
+      return "PBA_ERR_SCRATCH: the call needs more workspace than the 128 MiB static scratch area of "
+             "pba_backward_noalloc holds";
     default: return "unknown pba status";
   }
 }
@@ -269,6 +299,28 @@ int pba_backward(int B, int H, int N, int d, int dtype, const void* q, const voi
   pba::BwdArgs a{};
   const int st = prep_backward(B, H, N, d, dtype, q, k, v, g, bias, key_mask, out, lse, dout, dq, dk, dv, dg,
                                dbias, workspace, workspace_bytes, a);
+  if (st != PBA_OK) return st;
+  const hipError_t e = pba::launch_attn_bwd(a, dtype == PBA_BF16, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;
+}
+
+int pba_backward_noalloc(int B, int H, int N, int d, int dtype, const void* q, const void* k, const void* v,
+                         const void* g, const void* bias, const uint8_t* key_mask, const void* out,
+                         const float* lse, const void* dout, void* dq, void* dk, void* dv, void* dg, void* dbias,
+                         void* stream) {
+  // every argument check before the first HIP call
+  int st = check_attn_sizes(B, H, N, d, dtype);
+  if (st != PBA_OK) return st;
+  if ((st = all_nonnull({q, k, v, g, bias, out, lse, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
+  if ((st = all_aligned16({q, k, v, g, bias, out, dout, dq, dk, dv, dg, dbias})) != PBA_OK) return st;
+  if (!aligned4(lse)) return PBA_ERR_ALIGN;
+  const size_t need = pba::plan_attn_bwd(B, H, N, d, dtype == PBA_BF16).total;
+  if (need > PBA_NOALLOC_SCRATCH_BYTES) return PBA_ERR_SCRATCH;
+  void* ws = nullptr;
+  if ((st = scratch_for_current_device(&ws)) != PBA_OK) return st;
+  pba::BwdArgs a{};
+  st = prep_backward(B, H, N, d, dtype, q, k, v, g, bias, key_mask, out, lse, dout, dq, dk, dv, dg, dbias, ws,
+                     PBA_NOALLOC_SCRATCH_BYTES, a);
   if (st != PBA_OK) return st;
   const hipError_t e = pba::launch_attn_bwd(a, dtype == PBA_BF16, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PBA_OK : PBA_ERR_HIP;

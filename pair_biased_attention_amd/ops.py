@@ -86,6 +86,28 @@ def pba_backward(q, k, v, g, bias, key_mask, out, lse, dout, workspace=None):
     return {"dq": dq, "dk": dk, "dv": dv, "dg": dg, "dbias": dbias}
 
 
+def pba_backward_noalloc(q, k, v, g, bias, key_mask, out, lse, dout, grads=None):
+    """Backward without a workspace: the library's static scratch area takes
+    its place (see include/pba.h).  With `grads` (a dict of preallocated dq,
+    dk, dv, dg, dbias) nothing is allocated on the call path; otherwise the
+    gradients are allocated here.  Returns the dict of gradients."""
+    lib = _lib.load()
+    B, H, N, d = q.shape
+    shp = {n: (B, H, N, d) for n in ("q", "k", "v", "g", "out", "dout", "dq", "dk", "dv", "dg")}
+    shp.update(bias=(H, N, N), dbias=(H, N, N), key_mask=(N,), lse=(B, H, N))
+    if grads is None:
+        grads = {n: torch.empty_like(q) for n in ("dq", "dk", "dv", "dg")}
+        grads["dbias"] = torch.empty_like(bias)
+    _check_tensors(q, dict(q=q, k=k, v=v, g=g, bias=bias, key_mask=key_mask, out=out, lse=lse,
+                           dout=dout, **grads), shp)
+    st = lib.pba_backward_noalloc(B, H, N, d, _DT[q.dtype], _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(bias),
+                                  _ptr(key_mask), _ptr(out), _ptr(lse), _ptr(dout), _ptr(grads["dq"]),
+                                  _ptr(grads["dk"]), _ptr(grads["dv"]), _ptr(grads["dg"]), _ptr(grads["dbias"]),
+                                  _stream(q.device))
+    _lib.check("pba_backward_noalloc", st)
+    return grads
+
+
 def pair_weighted_avg_workspace_bytes(S, N, H, d, dtype) -> int:
     return int(_lib.load().pair_weighted_avg_workspace_bytes(S, N, H, d, _DT[dtype]))
 

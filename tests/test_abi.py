@@ -12,7 +12,7 @@ from pair_biased_attention_amd import _lib
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "pba.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS = 0, 1, 2, 3, 4, 5
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUP, ERR_ALIGN, ERR_WS, ERR_HIP, ERR_SCRATCH = 0, 1, 2, 3, 4, 5, 6, 7
 
 
 def _declared():
@@ -46,8 +46,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.pba_abi_version() == 3
-    for code in range(7):
+    assert lib.pba_abi_version() == 4
+    for code in range(8):
         assert lib.pba_status_string(code)
     assert b"unknown" in lib.pba_status_string(99)
 
@@ -117,6 +117,36 @@ def test_backward_validation(lib):
     assert call(ws=None) == ERR_WS
     assert call(wsb=need - 1) == ERR_WS
     assert call(ws=FAKE + 8) == ERR_ALIGN
+
+
+def test_backward_noalloc_validation(lib):
+    """Every argument check of the allocation-free backward runs before its
+    first HIP call, so these run without a GPU."""
+    B, H, N, d = 2, 2, 64, 32
+
+    def call(B_=B, N_=N, d_=d, null_at=None, misalign_at=None):
+        p = [FAKE] * 13
+        if null_at is not None:
+            p[null_at] = None
+        if misalign_at is not None:
+            p[misalign_at] = FAKE + 4
+        return lib.pba_backward_noalloc(B_, H, N_, d_, 1, p[0], p[1], p[2], p[3], p[4], None, p[5], p[6],
+                                        p[7], p[8], p[9], p[10], p[11], p[12], None)
+
+    assert call(d_=20) == ERR_UNSUP
+    assert call(B_=0) == ERR_SHAPE
+    for i in range(13):
+        assert call(null_at=i) == ERR_NULL, i
+    assert call(misalign_at=0) == ERR_ALIGN
+    # sizes whose workspace exceeds the static area: rejected before any HIP call
+    assert lib.pba_backward_workspace_bytes(1024, H, 768, d, 1) > _lib.NOALLOC_SCRATCH_BYTES
+    assert call(B_=1024, N_=768) == ERR_SCRATCH
+    assert b"128 MiB" in lib.pba_status_string(ERR_SCRATCH)
+    # the triangle workload fits
+    assert lib.pba_backward_workspace_bytes(384, 4, 384, 32, 1) <= _lib.NOALLOC_SCRATCH_BYTES
+    hdr = open(HEADER).read()
+    assert "#define PBA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)" in hdr
+    assert _lib.NOALLOC_SCRATCH_BYTES == 128 << 20
 
 
 def test_pwa_validation(lib):
