@@ -331,23 +331,20 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
 
   const bf16x8 id_l2hi[2] = {ident_cols_frag(lane, kLog2eHiBf16, 0), ident_cols_frag(lane, kLog2eHiBf16, 2)};
   const bf16x8 id_l2lo[2] = {ident_cols_frag(lane, kLog2eLoBf16, 0), ident_cols_frag(lane, kLog2eLoBf16, 2)};
-  const bf16x8 id_lo = ident_rows_frag(lane, 0), id_hi = ident_rows_frag(lane, 1);
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const u32x4 zero_u4 = {0u, 0u, 0u, 0u};
   bf16x8 kf[KC], vf[KC];
   f32x4 dk[CT], dv[CT];
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
-  // K enters the score product pre-multiplied by log2(e)/sqrt(d) (rounded
-  // once to bf16), so the products give S' in log2 units directly
-  const float kscale = a.scale * kLog2e;
+  // S' = c1 * Q K^T + (log2(e) * bias - log2(e) * LSE), c1 = log2(e) * scale:
+  // the score product takes the unscaled bf16 operands and is scaled in fp32
+  // by one FMA, so no operand is rounded after scaling
+  const float c1 = a.scale * kLog2e;
   auto take_kv = [&](const DkdvStage<DP>& st) {
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc) {
-      u32x4 ks;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) ks[e] = pack2(bf2f(lo16(st.k[kc][e])) * kscale, bf2f(hi16(st.k[kc][e])) * kscale);
-      kf[kc] = as_bf8(colok[kc] ? ks : zero_u4);
+      kf[kc] = as_bf8(colok[kc] ? st.k[kc] : zero_u4);
       vf[kc] = as_bf8(colok[kc] ? st.v[kc] : zero_u4);
     }
   };
@@ -402,11 +399,12 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
     for (int j = 0; j < 2; ++j) sacc[j] = mfma32(as_bf8(R[S].bias), id_l2lo[j], sacc[j]);
     fetch(R[S], fq);  // iteration it+2
     advance_fetch();
+    f32x4 qk[2] = {zero4, zero4};
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        sacc[j] = mfma32(qfr[j][kc], kf[kc], sacc[j]);
+        qk[j] = mfma32(qfr[j][kc], kf[kc], qk[j]);
         dp[j] = mfma32(afr[j][kc], vf[kc], dp[j]);
       }
     // P = exp2(S'), dS = P * (dP - D)
@@ -415,7 +413,7 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pj[j][r] = exp2_fast(sacc[j][r]);
+        pj[j][r] = exp2_fast(fmaf(qk[j][r], c1, sacc[j][r]));
         dsj[j][r] = pj[j][r] * dp[j][r];
       }
     if (wave_masked && !keep_lane) {  // masked keys: P = dS = 0
@@ -446,13 +444,14 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
     // 32qh + 16(v/4) + 4g + v%4 of the block
     const bf16x8 pb = pack8(pj[0], pj[1]);
     const bf16x8 dsb = pack8(dsj[0], dsj[1]);
+    // slab tiles (qblk, 2qh+j, kt) += dS of query tile 2qh+j, in fp32 and in
+    // the result layout (lane (g, n): queries 4g..4g+3 at key n)
     if constexpr (NQR > 0) {
-      rslab[QB][0] = mfma32(id_lo, dsb, rslab[QB][0]);
-      rslab[QB][1] = mfma32(id_hi, dsb, rslab[QB][1]);
+      rslab[QB][0] += dsj[0];
+      rslab[QB][1] += dsj[1];
     } else if constexpr (SLAB) {
-      // slab tiles (qblk, 2qh+j, kt) += dS rows of query tile 2qh+j
-      st[0] = mfma32(id_lo, dsb, slab0);
-      st[128] = mfma32(id_hi, dsb, slab1);
+      st[0] = slab0 + dsj[0];
+      st[128] = slab1 + dsj[1];
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -666,7 +665,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
 
   bf16x8 qf[QT][KC], daf[QT][KC];
   f32x4 nl4[QT], nd4[QT];  // -log2(e) LSE and -D of the lane's query, as accumulator seeds
-  const float qscale = a.scale * kLog2e;  // Q enters the products as Q log2(e) / sqrt(d)
+  // S' = c1 * Q K^T + (log2(e) * bias - log2(e) * LSE), c1 = log2(e) * scale:
+  // unscaled bf16 operands, the scale applied in fp32 by one FMA
+  const float c1 = a.scale * kLog2e;
 #pragma unroll
   for (int s = 0; s < QT; ++s) {
     const int qrow = q0 + 16 * s + ln;
@@ -678,8 +679,6 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
         rq = ld16(Q + (size_t)qrow * d + c0);
         rda = ld16(dA + (size_t)qrow * d + c0);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rq[e] = pack2(bf2f(lo16(rq[e])) * qscale, bf2f(hi16(rq[e])) * qscale);
       qf[s][kc] = as_bf8(rq);
       daf[s][kc] = as_bf8(rda);
     }
@@ -753,7 +752,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     }
     // S'^T and (dP - D)^T of every sub-tile first, then the elementwise work
     // and the dQ products as one block of code
-    f32x4 acc[QT][4], dp[QT][4];
+    f32x4 acc[QT][4], qk[QT][4], dp[QT][4];
 #pragma unroll
     for (int s = 0; s < QT; ++s) {
       u32x4 blo = bcur[s][0], bhi = bcur[s][1];
@@ -769,9 +768,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         dp[s][t] = nd4[s];
+        qk[s][t] = zero4;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          acc[s][t] = mfma32(kf[t][kc], qf[s][kc], acc[s][t]);
+          qk[s][t] = mfma32(kf[t][kc], qf[s][kc], qk[s][t]);
           dp[s][t] = mfma32(vf[t][kc], daf[s][kc], dp[s][t]);
         }
       }
@@ -781,7 +781,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[s][t][r] = exp2_fast(acc[s][t][r]) * dp[s][t][r];
+        for (int r = 0; r < 4; ++r) acc[s][t][r] = exp2_fast(fmaf(qk[s][t][r], c1, acc[s][t][r])) * dp[s][t][r];
       const bf16x8 s0 = pack8(acc[s][0], acc[s][1]);
       const bf16x8 s1 = pack8(acc[s][2], acc[s][3]);
 #pragma unroll

@@ -119,7 +119,8 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  // ---- per-wave query fragments (B operand of S^T = K Q^T), pre-scaled by 1/sqrt(d)
+  // ---- per-wave query fragments (B operand of S^T = K Q^T), unscaled: the
+  // product is scaled by 1/sqrt(d) in fp32
   bf16x8 qf[QT][KC];
 #pragma unroll
   for (int s = 0; s < QT; ++s) {
@@ -129,11 +130,7 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
       const int c0 = 32 * kc + 8 * g;
       u32x4 raw = u32x4{0, 0, 0, 0};
       if (qrow < N && c0 < d) raw = ld16(Q + (size_t)qrow * d + c0);
-      u32x4 sc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sc[e] = pack2(bf2f((u16)(raw[e] & 0xFFFFu)) * a.scale, bf2f((u16)(raw[e] >> 16)) * a.scale);
-      qf[s][kc] = as_bf8(sc);
+      qf[s][kc] = as_bf8(raw);
     }
   }
 
@@ -235,9 +232,13 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
       acc[s][2] = mfma32(id_lo, as_bf8(bhi), zero4);  // keys 16g + 8..11
       acc[s][3] = mfma32(id_hi, as_bf8(bhi), zero4);  // keys 16g + 12..15
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) {
+        f32x4 qk = zero4;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) acc[s][t] = mfma32(kf[t][kc], qf[s][kc], acc[s][t]);
+        for (int kc = 0; kc < KC; ++kc) qk = mfma32(kf[t][kc], qf[s][kc], qk);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[s][t][r] = fmaf(qk[r], a.scale, acc[s][t][r]);
+      }
     }
 
     // block maxima of every sub-tile, then one (rarely taken) rescale branch,
@@ -424,18 +425,14 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_res_kernel(FwdArgs a) {
   __syncthreads();  // the only barrier: from here on every wave runs alone
   if (q0 >= N) return;
 
-  const float qscale = a.scale * kLog2e;
+  // S' = c1 * Q K^T + log2(e) * bias - ref with c1 = log2(e) / sqrt(d): the
+  // product takes the unscaled bf16 operands and is scaled in fp32
+  const float c1 = a.scale * kLog2e;
   bf16x8 qf[QT][KC];
 #pragma unroll
   for (int s = 0; s < QT; ++s)
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      u32x4 sc;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        sc[e] = pack2(bf2f((u16)(qraw[s][kc][e] & 0xFFFFu)) * qscale, bf2f((u16)(qraw[s][kc][e] >> 16)) * qscale);
-      qf[s][kc] = as_bf8(sc);
-    }
+    for (int kc = 0; kc < KC; ++kc) qf[s][kc] = as_bf8(qraw[s][kc]);
 
   const bf16x8 i2h_lo = ident_rows_frag(lane, 0, kLog2eHiBf16), i2h_hi = ident_rows_frag(lane, 1, kLog2eHiBf16);
   const bf16x8 i2l_lo = ident_rows_frag(lane, 0, kLog2eLoBf16), i2l_hi = ident_rows_frag(lane, 1, kLog2eLoBf16);
@@ -529,9 +526,13 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_res_kernel(FwdArgs a) {
       acc[s][2] = mfma32(i2l_lo, bhi, mfma32(i2h_lo, bhi, c4));  // keys 16g + 8..11
       acc[s][3] = mfma32(i2l_hi, bhi, mfma32(i2h_hi, bhi, c4));  // keys 16g + 12..15
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+      for (int t = 0; t < 4; ++t) {
+        f32x4 qk = zero4;
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) acc[s][t] = mfma32(kf[t][kc], qf[s][kc], acc[s][t]);
+        for (int kc = 0; kc < KC; ++kc) qk = mfma32(kf[t][kc], qf[s][kc], qk);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[s][t][r] = fmaf(qk[r], c1, acc[s][t][r]);
+      }
     }
     // fast path: P = exp2(acc) and the block row sums
     f32x4 pv[QT][4];

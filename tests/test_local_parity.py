@@ -18,7 +18,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import TOL, check_all, d_rounding_slack, log, oracle_probs, to_dev, to_f64
+from gpu_util import TOL, check_all, log, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -58,36 +58,7 @@ def _check(inp, res, tag):
     if all(np.max(np.abs(gr[n])) <= 1e-12 * vmax for n in ("dq", "dk", "dbias")):
         floors = {"dq": vmax, "dk": vmax, "dbias": vmax}  # dS identically zero
 
-    def rerun(failing):
-        # the backward again from the oracle's O in storage precision, and
-        # the bound on what that rounding forces into dq, dk, dbias
-        # (d_rounding_slack), with the window bias gradient gathered from
-        # the dense [H, N, N] bound
-        names = failing
-        B, H, N, d = inp["q64"].shape
-        if B * H * N * N > 5_000_000:
-            return {}, {}
-        fwd = lambda v, g: oracle.local_attention_forward(inp["q64"], inp["k64"], v, g, inp["bias64"],
-                                                          inp["key_mask"])
-        P = oracle_probs(fwd, inp)
-        b = d_rounding_slack(inp, O, P, 1.0 / np.sqrt(d))
-        dense = b["dbias"]
-        win = np.zeros_like(inp["bias64"])
-        for i in range(N):
-            qb = i // 32
-            keys = 32 * qb - 48 + np.arange(128)
-            ok = (keys >= 0) & (keys < N)
-            win[:, qb, i - 32 * qb, ok] = dense[:, i, keys[ok]]
-        b["dbias"] = win
-        t = {n: to_dev(inp[n], "bf16") for n in ("q", "k", "v", "g", "bias", "dout")}
-        km = None if inp["key_mask"] is None else to_dev(inp["key_mask"], "bf16")
-        out = to_dev(workloads.bf16_round_bits(O.astype(np.float32)), "bf16")
-        lse = torch.from_numpy(L.astype(np.float32)).cuda()
-        g2 = pba.pba_local_backward(t["q"], t["k"], t["v"], t["g"], t["bias"], km, out, lse, t["dout"])
-        torch.cuda.synchronize()
-        return {n: to_f64(g2[n]) for n in names}, {n: b[n] for n in names}
-
-    check_all(tag, pairs, TOL["bf16"], floors, rerun)
+    check_all(tag, pairs, TOL["bf16"], floors)
     if inp["key_mask"] is not None:
         dead = inp["key_mask"] == 0
         assert np.all(res["dk"][:, :, dead] == 0) and np.all(res["dv"][:, :, dead] == 0)
@@ -106,10 +77,11 @@ SMALL = [
     (3, 2, 1, 32, "none"),          # a single atom: one query, one key
     (2, 1, 17, 32, "random:3"),     # one ragged query block and key tile
     # the narrowest head, two keys: dS = P1 P2 (dP1 - dP2) is a small difference
-    # of large terms, and the bf16 rounding of the pre-scaled Q/K operands
-    # moves dk past the bar
+    # of large terms, so the bf16 rounding of dA (a matrix-core operand) and of
+    # the stored O is amplified past the bar in dk (4.2e-2 of max|dk|)
     pytest.param(1, 3, 2, 8, "none", marks=pytest.mark.xfail(
-        reason="two-key softmax: bf16 rounding of the pre-scaled Q/K operands moves dk past 2e-2", strict=False)),
+        reason="two-key softmax: bf16 rounding of dA and of the stored O, amplified by the cancellation in dS, "
+               "moves dk past 2e-2", strict=False)),
 ]
 
 

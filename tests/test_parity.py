@@ -19,8 +19,7 @@ import pytest
 
 import oracle
 import workloads
-from gpu_util import (TOL, assert_close, bf16_round_f64, bits_to_f64, check_all, d_rounding_slack, log,
-                      oracle_probs, to_dev, to_f64)
+from gpu_util import TOL, assert_close, bits_to_f64, check_all, log, to_dev, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -56,19 +55,6 @@ def _run_attn(inp, dtype):
     return res
 
 
-def _run_attn_backward_from(inp, dtype, O, L):
-    """pba_backward on forward outputs supplied by the caller (the oracle's
-    O and lse) instead of the GPU forward's."""
-    dev = {n: to_dev(inp[n], dtype) for n in ("q", "k", "v", "g", "bias", "dout")}
-    km = None if inp["key_mask"] is None else to_dev(inp["key_mask"], dtype)
-    ob = workloads.bf16_round_bits(O.astype(np.float32)) if dtype == "bf16" else O.astype(np.float32)
-    out = to_dev(ob, dtype)
-    lse = torch.from_numpy(L.astype(np.float32)).cuda()
-    grads = pba.pba_backward(dev["q"], dev["k"], dev["v"], dev["g"], dev["bias"], km, out, lse, dev["dout"])
-    torch.cuda.synchronize()
-    return {k: to_f64(v) for k, v in grads.items()}
-
-
 def _check_attn_full(inp, res, dtype, tag, zero_ds=False):
     """Every element of every output against the oracle, each tensor against
     its own max |ref|.
@@ -92,18 +78,7 @@ def _check_attn_full(inp, res, dtype, tag, zero_ds=False):
         floor = float(np.max(np.abs(gr["dv"])))
         floors = {n: floor for n in ("dq", "dk", "dbias")}
 
-    def rerun(failing):
-        # bf16 small cases only: the backward again, from the oracle's O in
-        # storage precision, with the bound on what that rounding forces
-        if dtype != "bf16" or inp["q64"].size * inp["q64"].shape[2] > 50_000_000:
-            return {}, {}
-        fwd = lambda v, g: oracle.attention_forward(inp["q64"], inp["k64"], v, g, inp["bias64"], inp["key_mask"])
-        P = oracle_probs(fwd, inp)
-        b = d_rounding_slack(inp, O, P, 1.0 / math.sqrt(inp["q64"].shape[3]))
-        res2 = _run_attn_backward_from(inp, dtype, bf16_round_f64(O), L)
-        return {n: res2[n] for n in failing}, {n: b[n] for n in failing}
-
-    check_all(tag, pairs, tol, floors, rerun)
+    check_all(tag, pairs, tol, floors)
     return gr
 
 
@@ -216,13 +191,14 @@ def test_fully_masked_keys_and_single_key():
 
 
 # Two keys, bf16: dS = P1 P2 (dP1 - dP2) is a small difference of large terms,
-# so any bf16 rounding that reaches the scores or D is amplified.  The
-# kernels round Q and K pre-multiplied by log2(e)/sqrt(d) to bf16, which moves
-# dq, dk and dbias past the bar here (1e-1 of max|ref| for dq) even when the
-# backward is fed the oracle's own forward output.
+# so the bf16 rounding of the backward's storage-type operands is amplified:
+# dA = dO * sigmoid(G) enters dP = dA V^T as a bf16 matrix-core operand, and O
+# (stored in bf16) enters D = rowsum(dO * O).  In fp64 with exactly those two
+# roundings and nothing else, dq moves by 1.0e-1 of max|dq| here (7.1e-2 from
+# dA alone, 7.8e-2 from O alone), which is what the kernels measure.
 _ILL_CONDITIONED = pytest.mark.xfail(
-    reason="two-key softmax: the bf16 rounding of the pre-scaled Q/K operands moves dq, dk, dbias past 2e-2",
-    strict=False)
+    reason="two-key softmax: bf16 rounding of dA (an MFMA operand) and of the stored O, amplified by the "
+           "cancellation in dS, moves dq, dk, dbias past 2e-2", strict=False)
 TINY = [(B, H, N, d, dt) for (B, H, N, d) in [(1, 1, 1, 8), (1, 1, 2, 8), (2, 1, 3, 16), (1, 3, 17, 64)]
         for dt in ("bf16", "f32")]
 
