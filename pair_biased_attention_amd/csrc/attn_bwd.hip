@@ -177,7 +177,7 @@ struct DkdvStage {
 
 template <int DP>
 struct DkdvSmem {
-  static constexpr int kTile = 64 * (DP + 8);
+  static constexpr int kTile = 64 * TileLds<DP, 0>::kRowElems;
   u16 sQA[2][2 * kTile];  // [buffer][Q tile | dA tile]
   float sLD[2][2][64];    // [buffer][-log2(e) LSE | -D]
   // query-half combine area of dK, dV at the end of a row; written again
@@ -194,9 +194,10 @@ struct DkdvSmem {
 template <int DP, bool ALIGNED, bool SLAB, int NQR>
 __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm, f32x4* const slab,
                                                const BwdArgs& a) {
-  constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
+  constexpr int KC = DP / 32, CT = DP / 16;
   constexpr int NCH = DP / 32;
   constexpr int kTile = DkdvSmem<DP>::kTile;
+  using LQ = TileLds<DP, 0>;
   auto& sQA = sm.sQA;
   auto& sLD = sm.sLD;
   auto& comb = sm.comb;
@@ -319,8 +320,8 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
     u16* tQ = sQA[buf];
 #pragma unroll
     for (int c8i = 0; c8i < NCH; ++c8i) {
-      *reinterpret_cast<u32x4*>(&tQ[kap[c8i] * RS + col[c8i]]) = st.q[c8i];
-      *reinterpret_cast<u32x4*>(&tQ[kTile + kap[c8i] * RS + col[c8i]]) = st.da[c8i];
+      *reinterpret_cast<u32x4*>(&tQ[LQ::off(kap[c8i], col[c8i])]) = st.q[c8i];
+      *reinterpret_cast<u32x4*>(&tQ[kTile + LQ::off(kap[c8i], col[c8i])]) = st.da[c8i];
     }
     if (tid < 64) {
       // queries past N get P = exp2(-inf) = 0 (rows without keys carry a -inf seed)
@@ -381,9 +382,19 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
       dp[j] = *reinterpret_cast<const f32x4*>(&sLD[S][1][16 * qtile + 4 * g]);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        qfr[j][kc] = as_bf8(*reinterpret_cast<const u32x4*>(&tQ[(16 * qtile + n) * RS + 32 * kc + 8 * g]));
-        afr[j][kc] = as_bf8(*reinterpret_cast<const u32x4*>(&tA[(16 * qtile + n) * RS + 32 * kc + 8 * g]));
+        qfr[j][kc] = as_bf8(*reinterpret_cast<const u32x4*>(&tQ[LQ::off(16 * qtile + n, 32 * kc + 8 * g)]));
+        afr[j][kc] = as_bf8(*reinterpret_cast<const u32x4*>(&tA[LQ::off(16 * qtile + n, 32 * kc + 8 * g)]));
       }
+    }
+    // the transposed operands of the dV and dK products depend only on the
+    // staged tiles: read them with the others, so their latency is not on
+    // the path after the exponentials
+    bf16x8 trA[CT], trQ[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      const int r0 = 32 * qh + 4 * g;
+      trA[ct] = tr_frag_l<LQ>(tA, r0, r0 + 16, 16 * ct, lane);
+      trQ[ct] = tr_frag_l<LQ>(tQ, r0, r0 + 16, 16 * ct, lane);
     }
     f32x4 slab0, slab1;
     f32x4* const st = slab + ((qblk * 4 + 2 * qh) * 2 + kt) * 64 + lane;
@@ -455,9 +466,8 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
-      const int r0 = 32 * qh + 4 * g;
-      dv[ct] = mfma32(tr_frag<RS>(tA, r0, r0 + 16, 16 * ct, lane), pb, dv[ct]);
-      dk[ct] = mfma32(tr_frag<RS>(tQ, r0, r0 + 16, 16 * ct, lane), dsb, dk[ct]);
+      dv[ct] = mfma32(trA[ct], pb, dv[ct]);
+      dk[ct] = mfma32(trQ[ct], dsb, dk[ct]);
     }
     // ---- stage iteration it+1 into the other buffer (its loads were issued
     // one iteration ago)
@@ -577,12 +587,13 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
 // the dynamic LDS is the dK/dV slab or the dQ keep bytes.
 template <int DP, int QT, bool ALIGNED, bool SLAB, int NQR>
 __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nqblocks, int ndk, int ndk_slots) {
-  constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
+  constexpr int KC = DP / 32, CT = DP / 16;
   constexpr int QW = 16 * QT, QBLK = 4 * QW;
   constexpr int NCH = DP / 32;
+  using LK = TileLds<DP, 1>;
   struct DqSmem {
-    u16 sK[2][64 * RS];
-    u16 sV[2][64 * RS];
+    u16 sK[2][64 * LK::kRowElems];
+    u16 sV[2][64 * LK::kRowElems];
   };
   union Smem {
     DqSmem dq;
@@ -644,8 +655,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     for (int it = 0; it < NCH; ++it) {
       const int c = tid + 256 * it;
       const int kappa = c / (DP / 8), c8 = c % (DP / 8);
-      *reinterpret_cast<u32x4*>(&sK[buf][kappa * RS + 8 * c8]) = rk[it];
-      *reinterpret_cast<u32x4*>(&sV[buf][kappa * RS + 8 * c8]) = rv[it];
+      *reinterpret_cast<u32x4*>(&sK[buf][LK::off(kappa, 8 * c8)]) = rk[it];
+      *reinterpret_cast<u32x4*>(&sV[buf][LK::off(kappa, 8 * c8)]) = rv[it];
     }
   };
   u32x4 bnext[QT][2];
@@ -733,13 +744,13 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        kf[t][kc] = as_bf8(*reinterpret_cast<const u32x4*>(tK + (krow + 4 * t) * RS + 32 * kc + 8 * g));
-        vf[t][kc] = as_bf8(*reinterpret_cast<const u32x4*>(tV + (krow + 4 * t) * RS + 32 * kc + 8 * g));
+        kf[t][kc] = as_bf8(*reinterpret_cast<const u32x4*>(tK + LK::off(krow + 4 * t, 32 * kc + 8 * g)));
+        vf[t][kc] = as_bf8(*reinterpret_cast<const u32x4*>(tV + LK::off(krow + 4 * t, 32 * kc + 8 * g)));
       }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) kt[ct][m] = tr_frag<RS>(tK, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
+      for (int m = 0; m < 2; ++m) kt[ct][m] = tr_frag_l<LK>(tK, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
 
     u32x4 mlo, mhi;
 #pragma unroll

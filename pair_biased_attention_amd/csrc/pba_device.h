@@ -131,6 +131,43 @@ __device__ __forceinline__ bf16x8 tr_frag(const u16* tile, int rb0, int rb1, int
   return as_bf8(u32x4{lo[0], lo[1], hi[0], hi[1]});
 }
 
+// ---- LDS tile layouts of bf16 row-major tiles (rows of DP elements).
+// TileLds<DP, MODE>::off(r, c) is the element offset of row r, column c.
+// DP = 32: 64-byte rows, no padding; the four 16-byte units of row r sit at
+// unit position u ^ f(r).  Under the 64-bank model (16 lanes per cycle for a
+// 16-byte read, 32 lanes for an 8-byte one) f spreads both kinds of reads
+// over every bank:
+//   MODE 0 (query tiles: operand rows r = 16t + i, transposed reads of rows
+//   4g + e and 16 + 4g + e):  f = 2 * bit2(r) + bit3(r)
+//   MODE 1 (key tiles: operand rows 16(i/4) + i%4 + 4t, transposed reads of
+//   rows 16g + 8m + e):        f = 2 * bit4(r) + bit5(r)
+// For a fixed unit, the 16 rows of a 16-byte read fall on four 64-byte
+// offsets (r mod 4) times four distinct units; the eight rows of a 32-lane
+// transposed read fall on four offsets times two distinct unit pairs.
+// DP = 64: rows padded to 72 elements (144 bytes).
+template <int DP, int MODE>
+struct TileLds {
+  static constexpr int kRowElems = DP == 32 ? 32 : DP + 8;
+  __device__ static __forceinline__ int f(int r) {
+    return MODE == 0 ? 2 * ((r >> 2) & 1) + ((r >> 3) & 1) : 2 * ((r >> 4) & 1) + ((r >> 5) & 1);
+  }
+  __device__ static __forceinline__ int off(int r, int c) {
+    if constexpr (DP == 32) return r * 32 + ((((c >> 3) ^ f(r)) & 3) << 3) + (c & 7);
+    else return r * (DP + 8) + c;
+  }
+};
+
+// tr_frag for a TileLds layout: lane (g, j) gets rows rb0+e and rb1+e
+// (e = 0..3) at column c0 + j of the tile.
+template <class L>
+__device__ __forceinline__ bf16x8 tr_frag_l(const u16* tile, int rb0, int rb1, int c0, int lane) {
+  const int j = lane & 15;
+  const int e = j >> 2, a = j & 3;
+  const u32x2 lo = lds_tr16(tile + L::off(rb0 + e, c0 + 4 * a));
+  const u32x2 hi = lds_tr16(tile + L::off(rb1 + e, c0 + 4 * a));
+  return as_bf8(u32x4{lo[0], lo[1], hi[0], hi[1]});
+}
+
 // ---- vector-memory waits for loads the compiler does not track as producers
 // (buffer loads with an LDS destination): s_waitcnt with only the vector
 // counter set, at most N of this wave's vector-memory operations outstanding.
