@@ -90,7 +90,8 @@ int pba_abi_version(void);
 const char* pba_status_string(int status);
 
 /*
- * Forward attention.
+ * Forward attention (AlphaFold3 open-source implementation page, section
+ * "Model Efficiency": the pair bias is added after the key-query product).
  *   q, k, v, g : [B, H, N, d]   input type
  *   bias       : [H, N, N]      input type, shared by every b
  *   key_mask   : [N] uint8 or NULL
@@ -106,8 +107,10 @@ int pba_forward(int B, int H, int N, int d, int dtype,
 size_t pba_backward_workspace_bytes(int B, int H, int N, int d, int dtype);
 
 /*
- * Backward attention.  Inputs as in pba_forward, plus the forward's out and
- * lse and the upstream gradient dout [B, H, N, d].  Writes
+ * Backward attention (same section: the bias gradient is the gradient of the
+ * scaled QK^T product, and the broadcast of the bias over b becomes a
+ * reduction).  Inputs as in pba_forward, plus the forward's out and lse and
+ * the upstream gradient dout [B, H, N, d].  Writes
  *   dq, dk, dv, dg : [B, H, N, d]  input type
  *   dbias          : [H, N, N]     input type, = sum over b of dS[b]
  * workspace: device buffer of at least pba_backward_workspace_bytes(...)
@@ -125,7 +128,10 @@ int pba_backward(int B, int H, int N, int d, int dtype,
 size_t pair_weighted_avg_workspace_bytes(int S, int N, int H, int d, int dtype);
 
 /*
- * Forward pair-weighted average (no query-key term, no scale).  bf16 only.
+ * Forward pair-weighted average (AlphaFold3 open-source implementation page,
+ * section "MSA Pair Averaging Efficiency": weights from the pair bias alone,
+ * no query-key term, no scale, without the (S, N, N, H, d) intermediate of the
+ * naive form).  bf16 only.
  *   b          : [H, N, N]      input type (pair bias logits)
  *   key_mask   : [N] uint8 or NULL
  *   v, g       : [S, N, H, d]   input type (MSA row, token, head, channel)
@@ -144,8 +150,10 @@ int pair_weighted_avg(int S, int N, int H, int d, int dtype,
 size_t pair_weighted_avg_backward_workspace_bytes(int S, int N, int H, int d, int dtype);
 
 /*
- * Backward pair-weighted average (bf16 only).  Inputs as in pair_weighted_avg, plus the
- * forward's out and lse_w and dout [S, N, H, d].  Writes
+ * Backward pair-weighted average (bf16 only; same section, with the weights
+ * shared by every MSA row, so db is a reduction over s).  Inputs as in
+ * pair_weighted_avg, plus the forward's out and lse_w and dout [S, N, H, d].
+ * Writes
  *   dv, dg : [S, N, H, d]  input type
  *   db     : [H, N, N]     input type (reduced over the S MSA rows)
  * workspace as for pba_backward.

@@ -6,22 +6,28 @@
 // AlphaFold3 open-source implementation page, molayo1419.me).  P is recomputed
 // from Q, K, bias and the forward logsumexp instead of being stored.
 //
-// Four launches on the caller's stream, no host synchronisation:
+// Launches on the caller's stream, no host synchronisation:
 //   1. attn_bwd_pre      dA = dO*sigmoid(G), dG = dO*O*(1-sigmoid(G)),
 //                        D = rowsum(dO*O)  (= rowsum(P*dP), so dS = P*(dP-D)),
 //                        and (bf16) the row seeds (-log2(e) * LSE, -D) of the
-//                        two gradient kernels
-//   2. attn_bwd_dkdv     key-stationary: each workgroup owns 32 keys of one
-//                        head for a chunk of C batch rows; per row it walks all
-//                        queries, accumulates dK, dV in registers, and adds dS
-//                        into an LDS slab [N x 32] that sums over the chunk.
-//                        The slab is written once per chunk as an fp32 partial.
-//   3. attn_bwd_dq       query-stationary: recomputes P and dP per key block
-//                        and accumulates dQ = dS K in registers.
-//   4. bias_grad_reduce  dBias = sum of the P partials in index order.
+//                        two gradient roles
+//   2. one launch with two roles (bf16; two launches of the same kernel when
+//      the dK/dV role's LDS slab leaves room for only one workgroup per CU):
+//      - key-stationary dK/dV tiles, first in the grid: a workgroup owns 32
+//        keys of one head for a chunk of C batch rows; per row it walks all
+//        queries in 64-query blocks, accumulates dK, dV in registers and adds
+//        dS into a dBias slab [N x 32] (registers for d <= 32 and an even count
+//        of at most six query blocks, LDS otherwise) that sums over the chunk
+//        and is written once per chunk as an fp32 partial;
+//      - query-stationary dQ tiles, filling the rest: P and dP recomputed per
+//        64-key block, dQ = dS K accumulated in registers.
+//      (fp32: attn_bwd_dkdv_f32 and attn_bwd_dq_f32, two launches.)
+//   3. bias_grad_reduce  dBias = sum of the P partials in index order (skipped
+//                        for one batch row, where dS is stored as dBias).
 // No floating-point atomics anywhere; every slab cell is owned by a single
-// wave and updated in program order, so results are bitwise repeatable (the deterministic-reduction principle the Design-CP page states
-// for atomic float reductions).
+// wave and updated in program order, so results are bitwise repeatable (the
+// deterministic-reduction principle the Design-CP page states for atomic
+// float reductions).
 #include <algorithm>
 #include <type_traits>
 
