@@ -324,6 +324,219 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- key-split variant
+// For grids that leave most of the chip idle (a single batch row and a few
+// heads: B H ceil(N / 64) < 512 workgroups of the streaming kernel), more
+// waves come from splitting the keys.  A workgroup takes one 16-query tile of
+// one (b, h) and its four waves split the key blocks: wave w walks blocks
+// [w nkb / 4, (w + 1) nkb / 4).  Each wave stages its own K, V and bias
+// blocks into a private LDS region with buffer loads that write LDS directly,
+// so the key loop has no barrier: once a block's fragments are in registers
+// the next block's loads go into the same region while this block's products
+// run.  The four partial softmax states (reference maximum m_w, row sum l_w,
+// unnormalised output o_w) are then merged through LDS in wave order,
+//   M = max_w m_w,  O = sum_w e^(m_w - M) o_w / sum_w e^(m_w - M) l_w,
+// which is the online-softmax recurrence applied across the four key ranges.
+// The per-block arithmetic is the streaming kernel's with one query tile.
+// d <= 32 and N % 8 == 0 (16-byte bias rows) only.
+struct SplitWaveLds {
+  u16 k[64 * 32];    // TileLds<32, 1>
+  u16 v[64 * 32];    // TileLds<32, 1>
+  u32x4 bias[128];   // 16 query rows x 8 units; unit u of row q at slot u ^ ((q >> 1) & 7)
+};
+
+__device__ __forceinline__ int split_bias_slot(int q, int u) { return 8 * q + (u ^ ((q >> 1) & 7)); }
+
+__global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
+  using LK = TileLds<32, 1>;
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+  __shared__ SplitWaveLds wl[4];
+  extern __shared__ __attribute__((aligned(16))) uint32_t split_keep[];  // keep bytes of every key block
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int g = lane >> 4, ln = lane & 15;
+  const int N = a.N, d = a.d;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int qt = L % a.nqb;
+  const int bh_lin = L / a.nqb;
+  const int h = bh_lin / a.B, b = bh_lin % a.B;
+  const size_t bh = (size_t)b * a.H + h;
+  const int q0 = 16 * qt;
+  const int nkb = (N + 63) / 64;
+  const int blo = wave * nkb / 4, bhi = (wave + 1) * nkb / 4;
+  const uint32_t plane_bytes = (uint32_t)((size_t)N * d * 2);
+  const i32x4 krs = rsrc_words(static_cast<const u16*>(a.k) + bh * N * d, plane_bytes);
+  const i32x4 vrs = rsrc_words(static_cast<const u16*>(a.v) + bh * N * d, plane_bytes);
+  const i32x4 brs = rsrc_words(static_cast<const u16*>(a.bias) + (size_t)h * N * N, (uint32_t)((size_t)N * N * 2));
+  SplitWaveLds& my = wl[wave];
+
+  // Staging of key block kb.  K and V: load i fills LDS units 64 i + lane,
+  // i.e. row r = 16 i + lane / 4 at slot lane % 4, which holds channel unit
+  // (slot ^ f(r)) (units past d read as zeros; rows past N fail the range
+  // check).  Bias: load i fills slots 64 i + lane, i.e. query row
+  // q = 8 i + lane / 8 at slot lane % 8, holding keys kb + 8u .. + 7 with
+  // u = slot ^ ((q >> 1) & 7); keys past N there are masked below.
+  auto stage = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * i + (lane >> 2);
+      const int c8 = ((lane & 3) ^ LK::f(r)) & 3;
+      const uint32_t off = 8 * c8 < d ? (uint32_t)(((kb + r) * d + 8 * c8) * 2) : kOob;
+      lds_dma16(krs, lds_addr(my.k) + 1024 * i, off);
+      lds_dma16(vrs, lds_addr(my.v) + 1024 * i, off);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = 8 * i + (lane >> 3);
+      const int u = (lane & 7) ^ ((q >> 1) & 7);
+      const uint32_t off = q0 + q < N ? (uint32_t)(((size_t)(q0 + q) * N + kb + 8 * u) * 2) : kOob;
+      lds_dma16(brs, lds_addr(my.bias) + 1024 * i, off);
+    }
+  };
+  if (blo < bhi) stage(64 * blo);
+
+  for (int k = tid; k < nkb * 64; k += 256)
+    reinterpret_cast<uint8_t*>(split_keep)[k] = (k < N && (a.mask == nullptr || a.mask[k] != 0)) ? 1 : 0;
+
+  // this tile's query row as the B operand of S^T = K Q^T (unscaled)
+  const u16* Q = static_cast<const u16*>(a.q) + bh * N * d;
+  u32x4 rq = u32x4{0, 0, 0, 0};
+  if (q0 + ln < N && 8 * g < d) rq = ld16(Q + (size_t)(q0 + ln) * d + 8 * g);
+  const bf16x8 qf = as_bf8(rq);
+  __syncthreads();  // keep bytes
+
+  const bf16x8 id_lo = ident_rows_frag(lane, 0), id_hi = ident_rows_frag(lane, 1);
+  const bf16x8 ones = ones_frag();
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 oacc[2] = {zero4, zero4};
+  f32x4 lacc = zero4;
+  float mrun = kNegInf;
+  const int krow = 16 * (ln >> 2) + (ln & 3);
+
+  for (int blk = blo; blk < bhi; ++blk) {
+    const int kb = blk * 64;
+    vm_wait<0>();  // this block's staging (the wave's only loads in flight)
+    bf16x8 kf[4], vt[2][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) kf[t] = as_bf8(*reinterpret_cast<const u32x4*>(my.k + LK::off(krow + 4 * t, 8 * g)));
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) vt[ct][m] = tr_frag_l<LK>(my.v, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
+    u32x4 blo4 = my.bias[split_bias_slot(ln, 2 * g)], bhi4 = my.bias[split_bias_slot(ln, 2 * g + 1)];
+    uint32_t kw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kw[e] = split_keep[(kb >> 2) + 4 * g + e];  // keep bytes of keys 16g+4e .. +3
+    // every read of the region has returned: the next block may overwrite it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (blk + 1 < bhi) stage(kb + 64);
+
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t m01 = ((kw[e] & 0xFFu) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF00u) ? 0u : 0xFFFF0000u);
+      const uint32_t m23 = ((kw[e] & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF000000u) ? 0u : 0xFFFF0000u);
+      if (e < 2) {
+        blo4[2 * e] = (blo4[2 * e] & ~m01) | (kMaskedBias2 & m01);
+        blo4[2 * e + 1] = (blo4[2 * e + 1] & ~m23) | (kMaskedBias2 & m23);
+      } else {
+        bhi4[2 * (e - 2)] = (bhi4[2 * (e - 2)] & ~m01) | (kMaskedBias2 & m01);
+        bhi4[2 * (e - 2) + 1] = (bhi4[2 * (e - 2) + 1] & ~m23) | (kMaskedBias2 & m23);
+      }
+    }
+    f32x4 acc[4];
+    acc[0] = mfma32(id_lo, as_bf8(blo4), zero4);  // keys 16g + 0..3
+    acc[1] = mfma32(id_hi, as_bf8(blo4), zero4);  // keys 16g + 4..7
+    acc[2] = mfma32(id_lo, as_bf8(bhi4), zero4);  // keys 16g + 8..11
+    acc[3] = mfma32(id_hi, as_bf8(bhi4), zero4);  // keys 16g + 12..15
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x4 qk = mfma32(kf[t], qf, zero4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(qk[r], a.scale, acc[t][r]);
+    }
+    float m = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
+                    fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
+    m = fmaxf(m, fmaxf(fmaxf(fmaxf(acc[2][0], acc[2][1]), fmaxf(acc[2][2], acc[2][3])),
+                       fmaxf(fmaxf(acc[3][0], acc[3][1]), fmaxf(acc[3][2], acc[3][3]))));
+    const float mx = max_over_groups(m);
+    // lazy rescaling as in the streaming kernel: the reference moves only
+    // when a block's maximum passes it by more than 8 in log2 units
+    const bool grow = mx * kLog2e > mrun * kLog2e + 8.f;
+    if (__any(grow)) {
+      if (grow) {
+        const float mnew = fmaxf(mrun, mx);
+        const float alpha = exp2_fast((mrun - mnew) * kLog2e);  // 0 when mrun is -inf or masked
+        oacc[0] *= alpha;
+        oacc[1] *= alpha;
+        lacc *= alpha;
+        mrun = mnew;
+      }
+    }
+    const float msc = (mrun < kMaskedThreshold) ? kPosInf : mrun * kLog2e;  // every key so far masked: P = 0
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][r] = exp2_fast(fmaf(acc[t][r], kLog2e, -msc));
+    const bf16x8 p0 = pack8(acc[0], acc[1]);
+    const bf16x8 p1 = pack8(acc[2], acc[3]);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      oacc[ct] = mfma32(vt[ct][0], p0, oacc[ct]);
+      oacc[ct] = mfma32(vt[ct][1], p1, oacc[ct]);
+    }
+    lacc = mfma32(ones, p0, lacc);
+    lacc = mfma32(ones, p1, lacc);
+  }
+
+  // the merging thread's gate, requested before the barrier: query mq,
+  // channels 2 cp and 2 cp + 1
+  const int mq = tid >> 4, cp = tid & 15;
+  const int qrow = q0 + mq, c = 2 * cp;
+  const bool live = qrow < N && c < d;
+  const __amdgpu_buffer_rsrc_t grs = make_rsrc(static_cast<const u16*>(a.g) + bh * N * d, plane_bytes);
+  const uint32_t gw = __builtin_bit_cast(uint32_t, buf_load_f32(grs, live ? (uint32_t)((qrow * d + c) * 2) : kOob));
+
+  // partial state into the wave's own region: o_w [16 queries][32 channels]
+  // over the K tile, (m_w, l_w) per query over the V tile.  Lane (g, ln)
+  // holds channels 16 ct + 4 g + r of query ln.
+  float* part = reinterpret_cast<float*>(my.k);
+  float2* ml = reinterpret_cast<float2*>(my.v);
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[ln * 32 + 16 * ct + 4 * g + r] = oacc[ct][r];
+  if (g == 0) ml[ln] = float2{mrun, lacc[0]};
+  __syncthreads();
+
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float2 s = reinterpret_cast<const float2*>(wl[w].v)[mq];
+    if (s.y > 0.f) M = fmaxf(M, s.x);
+  }
+  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float2 s = reinterpret_cast<const float2*>(wl[w].v)[mq];
+    if (s.y > 0.f) {
+      const float f = exp2_fast((s.x - M) * kLog2e);
+      const float* pw = reinterpret_cast<const float*>(wl[w].k) + mq * 32 + c;
+      lsum = fmaf(f, s.y, lsum);
+      o0 = fmaf(f, pw[0], o0);
+      o1 = fmaf(f, pw[1], o1);
+    }
+  }
+  const float inv = lsum > 0.f ? __builtin_amdgcn_rcpf(lsum) : 0.f;
+  if (live) {
+    u16* O = static_cast<u16*>(a.out) + bh * N * d;
+    const float g0 = bf2f((u16)(gw & 0xFFFFu)), g1 = bf2f((u16)(gw >> 16));
+    *reinterpret_cast<uint32_t*>(O + (size_t)qrow * d + c) =
+        pack2(o0 * inv * sigmoidf_fast(g0), o1 * inv * sigmoidf_fast(g1));
+  }
+  if (cp == 0 && qrow < N)
+    a.lse[bh * N + qrow] = lsum > 0.f ? M + __builtin_amdgcn_logf(lsum) * kLn2 : kNegInf;
+}
+
 // ---------------------------------------------------------------- K/V-resident variant
 // For moderate N the whole K and V of one (b, h) fit in LDS: the workgroup
 // (NW waves, 16*QT queries each) stages them once, synchronises once, and
@@ -833,6 +1046,13 @@ hipError_t launch_attn_fwd(const FwdArgs& args, bool bf16, hipStream_t stream) {
       void* kargs[] = {&a};
       return hipLaunchKernel(fn, grid, dim3(nw * 64), kargs, lds, stream);
     }
+  }
+  // grids that would leave most CUs idle split the keys over the waves
+  if (dp == 32 && al && a.N > 64 && a.N <= 16384 && bhs * ((a.N + 63) / 64) < 512) {
+    a.nqb = (a.N + 15) / 16;
+    const size_t keep = (size_t)((a.N + 63) / 64) * 64;
+    hipLaunchKernelGGL(attn_fwd_split_kernel, dim3((unsigned)(bhs * a.nqb)), dim3(256), keep, stream, a);
+    return hipGetLastError();
   }
   // two query sub-tiles per wave when that still leaves enough workgroups
   const bool qt2 = dp == 32 && bhs * ((a.N + 127) / 128) >= 1024;
