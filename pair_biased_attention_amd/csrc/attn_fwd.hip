@@ -560,7 +560,12 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
 template <int DP, int QT, bool ALIGNED, int NW>
 __global__ void __launch_bounds__(NW * 64) attn_fwd_res_kernel(FwdArgs a) {
   constexpr int kResThreads = NW * 64;
-  constexpr int KC = DP / 32, CT = DP / 16, RS = DP + 8;
+  constexpr int KC = DP / 32, CT = DP / 16;
+  // K and V rows in the key-tile layout: 64-byte rows with permuted 16-byte
+  // units at d <= 32 (the operand reads and the transposed reads of V each
+  // cover every bank), padded 144-byte rows at d <= 64
+  using LK = TileLds<DP, 1>;
+  constexpr int RS = LK::kRowElems;
   constexpr int QW = 16 * QT, QBLK = NW * QW;
   constexpr int C8 = DP / 8;
   constexpr int RIT = 512 * C8 / kResThreads;  // staging chunks per thread (N up to 512)
@@ -628,8 +633,8 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_res_kernel(FwdArgs a) {
       const int c = tid + kResThreads * it;
       const int key = c / C8, c8 = c % C8;
       if (key < NP) {
-        *reinterpret_cast<u32x4*>(&sK[key * RS + 8 * c8]) = rk[it];
-        *reinterpret_cast<u32x4*>(&sV[key * RS + 8 * c8]) = rv[it];
+        *reinterpret_cast<u32x4*>(&sK[LK::off(key, 8 * c8)]) = rk[it];
+        *reinterpret_cast<u32x4*>(&sV[LK::off(key, 8 * c8)]) = rv[it];
       }
     }
     for (int k = tid; k < NP; k += kResThreads)
@@ -697,11 +702,11 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_res_kernel(FwdArgs a) {
     for (int t = 0; t < 4; ++t)
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        kf[t][kc] = as_bf8(*reinterpret_cast<const u32x4*>(tK + (krow + 4 * t) * RS + 32 * kc + 8 * g));
+        kf[t][kc] = as_bf8(*reinterpret_cast<const u32x4*>(tK + LK::off(krow + 4 * t, 32 * kc + 8 * g)));
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) vt[ct][m] = tr_frag<RS>(tV, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
+      for (int m = 0; m < 2; ++m) vt[ct][m] = tr_frag_l<LK>(tV, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
 
     // masked keys get the most negative bias (x log2(e): -inf); only blocks
     // that contain masked keys pay for the select
@@ -1031,7 +1036,7 @@ hipError_t launch_attn_fwd(const FwdArgs& args, bool bf16, hipStream_t stream) {
     const int np = (a.N + 63) / 64 * 64;
     const int qblk = nw * 16 * qt;
     const int nqb = (a.N + qblk - 1) / qblk;
-    const size_t lds = (size_t)2 * np * (dp + 8) * 2 + np;
+    const size_t lds = (size_t)2 * np * (dp == 32 ? 32 : dp + 8) * 2 + np;
     if (a.N <= 512 && bhs * nqb >= 512) {
       a.nqb = nqb;
       const dim3 grid((unsigned)(bhs * nqb));
