@@ -590,8 +590,9 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
 // ndk_slots workgroups (ndk rounded up to a multiple of 8, so both parts keep
 // their XCD mapping) run the long dK/dV tiles and the dQ tiles fill the
 // slots they leave free, then the chip.  The two roles share the static LDS;
-// the dynamic LDS is the dK/dV slab or the dQ keep bytes.
-template <int DP, int QT, bool ALIGNED, bool SLAB, int NQR>
+// the dynamic LDS is the dK/dV slab or the dQ keep bytes.  DK = false builds
+// the dQ role alone (fewer registers) for a launch that carries only dQ tiles.
+template <int DP, int QT, bool ALIGNED, bool SLAB, int NQR, bool DK = true>
 __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nqblocks, int ndk, int ndk_slots) {
   constexpr int KC = DP / 32, CT = DP / 16;
   constexpr int QW = 16 * QT, QBLK = 4 * QW;
@@ -608,9 +609,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   __shared__ Smem sm;
   extern __shared__ f32x4 bwd_dyn_lds[];
   int wg = blockIdx.x, nwg = gridDim.x;
-  if (wg < ndk_slots) {
-    if (wg < ndk) attn_dkdv_tile<DP, ALIGNED, SLAB, NQR>(wg, ndk, sm.dk, bwd_dyn_lds, a);
-    return;
+  if constexpr (DK) {
+    if (wg < ndk_slots) {
+      if (wg < ndk) attn_dkdv_tile<DP, ALIGNED, SLAB, NQR>(wg, ndk, sm.dk, bwd_dyn_lds, a);
+      return;
+    }
   }
   wg -= ndk_slots;
   nwg -= ndk_slots;
@@ -1221,6 +1224,8 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
     const void* fn;
 #define PBA_BWD_FN(DPV, QTV, ALV, SLV, NQV) \
   reinterpret_cast<const void*>(&attn_bwd_dq_bf16_kernel<DPV, QTV, ALV, SLV, NQV>)
+#define PBA_BWD_FN6(DPV, QTV, ALV) \
+  reinterpret_cast<const void*>(&attn_bwd_dq_bf16_kernel<DPV, QTV, ALV, false, 0, false>)
 #define PBA_BWD_PICK(SLV)                                                                          \
   if (dp == 32) {                                                                                  \
     if (qt2) fn = al ? PBA_BWD_FN(32, 2, true, SLV, 0) : PBA_BWD_FN(32, 2, false, SLV, 0);         \
@@ -1237,24 +1242,34 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
     } else {
       PBA_BWD_PICK(false)
     }
+    // the dQ-only launch of the unfused case takes the dQ role alone
+    const void* fn_dq;
+    if (dp == 32) {
+      if (qt2) fn_dq = al ? PBA_BWD_FN6(32, 2, true) : PBA_BWD_FN6(32, 2, false);
+      else fn_dq = al ? PBA_BWD_FN6(32, 1, true) : PBA_BWD_FN6(32, 1, false);
+    } else {
+      fn_dq = al ? PBA_BWD_FN6(64, 1, true) : PBA_BWD_FN6(64, 1, false);
+    }
 #undef PBA_BWD_PICK
 #undef PBA_BWD_FN
+#undef PBA_BWD_FN6
     const size_t shmem_max = std::max(slab_shmem, keep_bytes);
     // the slab can exceed the default 64 KiB dynamic LDS limit
     if (shmem_max > 64 * 1024 &&
         (e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem_max)) != hipSuccess)
       return e;
-    auto launch = [&](unsigned grid, int ndk_arg, int slots_arg, size_t shmem) -> hipError_t {
+    auto launch = [&](const void* f, unsigned grid, int ndk_arg, int slots_arg, size_t shmem) -> hipError_t {
       int nqb_arg = nqb;
       void* kargs[] = {&a, &nqb_arg, &ndk_arg, &slots_arg};
-      return hipLaunchKernel(fn, dim3(grid), dim3(256), kargs, shmem, stream);
+      return hipLaunchKernel(f, dim3(grid), dim3(256), kargs, shmem, stream);
     };
     if (fuse) {
-      if ((e = launch((unsigned)(ndk_slots + bhs * nqb), ndk, ndk_slots, shmem_max)) != hipSuccess) return e;
+      if ((e = launch(fn, (unsigned)(ndk_slots + bhs * nqb), ndk, ndk_slots, shmem_max)) != hipSuccess) return e;
     } else {
-      if ((e = launch((unsigned)ndk_slots, ndk, ndk_slots, std::max(slab_shmem, (size_t)16))) != hipSuccess) return e;
+      if ((e = launch(fn, (unsigned)ndk_slots, ndk, ndk_slots, std::max(slab_shmem, (size_t)16))) != hipSuccess)
+        return e;
       timer_mark(timer, stream);
-      if ((e = launch((unsigned)(bhs * nqb), 0, 0, keep_bytes)) != hipSuccess) return e;
+      if ((e = launch(fn_dq, (unsigned)(bhs * nqb), 0, 0, keep_bytes)) != hipSuccess) return e;
     }
     timer_mark(timer, stream);
   } else {
