@@ -574,6 +574,166 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
   }
 }
 
+// ------------------------------------------------------------------ 3b. dQ, key-split (small grids)
+// For grids that leave most CUs idle (a single batch row and a few heads),
+// the dQ tiles split the keys the way the key-split forward does: one
+// 16-query tile per workgroup, wave w takes key blocks [w nkb / 4,
+// (w + 1) nkb / 4), stages its own K, V and bias blocks into a private LDS
+// region with LDS-destination loads (no barrier in the key loop), and the
+// four partial dQ tiles are summed in wave order through LDS at the end.  Per
+// block the arithmetic is the dQ role's with one query tile.  d <= 32 and
+// N % 8 == 0 only.
+struct DqSplitWaveLds {
+  u16 k[64 * 32];    // TileLds<32, 1>
+  u16 v[64 * 32];    // TileLds<32, 1>
+  u32x4 bias[128];   // bias_rows_slot layout
+};
+
+__device__ __forceinline__ void attn_dq_split_tile(int wg, int nwg, DqSplitWaveLds (&wl)[4], uint32_t* keep,
+                                                   const BwdArgs& a, int nqt) {
+  using LK = TileLds<32, 1>;
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int g = lane >> 4, ln = lane & 15;
+  const int N = a.N, d = a.d;
+  const int L = xcd_remap(wg, nwg);
+  const int qt = L % nqt;
+  const int bh_lin = L / nqt;
+  const int h = bh_lin / a.B, b = bh_lin % a.B;
+  const size_t bh = (size_t)b * a.H + h;
+  const int q0 = 16 * qt;
+  const int nkb = (N + 63) / 64;
+  const int blo = wave * nkb / 4, bhi = (wave + 1) * nkb / 4;
+  const uint32_t plane_bytes = (uint32_t)((size_t)N * d * 2);
+  const i32x4 krs = rsrc_words(static_cast<const u16*>(a.k) + bh * N * d, plane_bytes);
+  const i32x4 vrs = rsrc_words(static_cast<const u16*>(a.v) + bh * N * d, plane_bytes);
+  const i32x4 brs = rsrc_words(static_cast<const u16*>(a.bias) + (size_t)h * N * N, (uint32_t)((size_t)N * N * 2));
+  DqSplitWaveLds& my = wl[wave];
+
+  // staging of key block kb: K and V load i fills LDS units 64 i + lane (row
+  // 16 i + lane / 4, slot lane % 4 holding channel unit slot ^ f(row); units
+  // past d read as zeros, rows past N fail the range check); bias load i
+  // fills slots 64 i + lane (query row 8 i + lane / 8)
+  auto stage = [&](int kb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * i + (lane >> 2);
+      const int c8 = ((lane & 3) ^ LK::f(r)) & 3;
+      const uint32_t off = 8 * c8 < d ? (uint32_t)(((kb + r) * d + 8 * c8) * 2) : kOob;
+      lds_dma16(krs, lds_addr(my.k) + 1024 * i, off);
+      lds_dma16(vrs, lds_addr(my.v) + 1024 * i, off);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = 8 * i + (lane >> 3);
+      const int u = (lane & 7) ^ ((q >> 1) & 7);
+      const uint32_t off = q0 + q < N ? (uint32_t)(((size_t)(q0 + q) * N + kb + 8 * u) * 2) : kOob;
+      lds_dma16(brs, lds_addr(my.bias) + 1024 * i, off);
+    }
+  };
+  if (blo < bhi) stage(64 * blo);
+  for (int k = tid; k < nkb * 64; k += 256)
+    reinterpret_cast<uint8_t*>(keep)[k] = (k < N && (a.mask == nullptr || a.mask[k] != 0)) ? 1 : 0;
+
+  // this lane's query row: Q and dA as B operands, (-log2(e) LSE, -D) as seeds
+  const int qrow = q0 + ln;
+  u32x4 rq = u32x4{0, 0, 0, 0}, rda = u32x4{0, 0, 0, 0};
+  if (qrow < N && 8 * g < d) {
+    rq = ld16(static_cast<const u16*>(a.q) + bh * N * d + (size_t)qrow * d + 8 * g);
+    rda = ld16(static_cast<const u16*>(a.da) + bh * N * d + (size_t)qrow * d + 8 * g);
+  }
+  const bf16x8 qf = as_bf8(rq), daf = as_bf8(rda);
+  float nl = kNegInf, nd = 0.f;  // rows without keys carry a -inf seed: P = 0
+  if (qrow < N) {
+    const float2 sd = a.seed[bh * N + qrow];
+    nl = sd.x;
+    nd = sd.y;
+  }
+  const f32x4 nl4 = {nl, nl, nl, nl}, nd4 = {nd, nd, nd, nd};
+  const float c1 = a.scale * kLog2e;
+  const bf16x8 id2h_lo = ident_rows_frag(lane, 0, kLog2eHiBf16), id2h_hi = ident_rows_frag(lane, 1, kLog2eHiBf16);
+  const bf16x8 id2l_lo = ident_rows_frag(lane, 0, kLog2eLoBf16), id2l_hi = ident_rows_frag(lane, 1, kLog2eLoBf16);
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  f32x4 dq[2] = {zero4, zero4};
+  const int krow = 16 * (ln >> 2) + (ln & 3);
+  __syncthreads();  // keep bytes
+
+  for (int blk = blo; blk < bhi; ++blk) {
+    const int kb = blk * 64;
+    vm_wait<0>();  // this block's staging (the wave's only loads in flight)
+    bf16x8 kf[4], vf[4], kt[2][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      kf[t] = as_bf8(*reinterpret_cast<const u32x4*>(my.k + LK::off(krow + 4 * t, 8 * g)));
+      vf[t] = as_bf8(*reinterpret_cast<const u32x4*>(my.v + LK::off(krow + 4 * t, 8 * g)));
+    }
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) kt[ct][m] = tr_frag_l<LK>(my.k, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
+    u32x4 blo4 = my.bias[bias_rows_slot(ln, 2 * g)], bhi4 = my.bias[bias_rows_slot(ln, 2 * g + 1)];
+    uint32_t kw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) kw[e] = keep[(kb >> 2) + 4 * g + e];  // keep bytes of keys 16g+4e .. +3
+    // every read of the region has returned: the next block may overwrite it
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (blk + 1 < bhi) stage(kb + 64);
+
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t m01 = ((kw[e] & 0xFFu) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF00u) ? 0u : 0xFFFF0000u);
+      const uint32_t m23 = ((kw[e] & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF000000u) ? 0u : 0xFFFF0000u);
+      if (e < 2) {
+        blo4[2 * e] = (blo4[2 * e] & ~m01) | (kMaskedBias2 & m01);
+        blo4[2 * e + 1] = (blo4[2 * e + 1] & ~m23) | (kMaskedBias2 & m23);
+      } else {
+        bhi4[2 * (e - 2)] = (bhi4[2 * (e - 2)] & ~m01) | (kMaskedBias2 & m01);
+        bhi4[2 * (e - 2) + 1] = (bhi4[2 * (e - 2) + 1] & ~m23) | (kMaskedBias2 & m23);
+      }
+    }
+    f32x4 acc[4];
+    acc[0] = mfma32(id2l_lo, as_bf8(blo4), mfma32(id2h_lo, as_bf8(blo4), nl4));
+    acc[1] = mfma32(id2l_hi, as_bf8(blo4), mfma32(id2h_hi, as_bf8(blo4), nl4));
+    acc[2] = mfma32(id2l_lo, as_bf8(bhi4), mfma32(id2h_lo, as_bf8(bhi4), nl4));
+    acc[3] = mfma32(id2l_hi, as_bf8(bhi4), mfma32(id2h_hi, as_bf8(bhi4), nl4));
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f32x4 qk = mfma32(kf[t], qf, zero4);
+      const f32x4 dp = mfma32(vf[t], daf, nd4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[t][r] = exp2_fast(fmaf(qk[r], c1, acc[t][r])) * dp[r];
+    }
+    const bf16x8 s0 = pack8(acc[0], acc[1]);
+    const bf16x8 s1 = pack8(acc[2], acc[3]);
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) {
+      dq[ct] = mfma32(kt[ct][0], s0, dq[ct]);
+      dq[ct] = mfma32(kt[ct][1], s1, dq[ct]);
+    }
+  }
+
+  // partial dQ^T (lane (g, ln): channels 16 ct + 4 g + r of query ln) into
+  // the wave's own K region, then the sum over the waves in wave order
+  float* part = reinterpret_cast<float*>(my.k);
+#pragma unroll
+  for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) part[ln * 32 + 16 * ct + 4 * g + r] = dq[ct][r];
+  __syncthreads();
+  const int mq = tid >> 4, c = 2 * (tid & 15), row = q0 + mq;
+  if (row < N && c < d) {
+    float x0 = 0.f, x1 = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const float* pw = reinterpret_cast<const float*>(wl[w].k) + mq * 32 + c;
+      x0 += pw[0];
+      x1 += pw[1];
+    }
+    u16* dQ = static_cast<u16*>(a.dq) + bh * N * d;
+    *reinterpret_cast<uint32_t*>(dQ + (size_t)row * d + c) = pack2(x0 * a.scale, x1 * a.scale);
+  }
+}
+
 // ------------------------------------------------------------------ 3. dQ (bf16)
 // Same decomposition as the forward kernel: 4 waves x 16*QT queries of one
 // (b, h), 64-key blocks of K and V double-buffered in LDS in row-major form.
@@ -591,8 +751,9 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
 // their XCD mapping) run the long dK/dV tiles and the dQ tiles fill the
 // slots they leave free, then the chip.  The two roles share the static LDS;
 // the dynamic LDS is the dK/dV slab or the dQ keep bytes.  DK = false builds
-// the dQ role alone (fewer registers) for a launch that carries only dQ tiles.
-template <int DP, int QT, bool ALIGNED, bool SLAB, int NQR, bool DK = true>
+// the dQ role alone (fewer registers) for a launch that carries only dQ tiles;
+// KS = true runs the key-split dQ tiles (nqblocks then counts 16-query tiles).
+template <int DP, int QT, bool ALIGNED, bool SLAB, int NQR, bool DK = true, bool KS = false>
 __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nqblocks, int ndk, int ndk_slots) {
   constexpr int KC = DP / 32, CT = DP / 16;
   constexpr int QW = 16 * QT, QBLK = 4 * QW;
@@ -602,9 +763,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     u16 sK[2][64 * LK::kRowElems];
     u16 sV[2][64 * LK::kRowElems];
   };
+  static_assert(!KS || DP == 32, "key-split dQ tiles: d <= 32");
   union Smem {
     DqSmem dq;
     DkdvSmem<DP> dk;
+    DqSplitWaveLds ks[KS ? 4 : 1];
   };
   __shared__ Smem sm;
   extern __shared__ f32x4 bwd_dyn_lds[];
@@ -617,6 +780,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   }
   wg -= ndk_slots;
   nwg -= ndk_slots;
+  if constexpr (KS) {
+    attn_dq_split_tile(wg, nwg, sm.ks, reinterpret_cast<uint32_t*>(bwd_dyn_lds), a, nqblocks);
+    return;
+  }
   auto& sK = sm.dq.sK;
   auto& sV = sm.dq.sV;
   // keep bytes of every key (64 per key block): filled once, so the key
@@ -1218,14 +1385,19 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
     const int ndk_slots = (ndk + 7) & ~7;
     const bool qt2 = dp == 32 && bhs * ((a.N + 127) / 128) >= 1024;
     const bool al = (a.N % 8) == 0;
-    const int nqb = qt2 ? (a.N + 127) / 128 : (a.N + 63) / 64;
     const size_t keep_bytes = (size_t)((a.N + 63) / 64) * 64;
     const bool fuse = dkdv_wgs_per_cu(a.N, a.d, true, a.slab != 0 && !reg_slab) >= 2;
+    // grids that would leave most CUs idle run key-split dQ tiles (one per 16
+    // queries) in the fused launch
+    const bool ks = fuse && dp == 32 && al && a.N > 64 && a.N <= 16384 && bhs * ((a.N + 63) / 64) < 512;
+    const int nqb = ks ? (a.N + 15) / 16 : qt2 ? (a.N + 127) / 128 : (a.N + 63) / 64;
     const void* fn;
 #define PBA_BWD_FN(DPV, QTV, ALV, SLV, NQV) \
   reinterpret_cast<const void*>(&attn_bwd_dq_bf16_kernel<DPV, QTV, ALV, SLV, NQV>)
 #define PBA_BWD_FN6(DPV, QTV, ALV) \
   reinterpret_cast<const void*>(&attn_bwd_dq_bf16_kernel<DPV, QTV, ALV, false, 0, false>)
+#define PBA_BWD_FNKS(SLV, NQV) \
+  reinterpret_cast<const void*>(&attn_bwd_dq_bf16_kernel<32, 1, true, SLV, NQV, true, true>)
 #define PBA_BWD_PICK(SLV)                                                                          \
   if (dp == 32) {                                                                                  \
     if (qt2) fn = al ? PBA_BWD_FN(32, 2, true, SLV, 0) : PBA_BWD_FN(32, 2, false, SLV, 0);         \
@@ -1234,7 +1406,9 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
     if (qt2) fn = al ? PBA_BWD_FN(64, 2, true, SLV, 0) : PBA_BWD_FN(64, 2, false, SLV, 0);         \
     else fn = al ? PBA_BWD_FN(64, 1, true, SLV, 0) : PBA_BWD_FN(64, 1, false, SLV, 0);             \
   }
-    if (reg_slab) {
+    if (ks) {
+      fn = reg_slab ? PBA_BWD_FNKS(true, 6) : a.slab ? PBA_BWD_FNKS(true, 0) : PBA_BWD_FNKS(false, 0);
+    } else if (reg_slab) {
       if (qt2) fn = al ? PBA_BWD_FN(32, 2, true, true, 6) : PBA_BWD_FN(32, 2, false, true, 6);
       else fn = al ? PBA_BWD_FN(32, 1, true, true, 6) : PBA_BWD_FN(32, 1, false, true, 6);
     } else if (a.slab) {
@@ -1253,6 +1427,7 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
 #undef PBA_BWD_PICK
 #undef PBA_BWD_FN
 #undef PBA_BWD_FN6
+#undef PBA_BWD_FNKS
     const size_t shmem_max = std::max(slab_shmem, keep_bytes);
     // the slab can exceed the default 64 KiB dynamic LDS limit
     if (shmem_max > 64 * 1024 &&

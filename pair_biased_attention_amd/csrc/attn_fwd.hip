@@ -342,10 +342,8 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
 struct SplitWaveLds {
   u16 k[64 * 32];    // TileLds<32, 1>
   u16 v[64 * 32];    // TileLds<32, 1>
-  u32x4 bias[128];   // 16 query rows x 8 units; unit u of row q at slot u ^ ((q >> 1) & 7)
+  u32x4 bias[128];   // 16 query rows x 8 units in the bias_rows_slot layout
 };
-
-__device__ __forceinline__ int split_bias_slot(int q, int u) { return 8 * q + (u ^ ((q >> 1) & 7)); }
 
 __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
   using LK = TileLds<32, 1>;
@@ -423,7 +421,7 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
       for (int m = 0; m < 2; ++m) vt[ct][m] = tr_frag_l<LK>(my.v, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
-    u32x4 blo4 = my.bias[split_bias_slot(ln, 2 * g)], bhi4 = my.bias[split_bias_slot(ln, 2 * g + 1)];
+    u32x4 blo4 = my.bias[bias_rows_slot(ln, 2 * g)], bhi4 = my.bias[bias_rows_slot(ln, 2 * g + 1)];
     uint32_t kw[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) kw[e] = split_keep[(kb >> 2) + 4 * g + e];  // keep bytes of keys 16g+4e .. +3

@@ -157,6 +157,12 @@ struct TileLds {
   }
 };
 
+// 16 query rows x 64 keys of a bf16 bias block in LDS as 16-byte units:
+// unit u (keys 8u .. 8u + 7) of row q sits at slot 8q + (u ^ ((q >> 1) & 7)).
+// The two units a lane group reads from one row then fall on distinct banks
+// for all 16 rows of a 16-lane read.
+__device__ __forceinline__ int bias_rows_slot(int q, int u) { return 8 * q + (u ^ ((q >> 1) & 7)); }
+
 // tr_frag for a TileLds layout: lane (g, j) gets rows rb0+e and rb1+e
 // (e = 0..3) at column c0 + j of the tile.
 template <class L>

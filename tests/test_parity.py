@@ -100,12 +100,14 @@ SMALL_ATTN = [
     (2, 2, 65, 48, "f32", "none"),
     (3, 1, 33, 64, "f32", "random:2"),
     # small grids (B H ceil(N/64) < 512) with N % 8 == 0 and d <= 32 take the
-    # key-split forward: four waves per 16-query tile, each a range of key blocks
+    # key-split forward and key-split dQ tiles: four waves per 16-query tile,
+    # each a range of key blocks
     (1, 3, 328, 24, "bf16", "random:12"),    # six blocks over four waves (1, 2, 1, 2), ragged last block
     (2, 2, 1000, 32, "bf16", "tail:40"),     # sixteen blocks, the masked tail inside the last wave's range
     (1, 1, 136, 16, "bf16", "none"),         # three blocks: wave 0 has no keys
     (1, 2, 256, 32, "bf16", "tail:64"),      # one block per wave, the last wave's block wholly masked
     (1, 2, 2048, 8, "bf16", "random:30"),    # 32 blocks, d = 8
+    (2, 2, 264, 32, "bf16", "random:17"),    # the same split for dQ beside dK/dV tiles with the dBias slab in LDS
     # grids of >= 512 (b, h) workgroups take the K/V-resident forward kernel
     (128, 4, 200, 24, "bf16", "tail:7"),     # ragged N, padded d, idle waves past N
     (64, 8, 136, 48, "bf16", "random:5"),    # d = 48 in the 64-wide template
