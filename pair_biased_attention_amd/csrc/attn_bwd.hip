@@ -85,16 +85,20 @@ __device__ __forceinline__ u32x4 load_bias8(const u16* row, int k0, int N, bool 
 // bf16: one lane per 16-byte chunk of a row (L = d/8 lanes per row, 256/L
 // rows per workgroup), so every load and store is a coalesced 16-byte access;
 // D is summed over a row's lanes through LDS in a fixed order.
-__global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int rows_per_wg) {
-  __shared__ float sPart[256];
+__global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int lanes_log2) {
+  // each row takes 2^lanes_log2 consecutive lanes (d / 8 rounded up to a
+  // power of two), lane c its channels 8c .. 8c + 7; the row sum D is a
+  // butterfly over those lanes, so there is no LDS and no barrier, and the
+  // row's LSE is requested together with the other loads
   const int tid = threadIdx.x;
-  const int L = a.d / 8;
+  const int lanes = 1 << lanes_log2;
   const long long rows = (long long)a.B * a.H * a.N;
-  const long long row0 = (long long)blockIdx.x * rows_per_wg;
-  const int r = tid / L, c = tid % L;
-  const long long row = row0 + r;
+  const long long row = (long long)blockIdx.x * (256 >> lanes_log2) + (tid >> lanes_log2);
+  const int c = tid & (lanes - 1);
+  const bool live = row < rows && 8 * c < a.d;
+  const float l = (row < rows && c == 0) ? a.lse[row] : 0.f;
   float D = 0.f;
-  if (r < rows_per_wg && row < rows) {
+  if (live) {
     const size_t off = (size_t)row * a.d + 8 * c;
     const u32x4 xo = ld16(static_cast<const u16*>(a.dout) + off);
     const u32x4 xv = ld16(static_cast<const u16*>(a.out) + off);
@@ -118,15 +122,9 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int r
     *reinterpret_cast<u32x4*>(static_cast<u16*>(a.da) + off) = ra;
     *reinterpret_cast<u32x4*>(static_cast<u16*>(a.dg) + off) = rg;
   }
-  sPart[tid] = D;
-  __syncthreads();
-  if (tid < rows_per_wg && row0 + tid < rows) {
-    float s = 0.f;
-    for (int j = 0; j < L; ++j) s += sPart[tid * L + j];
-    const float l = a.lse[row0 + tid];
-    // rows without keys (LSE = -inf) get the seed -inf, so P = exp2(-inf) = 0
-    a.seed[row0 + tid] = make_float2(l == kNegInf ? kNegInf : -l * kLog2e, -s);
-  }
+  for (int m = 1; m < lanes; m <<= 1) D += __shfl_xor(D, m);
+  // rows without keys (LSE = -inf) get the seed -inf, so P = exp2(-inf) = 0
+  if (row < rows && c == 0) a.seed[row] = make_float2(l == kNegInf ? kNegInf : -l * kLog2e, -D);
 }
 
 __global__ void __launch_bounds__(256) attn_bwd_pre_f32_kernel(BwdArgs a) {
@@ -1335,10 +1333,18 @@ BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16) {
   return pl;
 }
 
+// lanes per row of the bf16 preprocess: d / 8 rounded up to a power of two (log2)
+static int pre_lanes_log2(int d) {
+  int lg = 0;
+  while ((1 << lg) < d / 8) ++lg;
+  return lg;
+}
+
 hipError_t launch_attn_bwd_pre_bf16(const BwdArgs& a, hipStream_t stream) {
   const long long rows = (long long)a.B * a.H * a.N;
-  const int rpw = 256 / (a.d / 8);
-  hipLaunchKernelGGL(attn_bwd_pre_bf16_kernel, dim3((unsigned)((rows + rpw - 1) / rpw)), dim3(256), 0, stream, a, rpw);
+  const int lg = pre_lanes_log2(a.d);
+  const int rpw = 256 >> lg;
+  hipLaunchKernelGGL(attn_bwd_pre_bf16_kernel, dim3((unsigned)((rows + rpw - 1) / rpw)), dim3(256), 0, stream, a, lg);
   return hipGetLastError();
 }
 
@@ -1359,9 +1365,10 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
   // 1. preprocess
   {
     if (bf16) {
-      const int rpw = 256 / (a.d / 8);
+      const int lg = pre_lanes_log2(a.d);
+      const int rpw = 256 >> lg;
       const dim3 grid((unsigned)((rows + rpw - 1) / rpw));
-      hipLaunchKernelGGL(attn_bwd_pre_bf16_kernel, grid, dim3(256), 0, stream, a, rpw);
+      hipLaunchKernelGGL(attn_bwd_pre_bf16_kernel, grid, dim3(256), 0, stream, a, lg);
     } else {
       const dim3 grid((unsigned)((rows + 255) / 256));
       hipLaunchKernelGGL(attn_bwd_pre_f32_kernel, grid, dim3(256), 0, stream, a);
