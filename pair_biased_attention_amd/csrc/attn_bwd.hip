@@ -20,7 +20,12 @@
 //        of at most six query blocks, LDS otherwise) that sums over the chunk
 //        and is written once per chunk as an fp32 partial;
 //      - query-stationary dQ tiles, filling the rest: P and dP recomputed per
-//        64-key block, dQ = dS K accumulated in registers.
+//        64-key block, dQ = dS K accumulated in registers.  Grids too small
+//        to fill the chip (B H ceil(N/64) < 512) take key-split dQ tiles
+//        instead: one 16-query tile per workgroup, its four waves each over a
+//        quarter of the key blocks, partial dQ summed in wave order.  When
+//        the two launches are separate, the dQ launch runs a kernel instance
+//        without the dK/dV role (fewer registers).
 //      (fp32: attn_bwd_dkdv_f32 and attn_bwd_dq_f32, two launches.)
 //   3. bias_grad_reduce  dBias = sum of the P partials in index order (skipped
 //                        for one batch row, where dS is stored as dBias).

@@ -8,12 +8,20 @@
 // to memory (online softmax over key blocks, the tiling that section credits
 // for the memory savings of fused biased-attention kernels).
 //
-// Work decomposition: one workgroup (4 waves) per (b, h, block of 64*QT
-// queries); each wave owns 16*QT queries and walks all keys in blocks of 64
-// that the workgroup stages through LDS (double-buffered).  Scores are
-// produced transposed, S^T = K Q^T, so each lane owns one query column and
-// its softmax statistics stay in-lane; the same layout feeds P^T straight
-// into the O^T = V^T P^T product, and the gate epilogue needs no shuffles.
+// Work decomposition (three kernels, chosen by the launcher):
+//  - streaming: one workgroup (4 waves) per (b, h, block of 64*QT queries);
+//    each wave owns 16*QT queries and walks all keys in blocks of 64 that the
+//    workgroup stages through LDS (double-buffered);
+//  - K/V-resident (N <= 512 on grids that fill the chip): the workgroup
+//    stages all of K and V of its (b, h) once, then its waves walk the key
+//    blocks without barriers;
+//  - key-split (grids too small to fill the chip): one 16-query tile per
+//    workgroup, its four waves over quarters of the keys, partial softmax
+//    states merged at the end.
+// Scores are produced transposed, S^T = K Q^T, so each lane owns one query
+// column and its softmax statistics stay in-lane; the same layout feeds P^T
+// straight into the O^T = V^T P^T product, and the gate epilogue needs no
+// shuffles.
 #include "pba_device.h"
 #include "pba_kernels.h"
 
