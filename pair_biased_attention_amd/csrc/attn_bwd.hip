@@ -586,16 +586,9 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
 // four partial dQ tiles are summed in wave order through LDS at the end.  Per
 // block the arithmetic is the dQ role's with one query tile.  d <= 32 and
 // N % 8 == 0 only.
-struct DqSplitWaveLds {
-  u16 k[64 * 32];    // TileLds<32, 1>
-  u16 v[64 * 32];    // TileLds<32, 1>
-  u32x4 bias[128];   // bias_rows_slot layout
-};
-
-__device__ __forceinline__ void attn_dq_split_tile(int wg, int nwg, DqSplitWaveLds (&wl)[4], uint32_t* keep,
+__device__ __forceinline__ void attn_dq_split_tile(int wg, int nwg, KeySplitLds (&wl)[4], uint32_t* keep,
                                                    const BwdArgs& a, int nqt) {
   using LK = TileLds<32, 1>;
-  constexpr uint32_t kOob = 0xFFFFFFF0u;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
   const int N = a.N, d = a.d;
@@ -611,29 +604,10 @@ __device__ __forceinline__ void attn_dq_split_tile(int wg, int nwg, DqSplitWaveL
   const i32x4 krs = rsrc_words(static_cast<const u16*>(a.k) + bh * N * d, plane_bytes);
   const i32x4 vrs = rsrc_words(static_cast<const u16*>(a.v) + bh * N * d, plane_bytes);
   const i32x4 brs = rsrc_words(static_cast<const u16*>(a.bias) + (size_t)h * N * N, (uint32_t)((size_t)N * N * 2));
-  DqSplitWaveLds& my = wl[wave];
+  KeySplitLds& my = wl[wave];
 
-  // staging of key block kb: K and V load i fills LDS units 64 i + lane (row
-  // 16 i + lane / 4, slot lane % 4 holding channel unit slot ^ f(row); units
-  // past d read as zeros, rows past N fail the range check); bias load i
-  // fills slots 64 i + lane (query row 8 i + lane / 8)
-  auto stage = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * i + (lane >> 2);
-      const int c8 = ((lane & 3) ^ LK::f(r)) & 3;
-      const uint32_t off = 8 * c8 < d ? (uint32_t)(((kb + r) * d + 8 * c8) * 2) : kOob;
-      lds_dma16(krs, lds_addr(my.k) + 1024 * i, off);
-      lds_dma16(vrs, lds_addr(my.v) + 1024 * i, off);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = 8 * i + (lane >> 3);
-      const int u = (lane & 7) ^ ((q >> 1) & 7);
-      const uint32_t off = q0 + q < N ? (uint32_t)(((size_t)(q0 + q) * N + kb + 8 * u) * 2) : kOob;
-      lds_dma16(brs, lds_addr(my.bias) + 1024 * i, off);
-    }
-  };
+  // staging of key block kb into this wave's region (keys past N are masked below)
+  auto stage = [&](int kb) { key_split_stage(my, krs, vrs, brs, q0, N, d, kb, lane); };
   if (blo < bhi) stage(64 * blo);
   for (int k = tid; k < nkb * 64; k += 256)
     reinterpret_cast<uint8_t*>(keep)[k] = (k < N && (a.mask == nullptr || a.mask[k] != 0)) ? 1 : 0;
@@ -770,7 +744,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   union Smem {
     DqSmem dq;
     DkdvSmem<DP> dk;
-    DqSplitWaveLds ks[KS ? 4 : 1];
+    KeySplitLds ks[KS ? 4 : 1];
   };
   __shared__ Smem sm;
   extern __shared__ f32x4 bwd_dyn_lds[];

@@ -347,16 +347,10 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
 // which is the online-softmax recurrence applied across the four key ranges.
 // The per-block arithmetic is the streaming kernel's with one query tile.
 // d <= 32 and N % 8 == 0 (16-byte bias rows) only.
-struct SplitWaveLds {
-  u16 k[64 * 32];    // TileLds<32, 1>
-  u16 v[64 * 32];    // TileLds<32, 1>
-  u32x4 bias[128];   // 16 query rows x 8 units in the bias_rows_slot layout
-};
-
 __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
   using LK = TileLds<32, 1>;
   constexpr uint32_t kOob = 0xFFFFFFF0u;
-  __shared__ SplitWaveLds wl[4];
+  __shared__ KeySplitLds wl[4];
   extern __shared__ __attribute__((aligned(16))) uint32_t split_keep[];  // keep bytes of every key block
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
@@ -374,31 +368,10 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
   const i32x4 krs = rsrc_words(static_cast<const u16*>(a.k) + bh * N * d, plane_bytes);
   const i32x4 vrs = rsrc_words(static_cast<const u16*>(a.v) + bh * N * d, plane_bytes);
   const i32x4 brs = rsrc_words(static_cast<const u16*>(a.bias) + (size_t)h * N * N, (uint32_t)((size_t)N * N * 2));
-  SplitWaveLds& my = wl[wave];
+  KeySplitLds& my = wl[wave];
 
-  // Staging of key block kb.  K and V: load i fills LDS units 64 i + lane,
-  // i.e. row r = 16 i + lane / 4 at slot lane % 4, which holds channel unit
-  // (slot ^ f(r)) (units past d read as zeros; rows past N fail the range
-  // check).  Bias: load i fills slots 64 i + lane, i.e. query row
-  // q = 8 i + lane / 8 at slot lane % 8, holding keys kb + 8u .. + 7 with
-  // u = slot ^ ((q >> 1) & 7); keys past N there are masked below.
-  auto stage = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * i + (lane >> 2);
-      const int c8 = ((lane & 3) ^ LK::f(r)) & 3;
-      const uint32_t off = 8 * c8 < d ? (uint32_t)(((kb + r) * d + 8 * c8) * 2) : kOob;
-      lds_dma16(krs, lds_addr(my.k) + 1024 * i, off);
-      lds_dma16(vrs, lds_addr(my.v) + 1024 * i, off);
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int q = 8 * i + (lane >> 3);
-      const int u = (lane & 7) ^ ((q >> 1) & 7);
-      const uint32_t off = q0 + q < N ? (uint32_t)(((size_t)(q0 + q) * N + kb + 8 * u) * 2) : kOob;
-      lds_dma16(brs, lds_addr(my.bias) + 1024 * i, off);
-    }
-  };
+  // staging of key block kb into this wave's region (keys past N are masked below)
+  auto stage = [&](int kb) { key_split_stage(my, krs, vrs, brs, q0, N, d, kb, lane); };
   if (blo < bhi) stage(64 * blo);
 
   for (int k = tid; k < nkb * 64; k += 256)

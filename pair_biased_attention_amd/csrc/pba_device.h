@@ -211,6 +211,43 @@ __device__ __forceinline__ void vm_wait() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// ---- key-split staging: one wave's private copy of a 64-key block
+// K and V rows in the TileLds<32, 1> layout (64-byte rows) and the bias of
+// the wave's 16 query rows in the bias_rows_slot layout, 10 KB per wave.
+struct KeySplitLds {
+  u16 k[64 * 32];
+  u16 v[64 * 32];
+  u32x4 bias[128];
+};
+
+// Stage key block kb (64 keys) of one (b, h) into `my` with LDS-destination
+// loads, ten per wave.  K and V: load i fills LDS units 64 i + lane, i.e. row
+// r = 16 i + lane / 4 at slot lane % 4, which holds channel unit
+// slot ^ f(r); units past d read as zeros and rows past N fail the range
+// check of the (b, h) plane.  Bias: load i fills slots 64 i + lane, i.e. query
+// row q = 8 i + lane / 8 at slot lane % 8, holding keys kb + 8u .. + 7 with
+// u = slot ^ ((q >> 1) & 7); rows past N read as zeros, keys past N land in
+// masked columns.  The loads are ordered by the caller's vm_wait.
+__device__ __forceinline__ void key_split_stage(KeySplitLds& my, i32x4 krs, i32x4 vrs, i32x4 brs, int q0, int N,
+                                                int d, int kb, int lane) {
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * i + (lane >> 2);
+    const int c8 = ((lane & 3) ^ TileLds<32, 1>::f(r)) & 3;
+    const uint32_t off = 8 * c8 < d ? (uint32_t)(((kb + r) * d + 8 * c8) * 2) : kOob;
+    lds_dma16(krs, lds_addr(my.k) + 1024 * i, off);
+    lds_dma16(vrs, lds_addr(my.v) + 1024 * i, off);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int q = 8 * i + (lane >> 3);
+    const int u = (lane & 7) ^ ((q >> 1) & 7);
+    const uint32_t off = q0 + q < N ? (uint32_t)(((size_t)(q0 + q) * N + kb + 8 * u) * 2) : kOob;
+    lds_dma16(brs, lds_addr(my.bias) + 1024 * i, off);
+  }
+}
+
 // ---- bounds-checked global loads through a buffer resource: any byte past
 // num_bytes reads as zero, so ragged tiles need no per-element guards.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
