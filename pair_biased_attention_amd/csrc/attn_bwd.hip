@@ -577,6 +577,290 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
   }
 }
 
+// ------------------------------------------------------------------ 2b. dK/dV, eight waves (LDS slab)
+// When the dBias slab sits in LDS and leaves room for only one workgroup per
+// CU (the launches are then split: dK/dV tiles, then dQ tiles), the dK/dV
+// tiles at d > 32 run as eight-wave workgroups: wave (kt, qq) owns 16 keys and one
+// 16-query tile (quarter qq) of every 64-query block, so the CU holds two
+// waves per SIMD instead of one in the same LDS.  The dV and dK products then
+// have the wave's 16 queries on their k axis (16x16x16 products, each on an
+// accumulator chain of its own), and at the end of a row the four query
+// quarters of dK and dV are summed in quarter order through LDS.  The rest
+// is the four-wave tile's: the same staged Q/dA tiles, row seeds and
+// bias identity products, and each slab cell (query tile, key tile) owned by
+// one wave and updated in program order.
+template <int DP>
+struct Dkdv8Smem {
+  static constexpr int kTile = 64 * TileLds<DP, 0>::kRowElems;
+  u16 sQA[2][2 * kTile];                  // [buffer][Q tile | dA tile]
+  float sLD[2][2][64];                    // [buffer][-log2(e) LSE | -D]
+  f32x4 comb[3][2][2][DP / 16][64];       // [quarter 1..3][kt][dK | dV][ct][lane]
+};
+
+template <int DP>
+struct Dkdv8Stage {
+  u32x4 q, da;                   // this thread's chunk of the staged Q and dA tiles (threads < 8 DP)
+  u32x4 k[DP / 32], v[DP / 32];  // this lane's K and V row (with a row's first query block)
+  u32x4 bias;                    // lane groups 0-1: keys 16 kt + 8 g .. +7 of query row 16 qq + n
+  float2 seed;                   // (-log2(e) LSE, -D) of query `lane` of the block (wave 0)
+};
+
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+  typedef short s16x4v __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4v, a), __builtin_bit_cast(s16x4v, b), c,
+                                                   0, 0, 0);
+}
+
+template <int DP, bool ALIGNED>
+__global__ void __launch_bounds__(512) attn_bwd_dkdv8_kernel(BwdArgs a) {
+  static_assert(DP == 64, "eight-wave dK/dV tiles: the 64-wide template only");
+  constexpr int KC = DP / 32, CT = DP / 16;
+  constexpr int kTile = Dkdv8Smem<DP>::kTile;
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+  using LQ = TileLds<DP, 0>;
+  __shared__ Dkdv8Smem<DP> sm;
+  extern __shared__ f32x4 dkdv8_slab[];  // [nqb][4 query tiles][2 key tiles][64 lanes]
+  f32x4* const slab = dkdv8_slab;
+  auto& sQA = sm.sQA;
+  auto& sLD = sm.sLD;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int g = lane >> 4, n = lane & 15;
+  const int kt = wave & 1, qq = wave >> 1;
+  const int N = a.N, d = a.d, H = a.H;
+  const int nkb = (N + 31) / 32;
+  const int nqb = (N + 63) / 64;
+  const int L = xcd_remap(blockIdx.x, gridDim.x);
+  const int kblk = L % nkb;
+  const int hp = L / nkb;
+  const int p = hp % a.P, h = hp / a.P;
+  const int kb = kblk * 32;
+  const int key = kb + 16 * kt + n;
+  const int b0 = p * a.C, b1 = min(a.B, b0 + a.C);
+  const int T = (b1 - b0) * nqb;
+  const u16* BiasH = static_cast<const u16*>(a.bias) + (size_t)h * N * N;
+  const __amdgpu_buffer_rsrc_t brs = make_rsrc(BiasH, (uint32_t)((size_t)N * N * 2));
+  const size_t plane = (size_t)N * d;
+  const uint32_t plane_bytes = (uint32_t)(plane * 2);
+  const bool keep_lane = key < N && (a.mask == nullptr || a.mask[key] != 0);
+  const bool wave_masked = __any(!keep_lane);
+
+  {
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int idx = tid; idx < nqb * 8 * 64; idx += 512) slab[idx] = z;
+  }
+
+  // staging: 64 DP / 8 sixteen-byte chunks per tile, one per thread below that
+  const bool stager = tid < 8 * DP;
+  const int kap = tid / (DP / 8), col = 8 * (tid % (DP / 8));
+  const uint32_t chunk_off = (uint32_t)((kap * d + col) * 2);
+  // bias: lane groups 0-1 hold keys 16 kt + 8 g .. + 7 of query row 16 qq + n;
+  // groups 2-3 read nothing (their entries meet zeros of the identity operand)
+  const int k0 = kb + 16 * kt + 8 * (g & 1);
+  const int bq = 16 * qq + n;
+  const uint32_t bias_off = (uint32_t)((bq * N + k0) * 2);
+  bool colok[KC];
+#pragma unroll
+  for (int kc = 0; kc < KC; ++kc) colok[kc] = 32 * kc + 8 * g < d;
+
+  Dkdv8Stage<DP> R[2];
+  const size_t row_step = (size_t)H * plane;
+  const u16* fK = static_cast<const u16*>(a.k) + ((size_t)b0 * H + h) * plane;
+  const u16* fV = static_cast<const u16*>(a.v) + ((size_t)b0 * H + h) * plane;
+  const u16* fQ = static_cast<const u16*>(a.q) + ((size_t)b0 * H + h) * plane;
+  const u16* fdA = static_cast<const u16*>(a.da) + ((size_t)b0 * H + h) * plane;
+  const float2* fS = a.seed + ((size_t)b0 * H + h) * N;
+  uint32_t rec_plane = plane_bytes, rec_row = (uint32_t)N * 8u;
+  int fb = b0, fq = 0;
+  auto advance_fetch = [&]() {
+    if (++fq == nqb) {
+      fq = 0;
+      ++fb;
+      fQ += row_step;
+      fdA += row_step;
+      fK += row_step;
+      fV += row_step;
+      fS += (size_t)H * N;
+      if (fb >= b1) rec_plane = rec_row = 0u;
+    }
+  };
+  auto fetch = [&](Dkdv8Stage<DP>& st, int qblk) {
+    const uint32_t qoff = (uint32_t)(qblk * 64 * d * 2);
+    st.q = buf_load16(make_rsrc(fQ, rec_plane), stager ? chunk_off + qoff : kOob);
+    st.da = buf_load16(make_rsrc(fdA, rec_plane), stager ? chunk_off + qoff : kOob);
+    if (qblk == 0) {
+      const __amdgpu_buffer_rsrc_t rk = make_rsrc(fK, rec_plane);
+      const __amdgpu_buffer_rsrc_t rv = make_rsrc(fV, rec_plane);
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const uint32_t off = (uint32_t)((key * d + 32 * kc + 8 * g) * 2);
+        st.k[kc] = buf_load16(rk, off);
+        st.v[kc] = buf_load16(rv, off);
+      }
+    }
+    if (wave == 0) st.seed = buf_load_f32x2(make_rsrc(fS, rec_row), (uint32_t)((qblk * 64 + lane) * 8));
+    if constexpr (ALIGNED) {
+      st.bias = buf_load16(brs, g < 2 ? bias_off + (uint32_t)(qblk * 64 * N * 2) : kOob);
+    } else {
+      const int qa = qblk * 64 + bq;
+      st.bias = (g < 2 && qa < N) ? load_bias8(BiasH + (size_t)qa * N, k0, N, false) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto commit = [&](const Dkdv8Stage<DP>& st, int buf, int qblk) {
+    u16* tQ = sQA[buf];
+    if (stager) {
+      *reinterpret_cast<u32x4*>(&tQ[LQ::off(kap, col)]) = st.q;
+      *reinterpret_cast<u32x4*>(&tQ[kTile + LQ::off(kap, col)]) = st.da;
+    }
+    if (tid < 64) {
+      sLD[buf][0][tid] = qblk * 64 + tid < N ? st.seed.x : kNegInf;
+      sLD[buf][1][tid] = st.seed.y;
+    }
+  };
+
+  const bf16x8 id_l2hi = ident_cols_frag(lane, kLog2eHiBf16, 0);
+  const bf16x8 id_l2lo = ident_cols_frag(lane, kLog2eLoBf16, 0);
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const u32x4 zero_u4 = {0u, 0u, 0u, 0u};
+  bf16x8 kf[KC], vf[KC];
+  f32x4 dk[CT], dv[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
+  const float c1 = a.scale * kLog2e;
+  auto take_kv = [&](const Dkdv8Stage<DP>& st) {
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      kf[kc] = as_bf8(colok[kc] ? st.k[kc] : zero_u4);
+      vf[kc] = as_bf8(colok[kc] ? st.v[kc] : zero_u4);
+    }
+  };
+
+  int cb = b0, cq = 0;
+  if (T > 0) {
+    fetch(R[0], fq);
+    advance_fetch();
+    fetch(R[1], fq);
+    advance_fetch();
+    commit(R[0], 0, 0);
+    take_kv(R[0]);
+  }
+  __syncthreads();
+
+  // transposed operand reads of the dV and dK products: lane (g, 4e + a)
+  // supplies row 16 qq + 4 g + e, columns 16 ct + 4 a .. + 3
+  const int tre = (lane & 15) >> 2, tra = lane & 3;
+  auto step = [&](auto S_c) {
+    constexpr int S = decltype(S_c)::value;
+    const int b = cb, qblk = cq;
+    const bool last_q = qblk == nqb - 1;
+    const u16* tQ = sQA[S];
+    const u16* tA = tQ + kTile;
+    f32x4 sacc = *reinterpret_cast<const f32x4*>(&sLD[S][0][16 * qq + 4 * g]);
+    f32x4 dp = *reinterpret_cast<const f32x4*>(&sLD[S][1][16 * qq + 4 * g]);
+    bf16x8 qfr[KC], afr[KC];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      qfr[kc] = as_bf8(*reinterpret_cast<const u32x4*>(&tQ[LQ::off(16 * qq + n, 32 * kc + 8 * g)]));
+      afr[kc] = as_bf8(*reinterpret_cast<const u32x4*>(&tA[LQ::off(16 * qq + n, 32 * kc + 8 * g)]));
+    }
+    u32x2 trA[CT], trQ[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      trA[ct] = lds_tr16(tA + LQ::off(16 * qq + 4 * g + tre, 16 * ct + 4 * tra));
+      trQ[ct] = lds_tr16(tQ + LQ::off(16 * qq + 4 * g + tre, 16 * ct + 4 * tra));
+    }
+    f32x4* const st = slab + ((qblk * 4 + qq) * 2 + kt) * 64 + lane;
+    const f32x4 slab0 = st[0];
+    sacc = mfma32(as_bf8(R[S].bias), id_l2hi, sacc);
+    sacc = mfma32(as_bf8(R[S].bias), id_l2lo, sacc);
+    fetch(R[S], fq);  // iteration it+2
+    advance_fetch();
+    f32x4 qk = zero4;
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc) {
+      qk = mfma32(qfr[kc], kf[kc], qk);
+      dp = mfma32(afr[kc], vf[kc], dp);
+    }
+    f32x4 pj, dsj;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      pj[r] = exp2_fast(fmaf(qk[r], c1, sacc[r]));
+      dsj[r] = pj[r] * dp[r];
+    }
+    if (wave_masked && !keep_lane) pj = dsj = zero4;  // masked keys: P = dS = 0
+    st[0] = slab0 + dsj;
+    // P and dS as 16x16x16 B operands: k slot (g, v) is query 16 qq + 4 g + v
+    const u32x2 pb = {pack2(pj[0], pj[1]), pack2(pj[2], pj[3])};
+    const u32x2 dsb = {pack2(dsj[0], dsj[1]), pack2(dsj[2], dsj[3])};
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      dv[ct] = mfma16(trA[ct], pb, dv[ct]);
+      dk[ct] = mfma16(trQ[ct], dsb, dk[ct]);
+    }
+    if (++cq == nqb) {
+      cq = 0;
+      ++cb;
+    }
+    commit(R[S ^ 1], S ^ 1, cq);
+    if (last_q) take_kv(R[S ^ 1]);
+    __syncthreads();
+
+    if (last_q) {
+      // the four query quarters of dK and dV of row b, summed in quarter order
+      if (qq > 0) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          sm.comb[qq - 1][kt][0][ct][lane] = dk[ct];
+          sm.comb[qq - 1][kt][1][ct][lane] = dv[ct];
+        }
+      }
+      __syncthreads();
+      if (qq == 0 && key < N) {
+        const size_t bh = (size_t)b * H + h;
+        u16* dK = static_cast<u16*>(a.dk) + bh * plane;
+        u16* dV = static_cast<u16*>(a.dv) + bh * plane;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+          const int c = 16 * ct + 4 * g;
+          if (c >= d) continue;
+          f32x4 sk = dk[ct], sv = dv[ct];
+#pragma unroll
+          for (int w = 0; w < 3; ++w) {
+            sk += sm.comb[w][kt][0][ct][lane];
+            sv += sm.comb[w][kt][1][ct][lane];
+          }
+          sk *= a.scale;
+          *reinterpret_cast<u32x2*>(dK + (size_t)key * d + c) = u32x2{pack2(sk[0], sk[1]), pack2(sk[2], sk[3])};
+          *reinterpret_cast<u32x2*>(dV + (size_t)key * d + c) = u32x2{pack2(sv[0], sv[1]), pack2(sv[2], sv[3])};
+        }
+      }
+      // stores share the vector-memory counter with the prefetched loads:
+      // drain it once per row so later waits stay exact
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+#pragma unroll
+      for (int ct = 0; ct < CT; ++ct) dk[ct] = dv[ct] = zero4;
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  for (int it = 0; it < T; it += 2) {
+    step(I0{});
+    if (it + 1 < T) step(I1{});
+  }
+
+  if (key < N) {
+    float* part = a.partial + ((size_t)p * H + h) * N * N;
+    for (int qblk = 0; qblk < nqb; ++qblk) {
+      const f32x4 v = slab[((qblk * 4 + qq) * 2 + kt) * 64 + lane];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int q = qblk * 64 + 16 * qq + 4 * g + r;
+        if (q < N) part[(size_t)q * N + key] = v[r];
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ 3b. dQ, key-split (small grids)
 // For grids that leave most CUs idle (a single batch row and a few heads),
 // the dQ tiles split the keys the way the key-split forward does: one
@@ -1253,12 +1537,18 @@ static size_t slab_bytes(int N, bool bf16) {
 }
 constexpr size_t kMaxSlabBytes = 112 * 1024;
 
+// LDS of a four-wave dK/dV workgroup besides its slab (staged tiles, seeds,
+// combine area)
+static size_t dkdv_tile_bytes(int d, bool bf16) {
+  const size_t dp = d <= 32 ? 32 : 64;
+  return bf16 ? 2 * 2 * 64 * (dp + 8) * 2 + 1024 + 2 * 2 * (dp / 16) * 64 * 16
+              : 2 * 64 * (dp + 1) * 4 + 512 + 2 * 2 * (dp / 16) * 64 * 16;
+}
+
 // Resident dK/dV workgroups per CU (160 KiB of LDS; at most 2 by registers in
 // the bf16 launch that also carries dQ, 3 for fp32).
 static int dkdv_wgs_per_cu(int N, int d, bool bf16, bool slab) {
-  const size_t dp = d <= 32 ? 32 : 64;
-  size_t lds = bf16 ? 2 * 2 * 64 * (dp + 8) * 2 + 1024 + 2 * 2 * (dp / 16) * 64 * 16
-                    : 2 * 64 * (dp + 1) * 4 + 512 + 2 * 2 * (dp / 16) * 64 * 16;
+  size_t lds = dkdv_tile_bytes(d, bf16);
   if (slab) lds += slab_bytes(N, bf16);
   return (int)std::max<size_t>(1, std::min<size_t>(bf16 ? 2 : 3, 160 * 1024 / lds));
 }
@@ -1290,7 +1580,7 @@ static void pick_chunks(int B, int H, int N, int wpc, int& P, int& C) {
 BwdPlan plan_attn_bwd(int B, int H, int N, int d, bool bf16) {
   BwdPlan pl{};
   const size_t rows = (size_t)B * H * N;
-  if (B > 1 && slab_bytes(N, bf16) <= kMaxSlabBytes) {
+  if (B > 1 && slab_bytes(N, bf16) <= kMaxSlabBytes && dkdv_tile_bytes(d, bf16) + slab_bytes(N, bf16) <= 160 * 1024) {
     pl.slab = 1;  // dBias sums in an LDS slab
     pick_chunks(B, H, N, dkdv_wgs_per_cu(N, d, bf16, true), pl.P, pl.C);
   } else {
@@ -1427,8 +1717,24 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
     if (fuse) {
       if ((e = launch(fn, (unsigned)(ndk_slots + bhs * nqb), ndk, ndk_slots, shmem_max)) != hipSuccess) return e;
     } else {
-      if ((e = launch(fn, (unsigned)ndk_slots, ndk, ndk_slots, std::max(slab_shmem, (size_t)16))) != hipSuccess)
+      // the dK/dV launch: at d > 32, eight-wave workgroups (two waves per
+      // SIMD) when the LDS slab fits beside their tiles, else the four-wave
+      // tile (at d <= 32 the eight-wave form measured slower: each wave's
+      // per-block overhead is paid for half the products)
+      const size_t lds8 = sizeof(Dkdv8Smem<64>) + slab_shmem;
+      if (dp == 64 && a.slab && !reg_slab && lds8 <= 160 * 1024) {
+        const void* f8 = al ? reinterpret_cast<const void*>(&attn_bwd_dkdv8_kernel<64, true>)
+                            : reinterpret_cast<const void*>(&attn_bwd_dkdv8_kernel<64, false>);
+        if (slab_shmem > 64 * 1024 &&
+            (e = hipFuncSetAttribute(f8, hipFuncAttributeMaxDynamicSharedMemorySize, (int)slab_shmem)) != hipSuccess)
+          return e;
+        void* kargs[] = {&a};
+        if ((e = hipLaunchKernel(f8, dim3((unsigned)ndk), dim3(512), kargs, slab_shmem, stream)) != hipSuccess)
+          return e;
+      } else if ((e = launch(fn, (unsigned)ndk_slots, ndk, ndk_slots, std::max(slab_shmem, (size_t)16))) !=
+                 hipSuccess) {
         return e;
+      }
       timer_mark(timer, stream);
       if ((e = launch(fn_dq, (unsigned)(bhs * nqb), 0, 0, keep_bytes)) != hipSuccess) return e;
     }

@@ -108,6 +108,12 @@ SMALL_ATTN = [
     (1, 2, 256, 32, "bf16", "tail:64"),      # one block per wave, the last wave's block wholly masked
     (1, 2, 2048, 8, "bf16", "random:30"),    # 32 blocks, d = 8
     (2, 2, 264, 32, "bf16", "random:17"),    # the same split for dQ beside dK/dV tiles with the dBias slab in LDS
+    # the dBias slab in LDS with room for one workgroup per CU: separate
+    # dK/dV and dQ launches, the dK/dV tiles at d > 32 in eight-wave workgroups
+    (3, 2, 456, 32, "bf16", "tail:11"),      # d = 32: four-wave dK/dV launch, slab 64 KB
+    (4, 2, 300, 64, "bf16", "random:13"),    # d = 64, N % 8 != 0 (element-wise bias loads)
+    (2, 3, 520, 48, "bf16", "tail:20"),      # d = 48 in the 64-wide tile, slab 72 KB (159 KB with the tiles)
+    (2, 2, 600, 64, "bf16", "none"),         # slab 80 KB: too large beside the eight-wave tiles, four-wave tile
     # grids of >= 512 (b, h) workgroups take the K/V-resident forward kernel
     (128, 4, 200, 24, "bf16", "tail:7"),     # ragged N, padded d, idle waves past N
     (64, 8, 136, 48, "bf16", "random:5"),    # d = 48 in the 64-wide template
