@@ -18,7 +18,9 @@
 //        queries in 64-query blocks, accumulates dK, dV in registers and adds
 //        dS into a dBias slab [N x 32] (registers for d <= 32 and an even count
 //        of at most six query blocks, LDS otherwise) that sums over the chunk
-//        and is written once per chunk as an fp32 partial;
+//        and is written once per chunk as an fp32 partial.  On grids that
+//        fill the chip with N <= 384, N % 8 == 0 and d <= 32 the tile takes
+//        128-query steps instead, its operands staged by LDS-destination loads;
 //      - query-stationary dQ tiles, filling the rest: P and dP recomputed per
 //        64-key block, dQ = dS K accumulated in registers.  Grids too small
 //        to fill the chip (B H ceil(N/64) < 512) take key-split dQ tiles
@@ -577,6 +579,247 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
   }
 }
 
+// ------------------------------------------------------------------ 2c. dK/dV, 128-query steps
+// The register-slab tile (d <= 32, N <= 384, N % 8 == 0) in steps of 128
+// queries: wave (kt, qh) takes its 16 keys against query half qh of the step
+// (four 16-query tiles), so a step carries twice the products of the
+// 64-query form per barrier.  Every operand of a step -- the Q and dA tiles,
+// the row seeds, each wave's own bias tiles and, at a row's first step, the
+// K and V rows -- goes from memory straight into LDS through LDS-destination
+// buffer loads issued one step ahead into the other of two buffers.  No
+// register holds a staged tile and no LDS store is issued; each step ends
+// with one wait for this wave's loads and the barrier that publishes them.
+struct DkdvWSmem {
+  u16 qa[2][2 * 128 * 32];       // [buffer][Q tile | dA tile], TileLds<32, 0> rows
+  float2 seed[2][128];           // [buffer] (-log2(e) LSE, -D) per query of the step
+  u32x4 bias[2][4][2][64];       // [buffer][wave][half u][lane]: the wave's own bias
+  u32x4 kv[2][2][2][64];         // [row parity][K | V][key tile][lane]
+  f32x4 comb[2 * 2 * 2 * 64];    // query-half combine area of dK, dV
+};
+
+__device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm, const BwdArgs& a) {
+  using LQ = TileLds<32, 0>;
+  constexpr int kTile = 128 * 32;
+  constexpr uint32_t kOob = 0xFFFFFFF0u;
+  const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
+  const int g = lane >> 4, n = lane & 15;
+  const int kt = wave & 1, qh = wave >> 1;
+  const int N = a.N, d = a.d, H = a.H;
+  const int nkb = (N + 31) / 32;
+  const int nqb = (N + 127) / 128;  // 1 .. 3
+  const int L = xcd_remap(wg, nwg);
+  const int kblk = L % nkb;
+  const int hp = L / nkb;
+  const int p = hp % a.P, h = hp / a.P;
+  const int kb = kblk * 32;
+  const int key = kb + 16 * kt + n;
+  const int b0 = p * a.C, b1 = min(a.B, b0 + a.C);
+  const int T = (b1 - b0) * nqb;
+  const size_t plane = (size_t)N * d;
+  const uint32_t plane_bytes = (uint32_t)(plane * 2);
+  const bool keep_lane = key < N && (a.mask == nullptr || a.mask[key] != 0);
+  const bool wave_masked = __any(!keep_lane);
+
+  // per-lane load offsets.  Q / dA: instruction i of this wave fills tile
+  // units 64 (2 wave + i) + lane, i.e. row r = 16 (2 wave + i) + lane / 4 and
+  // the 16-byte chunk that the row's swizzle puts in slot lane % 4.
+  bool qa_ok[2];
+  uint32_t qa_off[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = 16 * (2 * wave + i) + (lane >> 2);
+    const int c = ((lane & 3) ^ LQ::f(r)) & 3;
+    qa_ok[i] = 8 * c < d;
+    qa_off[i] = (uint32_t)((r * d + 8 * c) * 2);
+  }
+  // bias: half u holds query rows 64 qh + 16 (2u + g/2) + n of the step, keys
+  // k0 .. k0 + 7; the identity product of tile j reads half j / 2, lane
+  // groups 2 (j % 2) and 2 (j % 2) + 1
+  const int k0 = kb + 16 * kt + 8 * (g & 1);
+  const int bq0 = 64 * qh + 16 * (g >> 1) + n;
+  // K / V at a row's start: wave w loads K (w even) or V (w odd) of key tile
+  // w / 2: lane (g, n) key kb + 16 (w / 2) + n, channels 8g .. 8g + 7
+  const int kv_key = kb + 16 * (wave >> 1) + n;
+  const uint32_t kv_off = (8 * g < d) ? (uint32_t)((kv_key * d + 8 * g) * 2) : kOob;
+  const i32x4 brs = rsrc_words(static_cast<const u16*>(a.bias) + (size_t)h * N * N, (uint32_t)((size_t)N * N * 2));
+
+  const size_t row_step = (size_t)H * plane;
+  const u16* fQ = static_cast<const u16*>(a.q) + ((size_t)b0 * H + h) * plane;
+  const u16* fdA = static_cast<const u16*>(a.da) + ((size_t)b0 * H + h) * plane;
+  const u16* fKV = static_cast<const u16*>((wave & 1) ? a.v : a.k) + ((size_t)b0 * H + h) * plane;
+  const float2* fS = a.seed + ((size_t)b0 * H + h) * N;
+  int fb = b0, fq = 0;
+  // loads of the step at the fetch position (fb, fq) into buffer buf
+  auto issue = [&](int buf) {
+    const i32x4 rq = rsrc_words(fQ, plane_bytes), ra = rsrc_words(fdA, plane_bytes);
+    const uint32_t qoff = (uint32_t)(fq * 128 * d * 2);
+    const uint32_t dq = lds_addr(sm.qa[buf]);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t off = qa_ok[i] ? qa_off[i] + qoff : kOob;
+      lds_dma16(rq, dq + 1024 * (2 * wave + i), off);
+      lds_dma16(ra, dq + 2 * kTile + 1024 * (2 * wave + i), off);
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int q = fq * 128 + bq0 + 32 * u;
+      const uint32_t off = (q < N && k0 < N) ? (uint32_t)(((size_t)q * N + k0) * 2) : kOob;
+      lds_dma16(brs, lds_addr(&sm.bias[buf][wave][u][0]), off);
+    }
+    if (wave == 0)
+      lds_dma16(rsrc_words(fS, (uint32_t)N * 8u), lds_addr(sm.seed[buf]), (uint32_t)((fq * 128 + 2 * lane) * 8));
+    if (fq == 0)
+      lds_dma16(rsrc_words(fKV, plane_bytes), lds_addr(&sm.kv[(fb - b0) & 1][wave & 1][wave >> 1][0]), kv_off);
+    if (++fq == nqb) {
+      fq = 0;
+      ++fb;
+      fQ += row_step;
+      fdA += row_step;
+      fKV += row_step;
+      fS += (size_t)H * N;
+    }
+  };
+
+  const bf16x8 id_l2hi[2] = {ident_cols_frag(lane, kLog2eHiBf16, 0), ident_cols_frag(lane, kLog2eHiBf16, 2)};
+  const bf16x8 id_l2lo[2] = {ident_cols_frag(lane, kLog2eLoBf16, 0), ident_cols_frag(lane, kLog2eLoBf16, 2)};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  const float c1 = a.scale * kLog2e;
+  f32x4 rslab[3][4];
+#pragma unroll
+  for (int i = 0; i < 3; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rslab[i][j] = zero4;
+  f32x4 dk[2], dv[2];
+  dk[0] = dk[1] = dv[0] = dv[1] = zero4;
+  bf16x8 kf, vf;
+
+  if (T > 0) issue(0);
+  vm_wait<0>();
+  __syncthreads();
+
+  int it = 0, cb = b0;
+  auto step = [&](auto QB_c) {
+    constexpr int QB = decltype(QB_c)::value;
+    const int buf = it & 1;
+    const bool last_q = QB == nqb - 1;
+    if (it + 1 < T) issue(buf ^ 1);
+    if constexpr (QB == 0) {
+      kf = as_bf8(sm.kv[(cb - b0) & 1][0][kt][lane]);
+      vf = as_bf8(sm.kv[(cb - b0) & 1][1][kt][lane]);
+    }
+    const u16* tQ = sm.qa[buf];
+    const u16* tA = tQ + kTile;
+    f32x4 sacc[4], dp[4];
+    bf16x8 qfr[4], afr[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int qt = 4 * qh + j;
+      const f32x4 s01 = *reinterpret_cast<const f32x4*>(&sm.seed[buf][16 * qt + 4 * g]);
+      const f32x4 s23 = *reinterpret_cast<const f32x4*>(&sm.seed[buf][16 * qt + 4 * g + 2]);
+      sacc[j] = f32x4{s01[0], s01[2], s23[0], s23[2]};
+      dp[j] = f32x4{s01[1], s01[3], s23[1], s23[3]};
+      qfr[j] = as_bf8(*reinterpret_cast<const u32x4*>(&tQ[LQ::off(16 * qt + n, 8 * g)]));
+      afr[j] = as_bf8(*reinterpret_cast<const u32x4*>(&tA[LQ::off(16 * qt + n, 8 * g)]));
+    }
+    bf16x8 trA[2][2], trQ[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        const int r0 = 64 * qh + 32 * m + 4 * g;
+        trA[m][ct] = tr_frag_l<LQ>(tA, r0, r0 + 16, 16 * ct, lane);
+        trQ[m][ct] = tr_frag_l<LQ>(tQ, r0, r0 + 16, 16 * ct, lane);
+      }
+    const bf16x8 bb[2] = {as_bf8(sm.bias[buf][wave][0][lane]), as_bf8(sm.bias[buf][wave][1][lane])};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sacc[j] = mfma32(bb[j >> 1], id_l2hi[j & 1], sacc[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sacc[j] = mfma32(bb[j >> 1], id_l2lo[j & 1], sacc[j]);
+    f32x4 qk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      qk[j] = mfma32(qfr[j], kf, zero4);
+      dp[j] = mfma32(afr[j], vf, dp[j]);
+    }
+    // P = exp2(S'), dS = P * (dP - D)
+    f32x4 pj[4], dsj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pj[j][r] = exp2_fast(fmaf(qk[j][r], c1, sacc[j][r]));
+        dsj[j][r] = pj[j][r] * dp[j][r];
+      }
+    if (wave_masked && !keep_lane) {  // masked keys: P = dS = 0
+#pragma unroll
+      for (int j = 0; j < 4; ++j) pj[j] = dsj[j] = zero4;
+    }
+    // P and dS as 16x16x32 operands: k slot (g, v) of product m is query
+    // row 64 qh + 32 m + 16 (v / 4) + 4 g + v % 4 of the step
+#pragma unroll
+    for (int j = 0; j < 4; ++j) rslab[QB][j] += dsj[j];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const bf16x8 pb = pack8(pj[2 * m], pj[2 * m + 1]);
+      const bf16x8 dsb = pack8(dsj[2 * m], dsj[2 * m + 1]);
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct) {
+        dv[ct] = mfma32(trA[m][ct], pb, dv[ct]);
+        dk[ct] = mfma32(trQ[m][ct], dsb, dk[ct]);
+      }
+    }
+    vm_wait<0>();  // this wave's loads of the next step have landed
+    __syncthreads();
+    if (last_q) {
+      // combine the two query halves and store dK, dV of row cb; `comb` is
+      // written again only a row later, after at least one more barrier
+      if (qh == 1) {
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          sm.comb[((kt * 2 + 0) * 2 + ct) * 64 + lane] = dk[ct];
+          sm.comb[((kt * 2 + 1) * 2 + ct) * 64 + lane] = dv[ct];
+        }
+      }
+      __syncthreads();
+      if (qh == 0 && key < N) {
+        const size_t bh = (size_t)cb * H + h;
+        u16* dK = static_cast<u16*>(a.dk) + bh * plane;
+        u16* dV = static_cast<u16*>(a.dv) + bh * plane;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct) {
+          const int c = 16 * ct + 4 * g;
+          if (c >= d) continue;
+          const f32x4 sk = (dk[ct] + sm.comb[((kt * 2 + 0) * 2 + ct) * 64 + lane]) * a.scale;
+          const f32x4 sv = dv[ct] + sm.comb[((kt * 2 + 1) * 2 + ct) * 64 + lane];
+          *reinterpret_cast<u32x2*>(dK + (size_t)key * d + c) = u32x2{pack2(sk[0], sk[1]), pack2(sk[2], sk[3])};
+          *reinterpret_cast<u32x2*>(dV + (size_t)key * d + c) = u32x2{pack2(sv[0], sv[1]), pack2(sv[2], sv[3])};
+        }
+      }
+      dk[0] = dk[1] = dv[0] = dv[1] = zero4;
+      ++cb;
+    }
+    ++it;
+  };
+  for (int b = b0; b < b1; ++b) {
+    step(std::integral_constant<int, 0>{});
+    if (nqb > 1) step(std::integral_constant<int, 1>{});
+    if (nqb > 2) step(std::integral_constant<int, 2>{});
+  }
+  if (key < N) {
+    float* part = a.partial + ((size_t)p * H + h) * N * N;
+#pragma unroll
+    for (int qblk = 0; qblk < 3; ++qblk)
+      if (qblk < nqb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int q = qblk * 128 + 16 * (4 * qh + j) + 4 * g + r;
+            if (q < N) part[(size_t)q * N + key] = rslab[qblk][j][r];
+          }
+  }
+}
+
 // ------------------------------------------------------------------ 2b. dK/dV, eight waves (LDS slab)
 // When the dBias slab sits in LDS and leaves room for only one workgroup per
 // CU (the launches are then split: dK/dV tiles, then dQ tiles), the dK/dV
@@ -1011,9 +1254,12 @@ __device__ __forceinline__ void attn_dq_split_tile(int wg, int nwg, KeySplitLds 
 // ndk_slots workgroups (ndk rounded up to a multiple of 8, so both parts keep
 // their XCD mapping) run the long dK/dV tiles and the dQ tiles fill the
 // slots they leave free, then the chip.  The two roles share the static LDS;
-// the dynamic LDS is the dK/dV slab or the dQ keep bytes.  DK = false builds
-// the dQ role alone (fewer registers) for a launch that carries only dQ tiles;
-// KS = true runs the key-split dQ tiles (nqblocks then counts 16-query tiles).
+// the dynamic LDS is the dK/dV slab or the dQ keep bytes.  NQR selects the
+// dK/dV tile: 0 the LDS slab (or none), 6 the register slab over up to six
+// 64-query steps, 3 the register slab over up to three 128-query steps with
+// LDS-destination staging.  DK = false builds the dQ role alone (fewer
+// registers) for a launch that carries only dQ tiles; KS = true runs the
+// key-split dQ tiles (nqblocks then counts 16-query tiles).
 template <int DP, int QT, bool ALIGNED, bool SLAB, int NQR, bool DK = true, bool KS = false>
 __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nqblocks, int ndk, int ndk_slots) {
   constexpr int KC = DP / 32, CT = DP / 16;
@@ -1029,13 +1275,19 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     DqSmem dq;
     DkdvSmem<DP> dk;
     KeySplitLds ks[KS ? 4 : 1];
+    std::conditional_t<NQR == 3, DkdvWSmem, char> dkw;
   };
   __shared__ Smem sm;
   extern __shared__ f32x4 bwd_dyn_lds[];
   int wg = blockIdx.x, nwg = gridDim.x;
   if constexpr (DK) {
     if (wg < ndk_slots) {
-      if (wg < ndk) attn_dkdv_tile<DP, ALIGNED, SLAB, NQR>(wg, ndk, sm.dk, bwd_dyn_lds, a);
+      if constexpr (NQR == 3) {
+        static_assert(DP == 32 && ALIGNED && SLAB, "128-query steps: d <= 32, N % 8 == 0, slab");
+        if (wg < ndk) attn_dkdv_tile_w(wg, ndk, sm.dkw, a);
+      } else {
+        if (wg < ndk) attn_dkdv_tile<DP, ALIGNED, SLAB, NQR>(wg, ndk, sm.dk, bwd_dyn_lds, a);
+      }
       return;
     }
   }
@@ -1651,7 +1903,9 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
   // bf16, d <= 32, an even number of at most 6 query blocks: the dBias slab
   // sits in registers (no dynamic slab LDS)
   const int nqb64 = (a.N + 63) / 64;
-  const bool reg_slab = bf16 && a.slab && dp == 32 && nqb64 % 2 == 0 && nqb64 <= 6;
+  // the 128-query-step tile: N <= 384, N % 8 == 0, grids that fill the chip
+  const bool wide = bf16 && a.slab && dp == 32 && a.N % 8 == 0 && a.N <= 384 && bhs * nqb64 >= 512;
+  const bool reg_slab = wide || (bf16 && a.slab && dp == 32 && nqb64 % 2 == 0 && nqb64 <= 6);
   const size_t slab_shmem = a.slab && !reg_slab ? slab_bytes(a.N, bf16) : 0;
   if (bf16) {
     // One launch, the dK/dV tiles first and then the dQ tiles, while the slab
@@ -1684,6 +1938,8 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
   }
     if (ks) {
       fn = reg_slab ? PBA_BWD_FNKS(true, 6) : a.slab ? PBA_BWD_FNKS(true, 0) : PBA_BWD_FNKS(false, 0);
+    } else if (wide) {
+      fn = qt2 ? PBA_BWD_FN(32, 2, true, true, 3) : PBA_BWD_FN(32, 1, true, true, 3);
     } else if (reg_slab) {
       if (qt2) fn = al ? PBA_BWD_FN(32, 2, true, true, 6) : PBA_BWD_FN(32, 2, false, true, 6);
       else fn = al ? PBA_BWD_FN(32, 1, true, true, 6) : PBA_BWD_FN(32, 1, false, true, 6);

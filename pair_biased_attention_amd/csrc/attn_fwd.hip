@@ -731,22 +731,25 @@ __global__ void __launch_bounds__(NW * 64) attn_fwd_res_kernel(FwdArgs a) {
         for (int r = 0; r < 4; ++r) acc[s][t][r] = fmaf(qk[r], c1, acc[s][t][r]);
       }
     }
-    // fast path: P = exp2(acc) and the block row sums
+    // fast path: P = exp2(acc) and the block row sums.  The first block has
+    // no reference yet and goes straight to the slow path.
     f32x4 pv[QT][4];
     bf16x8 p0[QT], p1[QT];
     f32x4 bsum[QT];
-    bool slow = false;
+    bool slow = blk == 0;
+    if (blk != 0) {
 #pragma unroll
-    for (int s = 0; s < QT; ++s) {
+      for (int s = 0; s < QT; ++s) {
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[s][t][r] = exp2_fast(acc[s][t][r]);
-      p0[s] = pack8(pv[s][0], pv[s][1]);
-      p1[s] = pack8(pv[s][2], pv[s][3]);
-      bsum[s] = mfma32(ones, p1[s], mfma32(ones, p0[s], zero4));
-      // not (sum <= limit) also catches NaN and +inf
-      slow = slow || ref[s] == kNegInf || !(bsum[s][0] <= kGrowLimit);
+          for (int r = 0; r < 4; ++r) pv[s][t][r] = exp2_fast(acc[s][t][r]);
+        p0[s] = pack8(pv[s][0], pv[s][1]);
+        p1[s] = pack8(pv[s][2], pv[s][3]);
+        bsum[s] = mfma32(ones, p1[s], mfma32(ones, p0[s], zero4));
+        // not (sum <= limit) also catches NaN and +inf
+        slow = slow || ref[s] == kNegInf || !(bsum[s][0] <= kGrowLimit);
+      }
     }
     if (__any(slow)) {
       // slow path: true block maxima, reference moves up (lazily, by more

@@ -114,8 +114,13 @@ SMALL_ATTN = [
     (4, 2, 300, 64, "bf16", "random:13"),    # d = 64, N % 8 != 0 (element-wise bias loads)
     (2, 3, 520, 48, "bf16", "tail:20"),      # d = 48 in the 64-wide tile, slab 72 KB (159 KB with the tiles)
     (2, 2, 600, 64, "bf16", "none"),         # slab 80 KB: too large beside the eight-wave tiles, four-wave tile
-    # grids of >= 512 (b, h) workgroups take the K/V-resident forward kernel
-    (128, 4, 200, 24, "bf16", "tail:7"),     # ragged N, padded d, idle waves past N
+    # grids of >= 512 (b, h) workgroups take the K/V-resident forward kernel;
+    # with N <= 384, N % 8 == 0 and d <= 32 the dK/dV tiles take 128-query
+    # steps with LDS-destination staging
+    (128, 4, 200, 24, "bf16", "tail:7"),     # ragged N, padded d, idle waves past N; two steps per row
+    (32, 4, 264, 32, "bf16", "random:17"),   # three steps per row, the last one 8 queries
+    (64, 4, 128, 16, "bf16", "tail:5"),      # one step per row, d = 16
+    (48, 4, 248, 24, "bf16", "none"),        # two steps per row, the second ragged
     (64, 8, 136, 48, "bf16", "random:5"),    # d = 48 in the 64-wide template
 ]
 
