@@ -1276,6 +1276,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     DkdvSmem<DP> dk;
     KeySplitLds ks[KS ? 4 : 1];
     std::conditional_t<NQR == 3, DkdvWSmem, char> dkw;
+    // NQR == 3 (N <= 384, N % 8 == 0, d <= 32): K and V of the whole (b, h)
+    // resident for the dQ tiles
+    struct {
+      u16 k[(NQR == 3 ? 384 : 1) * 32];
+      u16 v[(NQR == 3 ? 384 : 1) * 32];
+    } dqr;
   };
   __shared__ Smem sm;
   extern __shared__ f32x4 bwd_dyn_lds[];
@@ -1405,9 +1411,27 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
   const int nkb = (N + 63) / 64;
   for (int k = tid; k < nkb * 64; k += 256)
     reinterpret_cast<uint8_t*>(keep_lds)[k] = (k < N && (a.mask == nullptr || a.mask[k] != 0)) ? 1 : 0;
-  fetch(0);
-  fetch_bias(0);
-  commit(0);
+  // NQR == 3: K and V of the (b, h) resident.  Every 1 KB unit i (keys
+  // 16 i .. 16 i + 15 in the key-tile layout) arrives by one LDS-destination
+  // load per tensor, lane l holding the chunk that the row's swizzle puts in
+  // slot l % 4; then one barrier, and the key loop runs without barriers.
+  constexpr bool kResident = NQR == 3;
+  if constexpr (kResident) {
+    const i32x4 krs = rsrc_words(K, kv_bytes), vrs = rsrc_words(V, kv_bytes);
+    for (int i = wave; i < nkb * 4; i += 4) {
+      const int r = 16 * i + (lane >> 2);
+      const int c8 = ((lane & 3) ^ LK::f(r)) & 3;
+      const uint32_t off = 8 * c8 < d ? (uint32_t)((r * d + 8 * c8) * 2) : 0xFFFFFFF0u;
+      lds_dma16(krs, lds_addr(sm.dqr.k) + 1024 * i, off);
+      lds_dma16(vrs, lds_addr(sm.dqr.v) + 1024 * i, off);
+    }
+    fetch_bias(0);
+    vm_wait<0>();
+  } else {
+    fetch(0);
+    fetch_bias(0);
+    commit(0);
+  }
   __syncthreads();
   for (int blk = 0; blk < nkb; ++blk) {
     const int buf = blk & 1;
@@ -1420,15 +1444,15 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     }
     // the next block's loads (past the last block they read zeros and are
     // never used; issuing them anyway keeps every iteration's loads alike)
-    fetch(kb + 64);
+    if constexpr (!kResident) fetch(kb + 64);
     fetch_bias(kb + 64);
     // keep these loads here, a whole iteration ahead of their use (the
     // scheduler would otherwise sink them next to the commit)
     __builtin_amdgcn_sched_barrier(0);
 
     bf16x8 kf[4][KC], vf[4][KC], kt[CT][2];
-    const u16* tK = sK[buf];
-    const u16* tV = sV[buf];
+    const u16* tK = kResident ? sm.dqr.k + kb * 32 : sK[buf];
+    const u16* tV = kResident ? sm.dqr.v + kb * 32 : sV[buf];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -1490,8 +1514,10 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
         dq[s][ct] = mfma32(kt[ct][1], s1, dq[s][ct]);
       }
     }
-    commit(buf ^ 1);
-    __syncthreads();
+    if constexpr (!kResident) {
+      commit(buf ^ 1);
+      __syncthreads();
+    }
   }
 
 #pragma unroll
