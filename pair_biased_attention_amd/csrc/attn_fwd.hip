@@ -127,8 +127,7 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
     }
   };
 
-  // ---- per-wave query fragments (B operand of S^T = K Q^T), unscaled: the
-  // product is scaled by 1/sqrt(d) in fp32
+  // ---- per-wave query fragments (B operand of S^T = K Q^T), unscaled
   bf16x8 qf[QT][KC];
 #pragma unroll
   for (int s = 0; s < QT; ++s) {
@@ -142,7 +141,16 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  const bf16x8 id_lo = ident_rows_frag(lane, 0), id_hi = ident_rows_frag(lane, 1);
+  // T = Q K^T + bias / scale on the matrix core: the bias enters through two
+  // identity products with 1/scale split into bf16 hi + lo, and Q K^T
+  // accumulates onto them unscaled, so no score takes a separate scaling
+  // step.  The exponentials apply cs = scale * log2(e): P = exp2(cs (T - m)),
+  // and the natural-log LSE is scale * m + ln(l).
+  const float isc = 1.f / a.scale;
+  const uint32_t isc_hi = f2bf(isc), isc_lo = f2bf(isc - bf2f((u16)isc_hi));
+  const bf16x8 ih0 = ident_rows_frag(lane, 0, isc_hi), ih1 = ident_rows_frag(lane, 1, isc_hi);
+  const bf16x8 il0 = ident_rows_frag(lane, 0, isc_lo), il1 = ident_rows_frag(lane, 1, isc_lo);
+  const float cs = a.scale * kLog2e;
   const bf16x8 ones = ones_frag();
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 oacc[QT][CT];
@@ -235,18 +243,14 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
         blo[e] = (blo[e] & ~mlo[e]) | (kMaskedBias2 & mlo[e]);
         bhi[e] = (bhi[e] & ~mhi[e]) | (kMaskedBias2 & mhi[e]);
       }
-      acc[s][0] = mfma32(id_lo, as_bf8(blo), zero4);  // keys 16g + 0..3
-      acc[s][1] = mfma32(id_hi, as_bf8(blo), zero4);  // keys 16g + 4..7
-      acc[s][2] = mfma32(id_lo, as_bf8(bhi), zero4);  // keys 16g + 8..11
-      acc[s][3] = mfma32(id_hi, as_bf8(bhi), zero4);  // keys 16g + 12..15
+      acc[s][0] = mfma32(il0, as_bf8(blo), mfma32(ih0, as_bf8(blo), zero4));  // keys 16g + 0..3
+      acc[s][1] = mfma32(il1, as_bf8(blo), mfma32(ih1, as_bf8(blo), zero4));  // keys 16g + 4..7
+      acc[s][2] = mfma32(il0, as_bf8(bhi), mfma32(ih0, as_bf8(bhi), zero4));  // keys 16g + 8..11
+      acc[s][3] = mfma32(il1, as_bf8(bhi), mfma32(ih1, as_bf8(bhi), zero4));  // keys 16g + 12..15
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        f32x4 qk = zero4;
+      for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int kc = 0; kc < KC; ++kc) qk = mfma32(kf[t][kc], qf[s][kc], qk);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) acc[s][t][r] = fmaf(qk[r], a.scale, acc[s][t][r]);
-      }
+        for (int kc = 0; kc < KC; ++kc) acc[s][t] = mfma32(kf[t][kc], qf[s][kc], acc[s][t]);
     }
 
     // block maxima of every sub-tile, then one (rarely taken) rescale branch,
@@ -266,14 +270,14 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
       m = fmaxf(m, fmaxf(fmaxf(fmaxf(acc[s][2][0], acc[s][2][1]), fmaxf(acc[s][2][2], acc[s][2][3])),
                          fmaxf(fmaxf(acc[s][3][0], acc[s][3][1]), fmaxf(acc[s][3][2], acc[s][3][3]))));
       mx[s] = max_over_groups(m);
-      grow = grow || (mx[s] * kLog2e > mrun[s] * kLog2e + 8.f);
+      grow = grow || (mx[s] * cs > mrun[s] * cs + 8.f);
     }
     if (__any(grow)) {
 #pragma unroll
       for (int s = 0; s < QT; ++s) {
-        if (mx[s] * kLog2e > mrun[s] * kLog2e + 8.f) {
+        if (mx[s] * cs > mrun[s] * cs + 8.f) {
           const float mnew = fmaxf(mrun[s], mx[s]);
-          const float alpha = exp2_fast((mrun[s] - mnew) * kLog2e);  // 0 when mrun is -inf or masked
+          const float alpha = exp2_fast((mrun[s] - mnew) * cs);  // 0 when mrun is -inf or masked
 #pragma unroll
           for (int ct = 0; ct < CT; ++ct) oacc[s][ct] *= alpha;
           lacc[s] *= alpha;
@@ -284,11 +288,11 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
     for (int s = 0; s < QT; ++s) {
       // a row whose keys so far are all masked keeps P = 0
-      const float msc = (mrun[s] < kMaskedThreshold) ? kPosInf : mrun[s] * kLog2e;
+      const float msc = (mrun[s] < kMaskedThreshold) ? kPosInf : mrun[s] * cs;
 #pragma unroll
       for (int t = 0; t < 4; ++t)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[s][t][r] = exp2_fast(fmaf(acc[s][t][r], kLog2e, -msc));
+        for (int r = 0; r < 4; ++r) acc[s][t][r] = exp2_fast(fmaf(acc[s][t][r], cs, -msc));
       // P^T as the B operand: k slot (g, v) <-> key 16g + 8m + v
       const bf16x8 p0 = pack8(acc[s][0], acc[s][1]);
       const bf16x8 p1 = pack8(acc[s][2], acc[s][3]);
@@ -328,7 +332,7 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
       }
       *reinterpret_cast<u32x2*>(O + off) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
     }
-    if (g == 0) LSE[qrow] = l > 0.f ? mrun[s] + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
+    if (g == 0) LSE[qrow] = l > 0.f ? mrun[s] * a.scale + __builtin_amdgcn_logf(l) * kLn2 : kNegInf;
   }
 }
 
@@ -384,7 +388,16 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
   const bf16x8 qf = as_bf8(rq);
   __syncthreads();  // keep bytes
 
-  const bf16x8 id_lo = ident_rows_frag(lane, 0), id_hi = ident_rows_frag(lane, 1);
+  // T = Q K^T + bias / scale on the matrix core: the bias enters through two
+  // identity products with 1/scale split into bf16 hi + lo, and Q K^T
+  // accumulates onto them unscaled, so no score takes a separate scaling
+  // step.  The exponentials apply cs = scale * log2(e): P = exp2(cs (T - m)),
+  // and the natural-log LSE is scale * m + ln(l).
+  const float isc = 1.f / a.scale;
+  const uint32_t isc_hi = f2bf(isc), isc_lo = f2bf(isc - bf2f((u16)isc_hi));
+  const bf16x8 ih0 = ident_rows_frag(lane, 0, isc_hi), ih1 = ident_rows_frag(lane, 1, isc_hi);
+  const bf16x8 il0 = ident_rows_frag(lane, 0, isc_lo), il1 = ident_rows_frag(lane, 1, isc_lo);
+  const float cs = a.scale * kLog2e;
   const bf16x8 ones = ones_frag();
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   f32x4 oacc[2] = {zero4, zero4};
@@ -423,16 +436,12 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
       }
     }
     f32x4 acc[4];
-    acc[0] = mfma32(id_lo, as_bf8(blo4), zero4);  // keys 16g + 0..3
-    acc[1] = mfma32(id_hi, as_bf8(blo4), zero4);  // keys 16g + 4..7
-    acc[2] = mfma32(id_lo, as_bf8(bhi4), zero4);  // keys 16g + 8..11
-    acc[3] = mfma32(id_hi, as_bf8(bhi4), zero4);  // keys 16g + 12..15
+    acc[0] = mfma32(il0, as_bf8(blo4), mfma32(ih0, as_bf8(blo4), zero4));  // keys 16g + 0..3
+    acc[1] = mfma32(il1, as_bf8(blo4), mfma32(ih1, as_bf8(blo4), zero4));  // keys 16g + 4..7
+    acc[2] = mfma32(il0, as_bf8(bhi4), mfma32(ih0, as_bf8(bhi4), zero4));  // keys 16g + 8..11
+    acc[3] = mfma32(il1, as_bf8(bhi4), mfma32(ih1, as_bf8(bhi4), zero4));  // keys 16g + 12..15
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const f32x4 qk = mfma32(kf[t], qf, zero4);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(qk[r], a.scale, acc[t][r]);
-    }
+    for (int t = 0; t < 4; ++t) acc[t] = mfma32(kf[t], qf, acc[t]);
     float m = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
                     fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
     m = fmaxf(m, fmaxf(fmaxf(fmaxf(acc[2][0], acc[2][1]), fmaxf(acc[2][2], acc[2][3])),
@@ -440,22 +449,22 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
     const float mx = max_over_groups(m);
     // lazy rescaling as in the streaming kernel: the reference moves only
     // when a block's maximum passes it by more than 8 in log2 units
-    const bool grow = mx * kLog2e > mrun * kLog2e + 8.f;
+    const bool grow = mx * cs > mrun * cs + 8.f;
     if (__any(grow)) {
       if (grow) {
         const float mnew = fmaxf(mrun, mx);
-        const float alpha = exp2_fast((mrun - mnew) * kLog2e);  // 0 when mrun is -inf or masked
+        const float alpha = exp2_fast((mrun - mnew) * cs);  // 0 when mrun is -inf or masked
         oacc[0] *= alpha;
         oacc[1] *= alpha;
         lacc *= alpha;
         mrun = mnew;
       }
     }
-    const float msc = (mrun < kMaskedThreshold) ? kPosInf : mrun * kLog2e;  // every key so far masked: P = 0
+    const float msc = (mrun < kMaskedThreshold) ? kPosInf : mrun * cs;  // every key so far masked: P = 0
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[t][r] = exp2_fast(fmaf(acc[t][r], kLog2e, -msc));
+      for (int r = 0; r < 4; ++r) acc[t][r] = exp2_fast(fmaf(acc[t][r], cs, -msc));
     const bf16x8 p0 = pack8(acc[0], acc[1]);
     const bf16x8 p1 = pack8(acc[2], acc[3]);
 #pragma unroll
@@ -498,7 +507,7 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
   for (int w = 0; w < 4; ++w) {
     const float2 s = reinterpret_cast<const float2*>(wl[w].v)[mq];
     if (s.y > 0.f) {
-      const float f = exp2_fast((s.x - M) * kLog2e);
+      const float f = exp2_fast((s.x - M) * cs);
       const float* pw = reinterpret_cast<const float*>(wl[w].k) + mq * 32 + c;
       lsum = fmaf(f, s.y, lsum);
       o0 = fmaf(f, pw[0], o0);
@@ -513,7 +522,7 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
         pack2(o0 * inv * sigmoidf_fast(g0), o1 * inv * sigmoidf_fast(g1));
   }
   if (cp == 0 && qrow < N)
-    a.lse[bh * N + qrow] = lsum > 0.f ? M + __builtin_amdgcn_logf(lsum) * kLn2 : kNegInf;
+    a.lse[bh * N + qrow] = lsum > 0.f ? M * a.scale + __builtin_amdgcn_logf(lsum) * kLn2 : kNegInf;
 }
 
 // ---------------------------------------------------------------- K/V-resident variant
@@ -525,10 +534,10 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
 // prefetched one block ahead; its Q and gate rows are requested before the
 // staging barrier.
 //
-// Softmax in log2 units with a reference maximum.  Q is scaled by
-// log2(e)/sqrt(d) and the bias is multiplied by log2(e) on the matrix core
-// (two identity products, log2(e) split into bf16 hi + lo), so scores are
-// S' = log2(e) * L.  The first key block sets each query's reference r to its
+// Softmax in log2 units with a reference maximum.  The Q K^T product is
+// scaled by log2(e)/sqrt(d) in fp32 and the bias is multiplied by log2(e) on
+// the matrix core (two identity products, log2(e) split into bf16 hi + lo),
+// so scores are S' = log2(e) * L.  The first key block sets each query's reference r to its
 // block maximum; every later block starts its accumulators at -r, so
 // P = exp2(S') is one exponential per score.  The block's row sums (ones
 // product on the matrix core) show whether any P may exceed 2^8 (sum above
