@@ -580,33 +580,46 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
 }
 
 // ------------------------------------------------------------------ 2c. dK/dV, 128-query steps
-// The register-slab tile (d <= 32, N <= 384, N % 8 == 0) in steps of 128
-// queries: wave (kt, qh) takes its 16 keys against query half qh of the step
-// (four 16-query tiles), so a step carries twice the products of the
-// 64-query form per barrier.  Every operand of a step -- the Q and dA tiles,
-// the row seeds, each wave's own bias tiles and, at a row's first step, the
-// K and V rows -- goes from memory straight into LDS through LDS-destination
-// buffer loads issued one step ahead into the other of two buffers.  No
-// register holds a staged tile and no LDS store is issued; each step ends
-// with one wait for this wave's loads and the barrier that publishes them.
+// The register-slab tile (d <= 32, N % 8 == 0) in steps of 128 queries.  A
+// workgroup of NW waves owns 32 keys; wave (kt, qg) takes its 16 keys against
+// query group qg of every step, JT = 16 / NW of its eight 16-query tiles:
+//   NW = 4: two groups of four tiles, N <= 384 (three steps per row);
+//   NW = 8: four groups of two tiles, N <= 768 (six steps per row).
+// Either way a wave's dBias slab is 12 register tiles (48 VGPRs), so no LDS
+// slab limits the workgroups per CU.  Every operand of a step -- the Q and
+// dA tiles, the row seeds, each wave's own bias tiles and, at a row's first
+// step, the K and V rows -- goes from memory straight into LDS through
+// LDS-destination buffer loads issued one step ahead into the other of two
+// buffers.  No register holds a staged tile and no LDS store is issued; each
+// step ends with one wait for this wave's loads and the barrier that
+// publishes them.  At a row's end the query groups' dK and dV are summed in
+// group order.
+template <int NW>
 struct DkdvWSmem {
-  u16 qa[2][2 * 128 * 32];       // [buffer][Q tile | dA tile], TileLds<32, 0> rows
-  float2 seed[2][128];           // [buffer] (-log2(e) LSE, -D) per query of the step
-  u32x4 bias[2][4][2][64];       // [buffer][wave][half u][lane]: the wave's own bias
-  u32x4 kv[2][2][2][64];         // [row parity][K | V][key tile][lane]
-  f32x4 comb[2 * 2 * 2 * 64];    // query-half combine area of dK, dV
+  static constexpr int JT = 16 / NW;  // 16-query tiles per wave and step
+  u16 qa[2][2 * 128 * 32];            // [buffer][Q tile | dA tile], TileLds<32, 0> rows
+  float2 seed[2][128];                // [buffer] (-log2(e) LSE, -D) per query of the step
+  u32x4 bias[2][NW][JT / 2][64];      // [buffer][wave][half u][lane]: the wave's own bias
+  u32x4 kv[2][2][2][64];              // [row parity][K | V][key tile][lane]
+  f32x4 comb[NW / 2 - 1][2][2][2][64];  // [group - 1][kt][dK | dV][ct][lane]
 };
 
-__device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm, const BwdArgs& a) {
+template <int NW>
+__device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem<NW>& sm, const BwdArgs& a) {
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
   using LQ = TileLds<32, 0>;
+  constexpr int JT = DkdvWSmem<NW>::JT;
+  constexpr int NQB = 12 / JT;    // most 128-query steps per row: 3 or 6
+  constexpr int NG = NW / 2;      // query groups
+  constexpr int UQ = 8 / NW;      // Q (and dA) loads per wave and step
   constexpr int kTile = 128 * 32;
   constexpr uint32_t kOob = 0xFFFFFFF0u;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, n = lane & 15;
-  const int kt = wave & 1, qh = wave >> 1;
+  const int kt = wave & 1, qg = wave >> 1;
   const int N = a.N, d = a.d, H = a.H;
   const int nkb = (N + 31) / 32;
-  const int nqb = (N + 127) / 128;  // 1 .. 3
+  const int nqb = (N + 127) / 128;  // 1 .. NQB
   const int L = xcd_remap(wg, nwg);
   const int kblk = L % nkb;
   const int hp = L / nkb;
@@ -620,26 +633,26 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm,
   const bool keep_lane = key < N && (a.mask == nullptr || a.mask[key] != 0);
   const bool wave_masked = __any(!keep_lane);
 
-  // per-lane load offsets.  Q / dA: instruction i of this wave fills tile
-  // units 64 (2 wave + i) + lane, i.e. row r = 16 (2 wave + i) + lane / 4 and
-  // the 16-byte chunk that the row's swizzle puts in slot lane % 4.
-  bool qa_ok[2];
-  uint32_t qa_off[2];
+  // per-lane load offsets.  Q / dA: load i of this wave fills tile units
+  // 64 (UQ wave + i) + lane, i.e. row r = 16 (UQ wave + i) + lane / 4 and the
+  // 16-byte chunk that the row's swizzle puts in slot lane % 4.
+  bool qa_ok[UQ];
+  uint32_t qa_off[UQ];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = 16 * (2 * wave + i) + (lane >> 2);
+  for (int i = 0; i < UQ; ++i) {
+    const int r = 16 * (UQ * wave + i) + (lane >> 2);
     const int c = ((lane & 3) ^ LQ::f(r)) & 3;
     qa_ok[i] = 8 * c < d;
     qa_off[i] = (uint32_t)((r * d + 8 * c) * 2);
   }
-  // bias: half u holds query rows 64 qh + 16 (2u + g/2) + n of the step, keys
+  // bias: half u holds query rows 16 (JT qg + 2u + g/2) + n of the step, keys
   // k0 .. k0 + 7; the identity product of tile j reads half j / 2, lane
   // groups 2 (j % 2) and 2 (j % 2) + 1
   const int k0 = kb + 16 * kt + 8 * (g & 1);
-  const int bq0 = 64 * qh + 16 * (g >> 1) + n;
-  // K / V at a row's start: wave w loads K (w even) or V (w odd) of key tile
-  // w / 2: lane (g, n) key kb + 16 (w / 2) + n, channels 8g .. 8g + 7
-  const int kv_key = kb + 16 * (wave >> 1) + n;
+  const int bq0 = 16 * (JT * qg + (g >> 1)) + n;
+  // K / V at a row's start: wave w < 4 loads K (w even) or V (w odd) of key
+  // tile w / 2: lane (g, n) key kb + 16 (w / 2) + n, channels 8g .. 8g + 7
+  const int kv_key = kb + 16 * ((wave >> 1) & 1) + n;
   const uint32_t kv_off = (8 * g < d) ? (uint32_t)((kv_key * d + 8 * g) * 2) : kOob;
   const i32x4 brs = rsrc_words(static_cast<const u16*>(a.bias) + (size_t)h * N * N, (uint32_t)((size_t)N * N * 2));
 
@@ -655,20 +668,20 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm,
     const uint32_t qoff = (uint32_t)(fq * 128 * d * 2);
     const uint32_t dq = lds_addr(sm.qa[buf]);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < UQ; ++i) {
       const uint32_t off = qa_ok[i] ? qa_off[i] + qoff : kOob;
-      lds_dma16(rq, dq + 1024 * (2 * wave + i), off);
-      lds_dma16(ra, dq + 2 * kTile + 1024 * (2 * wave + i), off);
+      lds_dma16(rq, dq + 1024 * (UQ * wave + i), off);
+      lds_dma16(ra, dq + 2 * kTile + 1024 * (UQ * wave + i), off);
     }
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < JT / 2; ++u) {
       const int q = fq * 128 + bq0 + 32 * u;
       const uint32_t off = (q < N && k0 < N) ? (uint32_t)(((size_t)q * N + k0) * 2) : kOob;
       lds_dma16(brs, lds_addr(&sm.bias[buf][wave][u][0]), off);
     }
     if (wave == 0)
       lds_dma16(rsrc_words(fS, (uint32_t)N * 8u), lds_addr(sm.seed[buf]), (uint32_t)((fq * 128 + 2 * lane) * 8));
-    if (fq == 0)
+    if (fq == 0 && wave < 4)
       lds_dma16(rsrc_words(fKV, plane_bytes), lds_addr(&sm.kv[(fb - b0) & 1][wave & 1][wave >> 1][0]), kv_off);
     if (++fq == nqb) {
       fq = 0;
@@ -684,11 +697,11 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm,
   const bf16x8 id_l2lo[2] = {ident_cols_frag(lane, kLog2eLoBf16, 0), ident_cols_frag(lane, kLog2eLoBf16, 2)};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   const float c1 = a.scale * kLog2e;
-  f32x4 rslab[3][4];
+  f32x4 rslab[NQB][JT];
 #pragma unroll
-  for (int i = 0; i < 3; ++i)
+  for (int i = 0; i < NQB; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rslab[i][j] = zero4;
+    for (int j = 0; j < JT; ++j) rslab[i][j] = zero4;
   f32x4 dk[2], dv[2];
   dk[0] = dk[1] = dv[0] = dv[1] = zero4;
   bf16x8 kf, vf;
@@ -709,11 +722,11 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm,
     }
     const u16* tQ = sm.qa[buf];
     const u16* tA = tQ + kTile;
-    f32x4 sacc[4], dp[4];
-    bf16x8 qfr[4], afr[4];
+    f32x4 sacc[JT], dp[JT];
+    bf16x8 qfr[JT], afr[JT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int qt = 4 * qh + j;
+    for (int j = 0; j < JT; ++j) {
+      const int qt = JT * qg + j;
       const f32x4 s01 = *reinterpret_cast<const f32x4*>(&sm.seed[buf][16 * qt + 4 * g]);
       const f32x4 s23 = *reinterpret_cast<const f32x4*>(&sm.seed[buf][16 * qt + 4 * g + 2]);
       sacc[j] = f32x4{s01[0], s01[2], s23[0], s23[2]};
@@ -721,30 +734,32 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm,
       qfr[j] = as_bf8(*reinterpret_cast<const u32x4*>(&tQ[LQ::off(16 * qt + n, 8 * g)]));
       afr[j] = as_bf8(*reinterpret_cast<const u32x4*>(&tA[LQ::off(16 * qt + n, 8 * g)]));
     }
-    bf16x8 trA[2][2], trQ[2][2];
+    bf16x8 trA[JT / 2][2], trQ[JT / 2][2];
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < JT / 2; ++m)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct) {
-        const int r0 = 64 * qh + 32 * m + 4 * g;
+        const int r0 = 16 * (JT * qg + 2 * m) + 4 * g;
         trA[m][ct] = tr_frag_l<LQ>(tA, r0, r0 + 16, 16 * ct, lane);
         trQ[m][ct] = tr_frag_l<LQ>(tQ, r0, r0 + 16, 16 * ct, lane);
       }
-    const bf16x8 bb[2] = {as_bf8(sm.bias[buf][wave][0][lane]), as_bf8(sm.bias[buf][wave][1][lane])};
+    bf16x8 bb[JT / 2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sacc[j] = mfma32(bb[j >> 1], id_l2hi[j & 1], sacc[j]);
+    for (int u = 0; u < JT / 2; ++u) bb[u] = as_bf8(sm.bias[buf][wave][u][lane]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) sacc[j] = mfma32(bb[j >> 1], id_l2lo[j & 1], sacc[j]);
-    f32x4 qk[4];
+    for (int j = 0; j < JT; ++j) sacc[j] = mfma32(bb[j >> 1], id_l2hi[j & 1], sacc[j]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < JT; ++j) sacc[j] = mfma32(bb[j >> 1], id_l2lo[j & 1], sacc[j]);
+    f32x4 qk[JT];
+#pragma unroll
+    for (int j = 0; j < JT; ++j) {
       qk[j] = mfma32(qfr[j], kf, zero4);
       dp[j] = mfma32(afr[j], vf, dp[j]);
     }
     // P = exp2(S'), dS = P * (dP - D)
-    f32x4 pj[4], dsj[4];
+    f32x4 pj[JT], dsj[JT];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < JT; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         pj[j][r] = exp2_fast(fmaf(qk[j][r], c1, sacc[j][r]));
@@ -752,14 +767,14 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm,
       }
     if (wave_masked && !keep_lane) {  // masked keys: P = dS = 0
 #pragma unroll
-      for (int j = 0; j < 4; ++j) pj[j] = dsj[j] = zero4;
+      for (int j = 0; j < JT; ++j) pj[j] = dsj[j] = zero4;
     }
     // P and dS as 16x16x32 operands: k slot (g, v) of product m is query
-    // row 64 qh + 32 m + 16 (v / 4) + 4 g + v % 4 of the step
+    // row 16 (JT qg + 2m) + 16 (v / 4) + 4 g + v % 4 of the step
 #pragma unroll
-    for (int j = 0; j < 4; ++j) rslab[QB][j] += dsj[j];
+    for (int j = 0; j < JT; ++j) rslab[QB][j] += dsj[j];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
+    for (int m = 0; m < JT / 2; ++m) {
       const bf16x8 pb = pack8(pj[2 * m], pj[2 * m + 1]);
       const bf16x8 dsb = pack8(dsj[2 * m], dsj[2 * m + 1]);
 #pragma unroll
@@ -771,17 +786,17 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm,
     vm_wait<0>();  // this wave's loads of the next step have landed
     __syncthreads();
     if (last_q) {
-      // combine the two query halves and store dK, dV of row cb; `comb` is
-      // written again only a row later, after at least one more barrier
-      if (qh == 1) {
+      // sum the query groups' dK, dV in group order and store row cb; `comb`
+      // is written again only a row later, after at least one more barrier
+      if (qg > 0) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct) {
-          sm.comb[((kt * 2 + 0) * 2 + ct) * 64 + lane] = dk[ct];
-          sm.comb[((kt * 2 + 1) * 2 + ct) * 64 + lane] = dv[ct];
+          sm.comb[qg - 1][kt][0][ct][lane] = dk[ct];
+          sm.comb[qg - 1][kt][1][ct][lane] = dv[ct];
         }
       }
       __syncthreads();
-      if (qh == 0 && key < N) {
+      if (qg == 0 && key < N) {
         const size_t bh = (size_t)cb * H + h;
         u16* dK = static_cast<u16*>(a.dk) + bh * plane;
         u16* dV = static_cast<u16*>(a.dv) + bh * plane;
@@ -789,8 +804,13 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm,
         for (int ct = 0; ct < 2; ++ct) {
           const int c = 16 * ct + 4 * g;
           if (c >= d) continue;
-          const f32x4 sk = (dk[ct] + sm.comb[((kt * 2 + 0) * 2 + ct) * 64 + lane]) * a.scale;
-          const f32x4 sv = dv[ct] + sm.comb[((kt * 2 + 1) * 2 + ct) * 64 + lane];
+          f32x4 sk = dk[ct], sv = dv[ct];
+#pragma unroll
+          for (int q2 = 0; q2 < NG - 1; ++q2) {
+            sk += sm.comb[q2][kt][0][ct][lane];
+            sv += sm.comb[q2][kt][1][ct][lane];
+          }
+          sk *= a.scale;
           *reinterpret_cast<u32x2*>(dK + (size_t)key * d + c) = u32x2{pack2(sk[0], sk[1]), pack2(sk[2], sk[3])};
           *reinterpret_cast<u32x2*>(dV + (size_t)key * d + c) = u32x2{pack2(sv[0], sv[1]), pack2(sv[2], sv[3])};
         }
@@ -804,20 +824,33 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem& sm,
     step(std::integral_constant<int, 0>{});
     if (nqb > 1) step(std::integral_constant<int, 1>{});
     if (nqb > 2) step(std::integral_constant<int, 2>{});
+    if constexpr (NQB > 3) {
+      if (nqb > 3) step(std::integral_constant<int, 3>{});
+      if (nqb > 4) step(std::integral_constant<int, 4>{});
+      if (nqb > 5) step(std::integral_constant<int, 5>{});
+    }
   }
   if (key < N) {
     float* part = a.partial + ((size_t)p * H + h) * N * N;
 #pragma unroll
-    for (int qblk = 0; qblk < 3; ++qblk)
+    for (int qblk = 0; qblk < NQB; ++qblk)
       if (qblk < nqb)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < JT; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int q = qblk * 128 + 16 * (4 * qh + j) + 4 * g + r;
+            const int q = qblk * 128 + 16 * (JT * qg + j) + 4 * g + r;
             if (q < N) part[(size_t)q * N + key] = rslab[qblk][j][r];
           }
   }
+}
+
+// The eight-wave form as a launch of its own (one workgroup per CU, two
+// waves per SIMD): the dK/dV tiles for 384 < N <= 768 at d <= 32, followed by
+// a dQ-only launch.
+__global__ void __launch_bounds__(512) attn_bwd_dkdv_w8_kernel(BwdArgs a) {
+  __shared__ DkdvWSmem<8> sm;
+  attn_dkdv_tile_w<8>(blockIdx.x, gridDim.x, sm, a);
 }
 
 // ------------------------------------------------------------------ 2b. dK/dV, eight waves (LDS slab)
@@ -1275,7 +1308,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     DqSmem dq;
     DkdvSmem<DP> dk;
     KeySplitLds ks[KS ? 4 : 1];
-    std::conditional_t<NQR == 3, DkdvWSmem, char> dkw;
+    std::conditional_t<NQR == 3, DkdvWSmem<4>, char> dkw;
     // NQR == 3 (N <= 384, N % 8 == 0, d <= 32): K and V of the whole (b, h)
     // resident for the dQ tiles
     struct {
@@ -1290,7 +1323,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
     if (wg < ndk_slots) {
       if constexpr (NQR == 3) {
         static_assert(DP == 32 && ALIGNED && SLAB, "128-query steps: d <= 32, N % 8 == 0, slab");
-        if (wg < ndk) attn_dkdv_tile_w(wg, ndk, sm.dkw, a);
+        if (wg < ndk) attn_dkdv_tile_w<4>(wg, ndk, sm.dkw, a);
       } else {
         if (wg < ndk) attn_dkdv_tile<DP, ALIGNED, SLAB, NQR>(wg, ndk, sm.dk, bwd_dyn_lds, a);
       }
@@ -2004,7 +2037,15 @@ hipError_t launch_attn_bwd(const BwdArgs& args, bool bf16, hipStream_t stream, K
       // tile (at d <= 32 the eight-wave form measured slower: each wave's
       // per-block overhead is paid for half the products)
       const size_t lds8 = sizeof(Dkdv8Smem<64>) + slab_shmem;
-      if (dp == 64 && a.slab && !reg_slab && lds8 <= 160 * 1024) {
+      // 384 < N <= 768 at d <= 32: eight-wave 128-query steps with the dBias
+      // slab in registers (no LDS slab)
+      const bool w8 = dp == 32 && al && a.slab && a.N > 384 && a.N <= 768;
+      if (w8) {
+        void* kargs[] = {&a};
+        if ((e = hipLaunchKernel(reinterpret_cast<const void*>(&attn_bwd_dkdv_w8_kernel), dim3((unsigned)ndk),
+                                 dim3(512), kargs, 0, stream)) != hipSuccess)
+          return e;
+      } else if (dp == 64 && a.slab && !reg_slab && lds8 <= 160 * 1024) {
         const void* f8 = al ? reinterpret_cast<const void*>(&attn_bwd_dkdv8_kernel<64, true>)
                             : reinterpret_cast<const void*>(&attn_bwd_dkdv8_kernel<64, false>);
         if (slab_shmem > 64 * 1024 &&

@@ -108,9 +108,15 @@ SMALL_ATTN = [
     (1, 2, 256, 32, "bf16", "tail:64"),      # one block per wave, the last wave's block wholly masked
     (1, 2, 2048, 8, "bf16", "random:30"),    # 32 blocks, d = 8
     (2, 2, 264, 32, "bf16", "random:17"),    # the same split for dQ beside dK/dV tiles with the dBias slab in LDS
-    # the dBias slab in LDS with room for one workgroup per CU: separate
-    # dK/dV and dQ launches, the dK/dV tiles at d > 32 in eight-wave workgroups
-    (3, 2, 456, 32, "bf16", "tail:11"),      # d = 32: four-wave dK/dV launch, slab 64 KB
+    # a dBias slab too large for two workgroups per CU: separate dK/dV and dQ
+    # launches.  384 < N <= 768 at d <= 32 (N % 8 == 0): eight-wave dK/dV
+    # workgroups in 128-query steps with the slab in registers; at d > 32 the
+    # eight-wave 64-query tiles beside an LDS slab
+    (3, 2, 456, 32, "bf16", "tail:11"),      # four steps per row, the last one 72 queries
+    (4, 2, 520, 32, "bf16", "random:9"),     # five steps, the last one 8 queries
+    (3, 3, 640, 16, "bf16", "tail:30"),      # five full steps, d = 16
+    (2, 2, 768, 24, "bf16", "none"),         # six steps, d = 24
+    (24, 2, 448, 32, "bf16", "tail:13"),     # several batch chunks of a few rows each
     (4, 2, 300, 64, "bf16", "random:13"),    # d = 64, N % 8 != 0 (element-wise bias loads)
     (2, 3, 520, 48, "bf16", "tail:20"),      # d = 48 in the 64-wide tile, slab 72 KB (159 KB with the tiles)
     (2, 2, 600, 64, "bf16", "none"),         # slab 80 KB: too large beside the eight-wave tiles, four-wave tile
