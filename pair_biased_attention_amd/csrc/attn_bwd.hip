@@ -1825,7 +1825,22 @@ __global__ void __launch_bounds__(256) bias_grad_reduce_kernel(const float* part
   typedef float f4 __attribute__((ext_vector_type(4)));
   f4 s = {0.f, 0.f, 0.f, 0.f};
   if (i4 + 4 <= count && (count & 3) == 0) {  // every partial plane stays 16-byte aligned
-    for (int p = 0; p < P; ++p) s += *reinterpret_cast<const f4*>(partial + (size_t)p * count + i4);
+    // eight partials requested at a time, then added in index order
+    int p = 0;
+    for (; p + 8 <= P; p += 8) {
+      f4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = *reinterpret_cast<const f4*>(partial + (size_t)(p + k) * count + i4);
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s += v[k];
+    }
+    for (; p < P; ++p) s += *reinterpret_cast<const f4*>(partial + (size_t)p * count + i4);
+    if constexpr (BF16) {
+      *reinterpret_cast<u32x2*>(static_cast<u16*>(out) + i4) = u32x2{pack2(s[0], s[1]), pack2(s[2], s[3])};
+    } else {
+      *reinterpret_cast<f4*>(static_cast<float*>(out) + i4) = s;
+    }
+    return;
   } else {
     for (int p = 0; p < P; ++p)
       for (int e = 0; e < 4; ++e)
