@@ -106,10 +106,13 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int l
   const float l = (row < rows && c == 0) ? a.lse[row] : 0.f;
   float D = 0.f;
   if (live) {
+    // dO, O and G are read only here and dG is written only here, so they go
+    // through the caches as streaming (nontemporal) accesses and do not evict
+    // the tensors the next launch reads again (Q, K, V, dA, bias, seeds)
     const size_t off = (size_t)row * a.d + 8 * c;
-    const u32x4 xo = ld16(static_cast<const u16*>(a.dout) + off);
-    const u32x4 xv = ld16(static_cast<const u16*>(a.out) + off);
-    const u32x4 xg = ld16(static_cast<const u16*>(a.g) + off);
+    const u32x4 xo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const u16*>(a.dout) + off));
+    const u32x4 xv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const u16*>(a.out) + off));
+    const u32x4 xg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(static_cast<const u16*>(a.g) + off));
     u32x4 ra, rg;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -127,7 +130,7 @@ __global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int l
       rg[e] = pack2(gg[0], gg[1]);
     }
     *reinterpret_cast<u32x4*>(static_cast<u16*>(a.da) + off) = ra;
-    *reinterpret_cast<u32x4*>(static_cast<u16*>(a.dg) + off) = rg;
+    __builtin_nontemporal_store(rg, reinterpret_cast<u32x4*>(static_cast<u16*>(a.dg) + off));
   }
   for (int m = 1; m < lanes; m <<= 1) D += __shfl_xor(D, m);
   // rows without keys (LSE = -inf) get the seed -inf, so P = exp2(-inf) = 0

@@ -840,7 +840,11 @@ __global__ void __launch_bounds__(256) pwa_bwd_pre_kernel(PwaArgs a) {
   const u16* dO = static_cast<const u16*>(a.dout);
   const u16* O = static_cast<const u16*>(a.out);
   const u16* G = static_cast<const u16*>(a.g);
-  const u32x4 xo = ld16(dO + 8 * i8), xv = ld16(O + 8 * i8), xg = ld16(G + 8 * i8);
+  // read-once inputs and the write-once dG as streaming (nontemporal)
+  // accesses: the dV / dw launch that follows reads dA and V again
+  const u32x4 xo = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(dO + 8 * i8));
+  const u32x4 xv = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(O + 8 * i8));
+  const u32x4 xg = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(G + 8 * i8));
   u32x4 ra, rg;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
@@ -851,7 +855,7 @@ __global__ void __launch_bounds__(256) pwa_bwd_pre_kernel(PwaArgs a) {
     rg[e] = pack2(f0 * o0 * (1.f - s0), f1 * o1 * (1.f - s1));
   }
   *reinterpret_cast<u32x4*>(static_cast<u16*>(a.da) + 8 * i8) = ra;
-  *reinterpret_cast<u32x4*>(static_cast<u16*>(a.dg) + 8 * i8) = rg;
+  __builtin_nontemporal_store(rg, reinterpret_cast<u32x4*>(static_cast<u16*>(a.dg) + 8 * i8));
 }
 
 // ------------------------------------------------------------------ db
