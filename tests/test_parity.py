@@ -117,6 +117,7 @@ SMALL_ATTN = [
     (3, 3, 640, 16, "bf16", "tail:30"),      # five full steps, d = 16
     (2, 2, 768, 24, "bf16", "none"),         # six steps, d = 24
     (24, 2, 448, 32, "bf16", "tail:13"),     # several batch chunks of a few rows each
+    (8, 2, 392, 32, "bf16", "tail:3"),       # the smallest N of the eight-wave path: the last step 8 queries
     (4, 2, 300, 64, "bf16", "random:13"),    # d = 64, N % 8 != 0 (element-wise bias loads)
     (2, 3, 520, 48, "bf16", "tail:20"),      # d = 48 in the 64-wide tile, slab 72 KB (159 KB with the tiles)
     (2, 2, 600, 64, "bf16", "none"),         # slab 80 KB: too large beside the eight-wave tiles, four-wave tile
@@ -127,6 +128,7 @@ SMALL_ATTN = [
     (32, 4, 264, 32, "bf16", "random:17"),   # three steps per row, the last one 8 queries
     (64, 4, 128, 16, "bf16", "tail:5"),      # one step per row, d = 16
     (48, 4, 248, 24, "bf16", "none"),        # two steps per row, the second ragged
+    (256, 2, 8, 8, "bf16", "none"),          # N = 8, d = 8: one step, 24 of the tile's 32 keys past N
     (64, 8, 136, 48, "bf16", "random:5"),    # d = 48 in the 64-wide template
 ]
 
