@@ -331,7 +331,9 @@ __global__ __launch_bounds__(proj_bwd_waves(32 * KT) * 64) void bias_proj_bwd_ke
       for (int q = 0; q < 4; ++q)
         o[q] = pack2(fmaf(dx[kt][2 * q], rstd, fmaf(x[kt][2 * q], k2, k1)),
                      fmaf(dx[kt][2 * q + 1], rstd, fmaf(x[kt][2 * q + 1], k2, k1)));
-      __builtin_amdgcn_raw_buffer_store_b128(o, rdz, zoff + 64u * kt, 0, 0);
+      // streaming (nontemporal) store: dz, as large as z, would otherwise
+      // displace the z lines this launch and the next forward read
+      __builtin_amdgcn_raw_buffer_store_b128(o, rdz, zoff + 64u * kt, 0, 2);
     }
   };
   bool more = t < ntiles;
