@@ -600,9 +600,10 @@ __device__ __forceinline__ void attn_dkdv_tile(int wg, int nwg, DkdvSmem<DP>& sm
 template <int NW>
 struct DkdvWSmem {
   static constexpr int JT = 16 / NW;  // 16-query tiles per wave and step
-  u16 qa[2][2 * 128 * 32];            // [buffer][Q tile | dA tile], TileLds<32, 0> rows
-  float2 seed[2][128];                // [buffer] (-log2(e) LSE, -D) per query of the step
-  u32x4 bias[2][NW][JT / 2][64];      // [buffer][wave][half u][lane]: the wave's own bias
+  static constexpr int NB = NW == 8 ? 3 : 2;  // step buffers: loads issued NB - 1 steps ahead
+  u16 qa[NB][2 * 128 * 32];            // [buffer][Q tile | dA tile], TileLds<32, 0> rows
+  float2 seed[NB][128];                // [buffer] (-log2(e) LSE, -D) per query of the step
+  u32x4 bias[NB][NW][JT / 2][64];      // [buffer][wave][half u][lane]: the wave's own bias
   u32x4 kv[2][2][2][64];              // [row parity][K | V][key tile][lane]
   f32x4 comb[NW / 2 - 1][2][2][2][64];  // [group - 1][kt][dK | dV][ct][lane]
 };
@@ -615,6 +616,8 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem<NW>&
   constexpr int NQB = 12 / JT;    // most 128-query steps per row: 3 or 6
   constexpr int NG = NW / 2;      // query groups
   constexpr int UQ = 8 / NW;      // Q (and dA) loads per wave and step
+  constexpr int NB = DkdvWSmem<NW>::NB;
+  constexpr int F = 2 * UQ + JT / 2;  // loads every wave issues for every step
   constexpr int kTile = 128 * 32;
   constexpr uint32_t kOob = 0xFFFFFFF0u;
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
@@ -665,8 +668,15 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem<NW>&
   const u16* fKV = static_cast<const u16*>((wave & 1) ? a.v : a.k) + ((size_t)b0 * H + h) * plane;
   const float2* fS = a.seed + ((size_t)b0 * H + h) * N;
   int fb = b0, fq = 0;
-  // loads of the step at the fetch position (fb, fq) into buffer buf
+  // loads of the step at the fetch position (fb, fq) into buffer buf.  The
+  // loads only some waves issue (K/V at a row's start, the seeds) go first
+  // and the F that every wave issues last, so that waiting until at most F
+  // loads are outstanding completes every older step.
   auto issue = [&](int buf) {
+    if (fq == 0 && wave < 4)
+      lds_dma16(rsrc_words(fKV, plane_bytes), lds_addr(&sm.kv[(fb - b0) & 1][wave & 1][wave >> 1][0]), kv_off);
+    if (wave == 0)
+      lds_dma16(rsrc_words(fS, (uint32_t)N * 8u), lds_addr(sm.seed[buf]), (uint32_t)((fq * 128 + 2 * lane) * 8));
     const i32x4 rq = rsrc_words(fQ, plane_bytes), ra = rsrc_words(fdA, plane_bytes);
     const uint32_t qoff = (uint32_t)(fq * 128 * d * 2);
     const uint32_t dq = lds_addr(sm.qa[buf]);
@@ -682,10 +692,6 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem<NW>&
       const uint32_t off = (q < N && k0 < N) ? (uint32_t)(((size_t)q * N + k0) * 2) : kOob;
       lds_dma16(brs, lds_addr(&sm.bias[buf][wave][u][0]), off);
     }
-    if (wave == 0)
-      lds_dma16(rsrc_words(fS, (uint32_t)N * 8u), lds_addr(sm.seed[buf]), (uint32_t)((fq * 128 + 2 * lane) * 8));
-    if (fq == 0 && wave < 4)
-      lds_dma16(rsrc_words(fKV, plane_bytes), lds_addr(&sm.kv[(fb - b0) & 1][wave & 1][wave >> 1][0]), kv_off);
     if (++fq == nqb) {
       fq = 0;
       ++fb;
@@ -709,16 +715,25 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem<NW>&
   dk[0] = dk[1] = dv[0] = dv[1] = zero4;
   bf16x8 kf, vf;
 
+  // the first NB - 1 steps; then each step issues the loads of the step
+  // NB - 1 ahead into the buffer the previous step used (with NB = 3 that
+  // is a step whose K/V parity differs from the current row's: eight waves
+  // run only with at least four steps per row)
   if (T > 0) issue(0);
-  vm_wait<0>();
+  if (NB == 3 && T > 1) {
+    issue(1);
+    vm_wait<F>();
+  } else {
+    vm_wait<0>();
+  }
   __syncthreads();
 
   int it = 0, cb = b0;
   auto step = [&](auto QB_c) {
     constexpr int QB = decltype(QB_c)::value;
-    const int buf = it & 1;
+    const int buf = it % NB;
     const bool last_q = QB == nqb - 1;
-    if (it + 1 < T) issue(buf ^ 1);
+    if (it + NB - 1 < T) issue((it + NB - 1) % NB);
     if constexpr (QB == 0) {
       kf = as_bf8(sm.kv[(cb - b0) & 1][0][kt][lane]);
       vf = as_bf8(sm.kv[(cb - b0) & 1][1][kt][lane]);
@@ -786,7 +801,10 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem<NW>&
         dk[ct] = mfma32(trQ[m][ct], dsb, dk[ct]);
       }
     }
-    vm_wait<0>();  // this wave's loads of the next step have landed
+    // this wave's loads of the next step have landed (with NB = 3 the F
+    // loads of the step after it may still be in flight)
+    if (NB == 3 && it + 2 < T) vm_wait<F>();
+    else vm_wait<0>();
     __syncthreads();
     if (last_q) {
       // sum the query groups' dK, dV in group order and store row cb; `comb`
