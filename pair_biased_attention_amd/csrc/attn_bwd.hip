@@ -602,7 +602,7 @@ struct DkdvWSmem {
   static constexpr int JT = 16 / NW;  // 16-query tiles per wave and step
   static constexpr int NB = NW == 8 ? 3 : 2;  // step buffers: loads issued NB - 1 steps ahead
   u16 qa[NB][2 * 128 * 32];            // [buffer][Q tile | dA tile], TileLds<32, 0> rows
-  float2 seed[NB][128];                // [buffer] (-log2(e) LSE, -D) per query of the step
+  float seed[NB][256];                 // [buffer] -log2(e) LSE of the step's 128 queries, then -D
   u32x4 bias[NB][NW][JT / 2][64];      // [buffer][wave][half u][lane]: the wave's own bias
   u32x4 kv[2][2][2][64];              // [row parity][K | V][key tile][lane]
   f32x4 comb[NW / 2 - 1][2][2][2][64];  // [group - 1][kt][dK | dV][ct][lane]
@@ -675,8 +675,16 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem<NW>&
   auto issue = [&](int buf) {
     if (fq == 0 && wave < 4)
       lds_dma16(rsrc_words(fKV, plane_bytes), lds_addr(&sm.kv[(fb - b0) & 1][wave & 1][wave >> 1][0]), kv_off);
-    if (wave == 0)
-      lds_dma16(rsrc_words(fS, (uint32_t)N * 8u), lds_addr(sm.seed[buf]), (uint32_t)((fq * 128 + 2 * lane) * 8));
+    if (wave == 0) {
+      // the step's 128 (-log2(e) LSE, -D) pairs split into two planes of
+      // 128 floats, so that each seeds an accumulator with one LDS read
+      const i32x4 srs = rsrc_words(fS, (uint32_t)N * 8u);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int e = 64 * m + lane;
+        lds_dma4(srs, lds_addr(sm.seed[buf]) + 256 * m, (uint32_t)((fq * 128 + (e & 127)) * 8 + 4 * (e >> 7)));
+      }
+    }
     const i32x4 rq = rsrc_words(fQ, plane_bytes), ra = rsrc_words(fdA, plane_bytes);
     const uint32_t qoff = (uint32_t)(fq * 128 * d * 2);
     const uint32_t dq = lds_addr(sm.qa[buf]);
@@ -745,10 +753,9 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem<NW>&
 #pragma unroll
     for (int j = 0; j < JT; ++j) {
       const int qt = JT * qg + j;
-      const f32x4 s01 = *reinterpret_cast<const f32x4*>(&sm.seed[buf][16 * qt + 4 * g]);
-      const f32x4 s23 = *reinterpret_cast<const f32x4*>(&sm.seed[buf][16 * qt + 4 * g + 2]);
-      sacc[j] = f32x4{s01[0], s01[2], s23[0], s23[2]};
-      dp[j] = f32x4{s01[1], s01[3], s23[1], s23[3]};
+      const float* sp = sm.seed[buf] + 16 * qt + 4 * g;
+      sacc[j] = *reinterpret_cast<const f32x4*>(sp);
+      dp[j] = *reinterpret_cast<const f32x4*>(sp + 128);
       qfr[j] = as_bf8(*reinterpret_cast<const u32x4*>(&tQ[LQ::off(16 * qt + n, 8 * g)]));
       afr[j] = as_bf8(*reinterpret_cast<const u32x4*>(&tA[LQ::off(16 * qt + n, 8 * g)]));
     }
@@ -1230,23 +1237,24 @@ __device__ __forceinline__ void attn_dq_split_tile(int wg, int nwg, KeySplitLds 
 #pragma unroll
       for (int m = 0; m < 2; ++m) kt[ct][m] = tr_frag_l<LK>(my.k, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
     u32x4 blo4 = my.bias[bias_rows_slot(ln, 2 * g)], bhi4 = my.bias[bias_rows_slot(ln, 2 * g + 1)];
-    uint32_t kw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) kw[e] = keep[(kb >> 2) + 4 * g + e];  // keep bytes of keys 16g+4e .. +3
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(&keep[(kb >> 2) + 4 * g]);  // keep bytes of keys 16g .. 16g+15
     // every read of the region has returned: the next block may overwrite it
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (blk + 1 < bhi) stage(kb + 64);
 
+    // masked keys and keys past N: the select only in blocks that hold one
+    if (__any((kw[0] & kw[1] & kw[2] & kw[3]) != 0x01010101u)) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t m01 = ((kw[e] & 0xFFu) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF00u) ? 0u : 0xFFFF0000u);
-      const uint32_t m23 = ((kw[e] & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF000000u) ? 0u : 0xFFFF0000u);
-      if (e < 2) {
-        blo4[2 * e] = (blo4[2 * e] & ~m01) | (kMaskedBias2 & m01);
-        blo4[2 * e + 1] = (blo4[2 * e + 1] & ~m23) | (kMaskedBias2 & m23);
-      } else {
-        bhi4[2 * (e - 2)] = (bhi4[2 * (e - 2)] & ~m01) | (kMaskedBias2 & m01);
-        bhi4[2 * (e - 2) + 1] = (bhi4[2 * (e - 2) + 1] & ~m23) | (kMaskedBias2 & m23);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t m01 = ((kw[e] & 0xFFu) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF00u) ? 0u : 0xFFFF0000u);
+        const uint32_t m23 = ((kw[e] & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF000000u) ? 0u : 0xFFFF0000u);
+        if (e < 2) {
+          blo4[2 * e] = (blo4[2 * e] & ~m01) | (kMaskedBias2 & m01);
+          blo4[2 * e + 1] = (blo4[2 * e + 1] & ~m23) | (kMaskedBias2 & m23);
+        } else {
+          bhi4[2 * (e - 2)] = (bhi4[2 * (e - 2)] & ~m01) | (kMaskedBias2 & m01);
+          bhi4[2 * (e - 2) + 1] = (bhi4[2 * (e - 2) + 1] & ~m23) | (kMaskedBias2 & m23);
+        }
       }
     }
     f32x4 acc[4];
@@ -1519,26 +1527,34 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_bf16_kernel(BwdArgs a, int nq
 #pragma unroll
       for (int m = 0; m < 2; ++m) kt[ct][m] = tr_frag_l<LK>(tK, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
 
-    u32x4 mlo, mhi;
+    // keep bytes of keys 16g .. 16g + 15 in one read; masked keys and keys
+    // past N get the most negative bias, and only blocks that hold one pay
+    // for the select (a uniform branch)
+    const u32x4 kw4 = *reinterpret_cast<const u32x4*>(&keep_lds[(kb >> 2) + 4 * g]);
+    if (__any((kw4[0] & kw4[1] & kw4[2] & kw4[3]) != 0x01010101u)) {
+      u32x4 mlo, mhi;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t kw = keep_lds[(kb >> 2) + 4 * g + e];
-      const uint32_t m01 = ((kw & 0xFFu) ? 0u : 0xFFFFu) | ((kw & 0xFF00u) ? 0u : 0xFFFF0000u);
-      const uint32_t m23 = ((kw & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw & 0xFF000000u) ? 0u : 0xFFFF0000u);
-      if (e < 2) { mlo[2 * e] = m01; mlo[2 * e + 1] = m23; }
-      else { mhi[2 * (e - 2)] = m01; mhi[2 * (e - 2) + 1] = m23; }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t kw = kw4[e];
+        const uint32_t m01 = ((kw & 0xFFu) ? 0u : 0xFFFFu) | ((kw & 0xFF00u) ? 0u : 0xFFFF0000u);
+        const uint32_t m23 = ((kw & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw & 0xFF000000u) ? 0u : 0xFFFF0000u);
+        if (e < 2) { mlo[2 * e] = m01; mlo[2 * e + 1] = m23; }
+        else { mhi[2 * (e - 2)] = m01; mhi[2 * (e - 2) + 1] = m23; }
+      }
+#pragma unroll
+      for (int s = 0; s < QT; ++s)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bcur[s][0][e] = (bcur[s][0][e] & ~mlo[e]) | (kMaskedBias2 & mlo[e]);
+          bcur[s][1][e] = (bcur[s][1][e] & ~mhi[e]) | (kMaskedBias2 & mhi[e]);
+        }
     }
     // S'^T and (dP - D)^T of every sub-tile first, then the elementwise work
     // and the dQ products as one block of code
     f32x4 acc[QT][4], qk[QT][4], dp[QT][4];
 #pragma unroll
     for (int s = 0; s < QT; ++s) {
-      u32x4 blo = bcur[s][0], bhi = bcur[s][1];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        blo[e] = (blo[e] & ~mlo[e]) | (kMaskedBias2 & mlo[e]);
-        bhi[e] = (bhi[e] & ~mhi[e]) | (kMaskedBias2 & mhi[e]);
-      }
+      const u32x4 blo = bcur[s][0], bhi = bcur[s][1];
       acc[s][0] = mfma32(id2l_lo, as_bf8(blo), mfma32(id2h_lo, as_bf8(blo), nl4[s]));
       acc[s][1] = mfma32(id2l_hi, as_bf8(blo), mfma32(id2h_hi, as_bf8(blo), nl4[s]));
       acc[s][2] = mfma32(id2l_lo, as_bf8(bhi), mfma32(id2h_lo, as_bf8(bhi), nl4[s]));

@@ -416,23 +416,24 @@ __global__ void __launch_bounds__(256) attn_fwd_split_kernel(FwdArgs a) {
 #pragma unroll
       for (int m = 0; m < 2; ++m) vt[ct][m] = tr_frag_l<LK>(my.v, 16 * g + 8 * m, 16 * g + 8 * m + 4, 16 * ct, lane);
     u32x4 blo4 = my.bias[bias_rows_slot(ln, 2 * g)], bhi4 = my.bias[bias_rows_slot(ln, 2 * g + 1)];
-    uint32_t kw[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) kw[e] = split_keep[(kb >> 2) + 4 * g + e];  // keep bytes of keys 16g+4e .. +3
+    const u32x4 kw = *reinterpret_cast<const u32x4*>(&split_keep[(kb >> 2) + 4 * g]);  // keep bytes of keys 16g .. 16g+15
     // every read of the region has returned: the next block may overwrite it
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     if (blk + 1 < bhi) stage(kb + 64);
 
+    // masked keys and keys past N: the select only in blocks that hold one
+    if (__any((kw[0] & kw[1] & kw[2] & kw[3]) != 0x01010101u)) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const uint32_t m01 = ((kw[e] & 0xFFu) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF00u) ? 0u : 0xFFFF0000u);
-      const uint32_t m23 = ((kw[e] & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF000000u) ? 0u : 0xFFFF0000u);
-      if (e < 2) {
-        blo4[2 * e] = (blo4[2 * e] & ~m01) | (kMaskedBias2 & m01);
-        blo4[2 * e + 1] = (blo4[2 * e + 1] & ~m23) | (kMaskedBias2 & m23);
-      } else {
-        bhi4[2 * (e - 2)] = (bhi4[2 * (e - 2)] & ~m01) | (kMaskedBias2 & m01);
-        bhi4[2 * (e - 2) + 1] = (bhi4[2 * (e - 2) + 1] & ~m23) | (kMaskedBias2 & m23);
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t m01 = ((kw[e] & 0xFFu) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF00u) ? 0u : 0xFFFF0000u);
+        const uint32_t m23 = ((kw[e] & 0xFF0000u) ? 0u : 0xFFFFu) | ((kw[e] & 0xFF000000u) ? 0u : 0xFFFF0000u);
+        if (e < 2) {
+          blo4[2 * e] = (blo4[2 * e] & ~m01) | (kMaskedBias2 & m01);
+          blo4[2 * e + 1] = (blo4[2 * e + 1] & ~m23) | (kMaskedBias2 & m23);
+        } else {
+          bhi4[2 * (e - 2)] = (bhi4[2 * (e - 2)] & ~m01) | (kMaskedBias2 & m01);
+          bhi4[2 * (e - 2) + 1] = (bhi4[2 * (e - 2) + 1] & ~m23) | (kMaskedBias2 & m23);
+        }
       }
     }
     f32x4 acc[4];

@@ -202,6 +202,15 @@ __device__ __forceinline__ void lds_dma16(i32x4 rsrc, uint32_t lds_base, uint32_
                : "v"(byte_off), "s"(rsrc), "{m0}"(lds_base)
                : "memory");
 }
+// 4 bytes per lane from a buffer straight into LDS: lane l writes LDS bytes
+// lds_base + 4 l .. + 3 (zero where byte_off fails the range check); ordered
+// like lds_dma16.
+__device__ __forceinline__ void lds_dma4(i32x4 rsrc, uint32_t lds_base, uint32_t byte_off) {
+  asm volatile("buffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(byte_off), "s"(rsrc), "{m0}"(lds_base)
+               : "memory");
+}
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(lds_void*)(p);
 }
