@@ -675,15 +675,13 @@ __device__ __forceinline__ void attn_dkdv_tile_w(int wg, int nwg, DkdvWSmem<NW>&
   auto issue = [&](int buf) {
     if (fq == 0 && wave < 4)
       lds_dma16(rsrc_words(fKV, plane_bytes), lds_addr(&sm.kv[(fb - b0) & 1][wave & 1][wave >> 1][0]), kv_off);
-    if (wave == 0) {
+    if (wave < 4) {
       // the step's 128 (-log2(e) LSE, -D) pairs split into two planes of
-      // 128 floats, so that each seeds an accumulator with one LDS read
-      const i32x4 srs = rsrc_words(fS, (uint32_t)N * 8u);
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int e = 64 * m + lane;
-        lds_dma4(srs, lds_addr(sm.seed[buf]) + 256 * m, (uint32_t)((fq * 128 + (e & 127)) * 8 + 4 * (e >> 7)));
-      }
+      // 128 floats, so that each seeds an accumulator with one LDS read:
+      // wave w < 4 loads floats 64 w .. 64 w + 63 of the two planes
+      const int e = 64 * wave + lane;
+      lds_dma4(rsrc_words(fS, (uint32_t)N * 8u), lds_addr(sm.seed[buf]) + 256 * wave,
+               (uint32_t)((fq * 128 + (e & 127)) * 8 + 4 * (e >> 7)));
     }
     const i32x4 rq = rsrc_words(fQ, plane_bytes), ra = rsrc_words(fdA, plane_bytes);
     const uint32_t qoff = (uint32_t)(fq * 128 * d * 2);

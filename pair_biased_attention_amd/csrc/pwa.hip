@@ -31,7 +31,6 @@ namespace {
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ u16 lo16(uint32_t w) { return (u16)(w & 0xFFFFu); }
 __device__ __forceinline__ u16 hi16(uint32_t w) { return (u16)(w >> 16); }
-__device__ __forceinline__ float sigmoid_precise(float x) { return 1.0f / (1.0f + expf(-x)); }
 }  // namespace
 
 // ------------------------------------------------------------------ softmax
@@ -850,7 +849,7 @@ __global__ void __launch_bounds__(256) pwa_bwd_pre_kernel(PwaArgs a) {
   for (int e = 0; e < 4; ++e) {
     const float f0 = bf2f(lo16(xo[e])), f1 = bf2f(hi16(xo[e]));
     const float o0 = bf2f(lo16(xv[e])), o1 = bf2f(hi16(xv[e]));
-    const float s0 = sigmoid_precise(bf2f(lo16(xg[e]))), s1 = sigmoid_precise(bf2f(hi16(xg[e])));
+    const float s0 = sigmoidf_fast(bf2f(lo16(xg[e]))), s1 = sigmoidf_fast(bf2f(hi16(xg[e])));
     ra[e] = pack2(f0 * s0, f1 * s1);
     rg[e] = pack2(f0 * o0 * (1.f - s0), f1 * o1 * (1.f - s1));
   }
