@@ -130,6 +130,8 @@ SMALL_ATTN = [
     (48, 4, 248, 24, "bf16", "none"),        # two steps per row, the second ragged
     (256, 2, 8, 8, "bf16", "none"),          # N = 8, d = 8: one step, 24 of the tile's 32 keys past N
     (64, 8, 136, 48, "bf16", "random:5"),    # d = 48 in the 64-wide template
+    (515, 2, 264, 24, "bf16", "random:17"),  # many (b, h): the second query block's last two waves without rows
+    (256, 4, 320, 32, "bf16", "tail:21"),    # five full key blocks, three 128-query steps (the last one 64)
 ]
 
 
