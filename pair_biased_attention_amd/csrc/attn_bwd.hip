@@ -91,7 +91,7 @@ __device__ __forceinline__ u32x4 load_bias8(const u16* row, int k0, int N, bool 
 // ------------------------------------------------------------------ 1. pre
 // bf16: one lane per 16-byte chunk of a row (L = d/8 lanes per row, 256/L
 // rows per workgroup), so every load and store is a coalesced 16-byte access;
-// D is summed over a row's lanes through LDS in a fixed order.
+// D is summed over a row's lanes by a butterfly in a fixed order.
 __global__ void __launch_bounds__(256) attn_bwd_pre_bf16_kernel(BwdArgs a, int lanes_log2) {
   // each row takes 2^lanes_log2 consecutive lanes (d / 8 rounded up to a
   // power of two), lane c its channels 8c .. 8c + 7; the row sum D is a
