@@ -49,10 +49,6 @@ namespace {
 constexpr int kSlabStride = 36;
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
-__device__ __forceinline__ void kperm_slot(int kappa, int& t, int& i) {
-  t = (kappa & 15) >> 2;
-  i = ((kappa >> 4) << 2) | (kappa & 3);
-}
 __device__ __forceinline__ u16 lo16(uint32_t w) { return (u16)(w & 0xFFFFu); }
 __device__ __forceinline__ u16 hi16(uint32_t w) { return (u16)(w >> 16); }
 __device__ __forceinline__ float sigmoid_precise(float x) { return 1.0f / (1.0f + expf(-x)); }

@@ -69,7 +69,6 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) u16 sK[2][64 * RS];
   __shared__ __attribute__((aligned(16))) u16 sV[2][64 * RS];
   __shared__ uint32_t sKeep[2][16];
-  __shared__ int sAny[2];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = wave_index();
   const int g = lane >> 4, ln = lane & 15;
@@ -120,11 +119,7 @@ __global__ void __launch_bounds__(256) attn_fwd_bf16_kernel(FwdArgs a) {
       *reinterpret_cast<u32x4*>(&sK[buf][kappa * RS + 8 * c8]) = rk[it];
       *reinterpret_cast<u32x4*>(&sV[buf][kappa * RS + 8 * c8]) = rv[it];
     }
-    if (tid < 64) {
-      reinterpret_cast<uint8_t*>(&sKeep[buf][0])[tid] = rkeep ? 1 : 0;
-      const unsigned long long bal = __ballot(!rkeep);
-      if (tid == 0) sAny[buf] = bal != 0ull;
-    }
+    if (tid < 64) reinterpret_cast<uint8_t*>(&sKeep[buf][0])[tid] = rkeep ? 1 : 0;
   };
 
   // ---- per-wave query fragments (B operand of S^T = K Q^T), unscaled

@@ -185,7 +185,7 @@ struct PwaDwSmem {
 template <int DP>
 __device__ __forceinline__ void pwa_dw_tile(int wg, int nwg, PwaDwSmem<DP>& sm, const u16* __restrict__ dA,
                                             const u16* __restrict__ V, float* __restrict__ partial, int S, int N,
-                                            int H, int d, int P, int spc, int nt1) {
+                                            int H, int d, int spc, int nt1) {
   using Sm = PwaDwSmem<DP>;
   constexpr int KS = Sm::KS, SPS = Sm::SPS;
   constexpr int C8 = DP / 8;
@@ -339,8 +339,8 @@ __global__ void __launch_bounds__(512) pwa_gemm_kernel(const u16* __restrict__ X
   if constexpr (DW) {
     if (wg < dw.ndw_slots) {
       if (wg < dw.ndw)
-        pwa_dw_tile<DP>(wg, dw.ndw, *reinterpret_cast<PwaDwSmem<DP>*>(&sm), X, dw.V, dw.partial, S, N, H, d, dw.P,
-                        dw.spc, dw.nt1);
+        pwa_dw_tile<DP>(wg, dw.ndw, *reinterpret_cast<PwaDwSmem<DP>*>(&sm), X, dw.V, dw.partial, S, N, H, d, dw.spc,
+                        dw.nt1);
       return;
     }
     wg -= dw.ndw_slots;
